@@ -1,0 +1,213 @@
+"""Python binding of the MI355X BinaryAttention library (libbinattn.so).
+
+Argument marshalling only: each ``ba_*`` function here has the name of, and
+forwards to, the C entry point declared in ``include/binattn.h``; every step
+of the computation runs in the gfx950 kernels. Torch is used for device
+memory and streams. There is no CPU fallback: if the library is missing or
+the device is not a gfx950 GPU, calls raise.
+
+Build the library in-tree with ``python -m bit_qk_attention_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbinattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "binattn.h")
+
+BA_OK, BA_ERR_INVALID_ARG, BA_ERR_UNSUPPORTED, BA_ERR_HIP = 0, 1, 2, 3
+BA_F16, BA_BF16, BA_F32 = 0, 1, 2
+BA_BIAS_NONE, BA_BIAS_DENSE, BA_BIAS_RELPOS = 0, 1, 2
+BA_MAX_TOKENS = 65536
+
+
+class BinAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+class ba_bias(ctypes.Structure):
+    """Mirror of the C struct ba_bias."""
+    _fields_ = [("kind", ctypes.c_int), ("data", ctypes.c_void_p), ("dtype", ctypes.c_int),
+                ("batch_stride", ctypes.c_int64), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("n_prefix", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbinattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not found: build it with `python -m bit_qk_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.ba_packed_words.argtypes = [I]
+        L.ba_packed_words.restype = I
+        L.ba_pack_qk.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P]
+        L.ba_pack_qk.restype = I
+        L.ba_quant_v.argtypes = [P, I, I, I, I, I, P, P, P]
+        L.ba_quant_v.restype = I
+        L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
+        L.ba_attention_fwd.restype = I
+        L.ba_debug_hamming_scores.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
+        L.ba_debug_hamming_scores.restype = I
+        L.ba_status_string.argtypes = [I]
+        L.ba_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions declared in include/binattn.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ba_[a-z_]+)\s*\(", text)))
+
+
+def status_string(s: int) -> str:
+    return lib().ba_status_string(s).decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != BA_OK:
+        raise BinAttnError(fn, st, status_string(st))
+
+
+# --------------------------------------------------------------- torch glue --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    return {torch.float16: BA_F16, torch.bfloat16: BA_BF16, torch.float32: BA_F32}.get(t.dtype, -1)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        torch = _torch()
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libbinattn takes device tensors only (no CPU path)")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("libbinattn takes contiguous tensors only")
+
+
+@dataclass
+class Bias:
+    """Bias description (see ba_bias in include/binattn.h).
+
+    DENSE: ``data`` [H,N,N] (shared over the batch, batch_stride 0) or
+    [B,H,N,N] (batch_stride H*N*N), float32 or float16.
+    RELPOS: ``data`` float32 [H,(2*grid_h-1)*(2*grid_w-1)].
+    """
+    kind: int = BA_BIAS_NONE
+    data: object = None
+    batch_stride: int = 0
+    grid_h: int = 0
+    grid_w: int = 0
+    n_prefix: int = 0
+
+    def to_c(self) -> ba_bias:
+        if self.kind == BA_BIAS_NONE or self.data is None:
+            return ba_bias(BA_BIAS_NONE, None, BA_F32, 0, 0, 0, 0)
+        _require_gpu(self.data)
+        return ba_bias(self.kind, self.data.data_ptr(), _dt(self.data), self.batch_stride,
+                       self.grid_h, self.grid_w, self.n_prefix)
+
+
+# ------------------------------------------------------------ entry points --
+
+def ba_packed_words(d: int) -> int:
+    return lib().ba_packed_words(d)
+
+
+def ba_pack_qk(q, k, qbits, qmu, kbits, kmu, stream=None) -> None:
+    """q, k [B,H,N,d] fp16/bf16 -> qbits/kbits int32 [B,H,N,W], qmu/kmu float32 [B,H,N]."""
+    _require_gpu(q, k, qbits, qmu, kbits, kmu)
+    B, H, N, d = q.shape
+    _check("ba_pack_qk", lib().ba_pack_qk(_ptr(q), _ptr(k), _dt(q), B, H, N, d, _ptr(qbits), _ptr(qmu),
+                                          _ptr(kbits), _ptr(kmu), _stream(stream)))
+
+
+def ba_quant_v(v, vq, vscale, stream=None) -> None:
+    """v [B,H,N,d] fp16/bf16 -> vq int8 [B,H,N,d], vscale float32 [B,H,d]."""
+    _require_gpu(v, vq, vscale)
+    B, H, N, d = v.shape
+    _check("ba_quant_v", lib().ba_quant_v(_ptr(v), _dt(v), B, H, N, d, _ptr(vq), _ptr(vscale),
+                                          _stream(stream)))
+
+
+def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream=None) -> None:
+    """Fused forward; out [B,H,N,d] fp16/bf16 defines the shape and output dtype."""
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, out)
+    B, H, N, d = out.shape
+    cb = (bias or Bias()).to_c()
+    _check("ba_attention_fwd", lib().ba_attention_fwd(
+        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), ctypes.byref(cb),
+        B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
+
+
+def ba_debug_hamming_scores(qbits, kbits, d, bh_begin, bh_count, row_begin, row_count, sigma,
+                            stream=None) -> None:
+    """sigma int32 [bh_count, row_count, N] = d - 2*popcount(q xor k) over a window."""
+    _require_gpu(qbits, kbits, sigma)
+    B, H, N, _W = qbits.shape
+    _check("ba_debug_hamming_scores", lib().ba_debug_hamming_scores(
+        _ptr(qbits), _ptr(kbits), B, H, N, d, bh_begin, bh_count, row_begin, row_count,
+        _ptr(sigma), _stream(stream)))
+
+
+# ------------------------------------------------------------- conveniences --
+
+def pack_qk(q, k, stream=None):
+    torch = _torch()
+    B, H, N, d = q.shape
+    W = ba_packed_words(d)
+    qbits = torch.empty((B, H, N, W), dtype=torch.int32, device=q.device)
+    kbits = torch.empty_like(qbits)
+    qmu = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    kmu = torch.empty_like(qmu)
+    ba_pack_qk(q, k, qbits, qmu, kbits, kmu, stream)
+    return qbits, qmu, kbits, kmu
+
+
+def quant_v(v, stream=None):
+    torch = _torch()
+    B, H, N, d = v.shape
+    vq = torch.empty((B, H, N, d), dtype=torch.int8, device=v.device)
+    vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
+    ba_quant_v(v, vq, vscale, stream)
+    return vq, vscale
+
+
+def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
+    """Whole forward pass: pack Q/K, quantise V, fused attention."""
+    torch = _torch()
+    qbits, qmu, kbits, kmu = pack_qk(q, k, stream)
+    vq, vscale = quant_v(v, stream)
+    if out is None:
+        out = torch.empty_like(q)
+    ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream)
+    return out

@@ -1,0 +1,83 @@
+// common.h — internal declarations shared by the gfx950 kernels and the
+// C-ABI layer of the BinaryAttention library. Not a public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "binattn.h"
+
+namespace binattn {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// ---- 16-bit formats -------------------------------------------------------
+
+// Widen an fp16 / bf16 bit pattern to float (exact).
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  _Float16 x = __builtin_bit_cast(_Float16, h);
+  return (float)x;
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+template <int DT>
+__device__ __forceinline__ float to_f32(uint16_t h) {
+  return DT == BA_F16 ? f16_to_f32(h) : bf16_to_f32(h);
+}
+
+// True iff the 16-bit value is < 0 (negative, non-zero, not NaN), i.e. its
+// sign is -1 under the convention sign(+0) = sign(-0) = +1.
+template <int DT>
+__device__ __forceinline__ uint32_t neg_bit(uint16_t h) {
+  const uint32_t mag = h & 0x7FFFu;
+  const uint32_t inf = DT == BA_F16 ? 0x7C00u : 0x7F80u;
+  return (h >> 15) & (uint32_t)(mag != 0u) & (uint32_t)(mag <= inf);
+}
+
+// Round float to fp16 / bf16, nearest even.
+__device__ __forceinline__ uint16_t f32_to_f16(float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- launchers (host side; arguments already validated) -------------------
+
+hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t ntok,
+                          int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
+                          float* kmu, hipStream_t s);
+hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
+                          int8_t* vq, float* vscale, hipStream_t s);
+hipError_t launch_hamming(const uint32_t* qbits, const uint32_t* kbits, int N,
+                          int d, int bh_begin, int bh_count, int row_begin,
+                          int row_count, int32_t* sigma, hipStream_t s);
+
+struct AttnArgs {
+  const uint32_t* qbits;
+  const float* qmu;
+  const uint32_t* kbits;
+  const float* kmu;
+  const int8_t* vq;
+  const float* vscale;
+  int bias_kind;           // ba_bias_kind
+  const void* bias;
+  int bias_dtype;          // dense: BA_F32 / BA_F16
+  int64_t bias_bstride;    // dense: elements between batch slices
+  int grid_h, grid_w, n_prefix;
+  int B, H, N, d;
+  void* out;
+  int out_dt;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace binattn

@@ -1,0 +1,234 @@
+// prepass.hip — gfx950 kernels for the steps before the fused attention:
+// sign/scale packing of Q and K, channel-wise int8 quantisation of V, and
+// the integer Hamming-score debug view.
+//
+// Method: BinaryAttention (gist.science summaries). Scaled binary Q/K: zh
+// technical summary section 2.2 item 1 (nl Methodologie 2, it/fr/pt section
+// 2B). Channel-wise 8-bit V: zh section 2.2 item 3 (nl Methodologie 2).
+// Hamming similarity: zh sections 2.1 and 2.2 item 1.
+//
+// All three are memory-bound; the kernels aim at coalesced 16-byte accesses
+// and an XCD-aware block order where blocks share cache lines.
+#include "common.h"
+
+namespace binattn {
+
+// ---------------------------------------------------------------------------
+// pack_qk: one thread per token. Loads the token's d 16-bit values (16-byte
+// vector loads when d % 8 == 0), sets bit c iff x_c < 0, and computes
+// mu = sum|x| / d with a float64 sum (exact for fp16/bf16 inputs of ordinary
+// range) and one float64 division rounded once to float.
+// grid.y selects Q (0) or K (1).
+// ---------------------------------------------------------------------------
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void pack_qk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
+    int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
+    uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= ntok) return;
+  const uint16_t* x = (blockIdx.y == 0 ? q : k) + t * d;
+  uint32_t* bits = (blockIdx.y == 0 ? qbits : kbits);
+  float* mu = (blockIdx.y == 0 ? qmu : kmu);
+  const int W = (d + 31) >> 5;
+  double asum = 0.0;
+  for (int w = 0; w < W; ++w) {
+    uint32_t word = 0;
+    const int c0 = w * 32;
+    const int nc = min(32, d - c0);
+    if (VEC) {
+      for (int g = 0; g < nc; g += 8) {
+        const u4v raw = *reinterpret_cast<const u4v*>(x + c0 + g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t h = (uint16_t)(raw[e >> 1] >> ((e & 1) * 16));
+          word |= neg_bit<DT>(h) << (g + e);
+          asum += (double)fabsf(to_f32<DT>(h));
+        }
+      }
+    } else {
+      for (int c = 0; c < nc; ++c) {
+        const uint16_t h = x[c0 + c];
+        word |= neg_bit<DT>(h) << c;
+        asum += (double)fabsf(to_f32<DT>(h));
+      }
+    }
+    bits[t * W + w] = word;
+  }
+  mu[t] = (float)(asum / (double)d);
+}
+
+hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t ntok,
+                          int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
+                          float* kmu, hipStream_t s) {
+  const dim3 grid((unsigned)((ntok + 255) / 256), 2);
+  const bool vec = (d % 8) == 0;
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  if (dt == BA_F16) {
+    if (vec) hipLaunchKernelGGL((pack_qk_kernel<BA_F16, true>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+    else     hipLaunchKernelGGL((pack_qk_kernel<BA_F16, false>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+  } else {
+    if (vec) hipLaunchKernelGGL((pack_qk_kernel<BA_BF16, true>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+    else     hipLaunchKernelGGL((pack_qk_kernel<BA_BF16, false>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// quant_v: one block per (head, channel group of CG channels). The block
+// reads the group's columns of all N tokens twice: pass 1 takes the per-
+// channel max |v| (an LDS atomic max on the float bits, valid because the
+// values are non-negative), pass 2 quantises with inv = 127/amax and writes
+// int8. With CG == d a wave reads whole rows (fully coalesced); smaller
+// groups keep enough blocks in flight when there are few heads, and the
+// block order keeps the groups of one head on one XCD so they share L2.
+// VEC: d % 8 == 0, each thread handles 8 consecutive channels.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void quant_v_kernel(
+    const uint16_t* __restrict__ v, int nbh, int N, int d, int CG,
+    int8_t* __restrict__ vq, float* __restrict__ vscale) {
+  __shared__ uint32_t amax_bits[128];
+  __shared__ float inv_s[128];
+  const int ngroups = (d + CG - 1) / CG;
+  const int nblk = nbh * ngroups;
+  // XCD-aware order: consecutive block ids go to different XCDs, so hand each
+  // XCD a contiguous range of (head, group) work items.
+  int u = blockIdx.x;
+  if ((nblk & 7) == 0) u = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int bh = u / ngroups;
+  const int c0 = (u % ngroups) * CG;
+  const int cg = min(CG, d - c0);
+  for (int i = threadIdx.x; i < cg; i += blockDim.x) amax_bits[i] = 0u;
+  __syncthreads();
+
+  const uint16_t* vh = v + (int64_t)bh * N * d;
+  int8_t* qh = vq + (int64_t)bh * N * d;
+  const bool vec = (d % 8) == 0 && (cg % 8) == 0;
+  if (vec) {
+    const int P = cg / 8;                 // 8-channel pieces per row
+    const int rows = blockDim.x / P;      // rows per sweep
+    const int piece = threadIdx.x % P;
+    const int r0 = threadIdx.x / P;
+    const bool active = r0 < rows;
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active) {
+      for (int j = r0; j < N; j += rows) {
+        const u4v raw = *reinterpret_cast<const u4v*>(vh + (int64_t)j * d + c0 + piece * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16)))));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicMax(&amax_bits[piece * 8 + e], __float_as_uint(m[e]));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < cg; i += blockDim.x) {
+      const float a = __uint_as_float(amax_bits[i]);
+      inv_s[i] = a > 0.0f ? 127.0f / a : 0.0f;
+      vscale[(int64_t)bh * d + c0 + i] = a / 127.0f;
+    }
+    __syncthreads();
+    if (active) {
+      float inv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) inv[e] = inv_s[piece * 8 + e];
+      for (int j = r0; j < N; j += rows) {
+        const int64_t off = (int64_t)j * d + c0 + piece * 8;
+        const u4v raw = *reinterpret_cast<const u4v*>(vh + off);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
+          y = fminf(fmaxf(y, -127.0f), 127.0f);
+          const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
+          if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+        }
+        *reinterpret_cast<uint2*>(qh + off) = make_uint2(lo, hi);
+      }
+    }
+  } else {
+    // generic d: one thread per (row, channel) element, scalar accesses
+    for (int idx = threadIdx.x; idx < N * cg; idx += blockDim.x) {
+      const int j = idx / cg, c = idx % cg;
+      atomicMax(&amax_bits[c], __float_as_uint(fabsf(to_f32<DT>(vh[(int64_t)j * d + c0 + c]))));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < cg; i += blockDim.x) {
+      const float a = __uint_as_float(amax_bits[i]);
+      inv_s[i] = a > 0.0f ? 127.0f / a : 0.0f;
+      vscale[(int64_t)bh * d + c0 + i] = a / 127.0f;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < N * cg; idx += blockDim.x) {
+      const int j = idx / cg, c = idx % cg;
+      float y = __builtin_rintf(to_f32<DT>(vh[(int64_t)j * d + c0 + c]) * inv_s[c]);
+      y = fminf(fmaxf(y, -127.0f), 127.0f);
+      qh[(int64_t)j * d + c0 + c] = (int8_t)(int)y;
+    }
+  }
+}
+
+hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
+                          int8_t* vq, float* vscale, hipStream_t s) {
+  // widest channel group (whole rows when possible) that still gives
+  // >= 1024 blocks; at least 8 channels per group, at most 128.
+  int CG = d;
+  if (d % 8 == 0) {
+    while (CG > 8 && (int64_t)nbh * ((d + CG - 1) / CG) < 1024) {
+      int next = CG / 2;
+      if (next % 8) next = (next / 8) * 8;
+      if (next < 8) next = 8;
+      CG = next;
+    }
+  }
+  const int ngroups = (d + CG - 1) / CG;
+  const int64_t nblk = (int64_t)nbh * ngroups;
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  if (dt == BA_F16)
+    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale);
+  else
+    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Hamming debug view: sigma = d - 2*popcount(q xor k), one thread per key.
+// Grid: x = key blocks of 256, y = query rows of the window, z = heads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void hamming_kernel(
+    const uint32_t* __restrict__ qbits, const uint32_t* __restrict__ kbits, int N,
+    int d, int W, int bh_begin, int row_begin, int row_count, int32_t* __restrict__ sigma) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int r = blockIdx.y;
+  const int hb = blockIdx.z;
+  if (j >= N) return;
+  const int64_t bh = bh_begin + hb;
+  const uint32_t* qi = qbits + (bh * N + row_begin + r) * W;
+  const uint32_t* kj = kbits + (bh * N + j) * W;
+  int h = 0;
+  for (int w = 0; w < W; ++w) h += __builtin_popcount(qi[w] ^ kj[w]);
+  sigma[((int64_t)hb * row_count + r) * N + j] = d - 2 * h;
+}
+
+hipError_t launch_hamming(const uint32_t* qbits, const uint32_t* kbits, int N,
+                          int d, int bh_begin, int bh_count, int row_begin,
+                          int row_count, int32_t* sigma, hipStream_t s) {
+  const int W = (d + 31) / 32;
+  // grid.y is limited to 65535 rows per launch; split larger windows
+  for (int r0 = 0; r0 < row_count; r0 += 65535) {
+    const int rc = min(65535, row_count - r0);
+    for (int h0 = 0; h0 < bh_count; h0 += 65535) {
+      const int hc = min(65535, bh_count - h0);
+      hipLaunchKernelGGL(hamming_kernel, dim3((N + 255) / 256, rc, hc), dim3(256), 0, s,
+                         qbits, kbits, N, d, W, bh_begin + h0, row_begin + r0, row_count,
+                         sigma + ((int64_t)h0 * row_count + r0) * N);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace binattn

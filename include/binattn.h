@@ -1,0 +1,147 @@
+/*
+ * binattn.h — C ABI of the MI355X (gfx950) BinaryAttention forward library.
+ *
+ * The method (BinaryAttention: One-Bit QK-Attention for Vision and Diffusion
+ * Transformers; technical summaries on gist.science, pages zh, nl, it, fr,
+ * pt) replaces each query and key by its sign vector and a magnitude scale,
+ * scores query/key pairs through a Hamming distance of the sign bits, adds a
+ * learnable bias, applies softmax, quantises the unnormalised probabilities
+ * to unsigned 8 bit and V to channel-wise int8, and aggregates P.V in
+ * integers before dequantising. The calls below follow that statement of the
+ * problem: pack Q/K, quantise V, then the fused attention; a debug call
+ * exposes the integer similarity.
+ *
+ * Conventions shared by every call
+ *  - Memory: every pointer argument is DEVICE memory allocated by the caller
+ *    (e.g. a torch tensor's data_ptr()). The library allocates nothing, keeps
+ *    no pointer after a call returns, and fully overwrites its outputs.
+ *    Outputs must not alias inputs. Buffers must stay alive until the work
+ *    queued on `stream` has finished.
+ *  - Stream: `stream` is a hipStream_t passed as void* (NULL = the default
+ *    stream). Every call only enqueues work; none synchronises.
+ *  - Layouts: dense, row-major, no strides. Tokens are [B, H, N, d] (head
+ *    index bh = b*H + h). W = ba_packed_words(d) = ceil(d/32).
+ *  - Errors: arguments are validated before any HIP call. A rejected call
+ *    returns BA_ERR_INVALID_ARG (null or misaligned pointer, size < 1,
+ *    inconsistent bias description) or BA_ERR_UNSUPPORTED (d outside
+ *    [1,128], N above BA_MAX_TOKENS, a dtype not listed for that argument)
+ *    and enqueues nothing. A failed kernel launch returns BA_ERR_HIP. Device
+ *    faults surface at the caller's next synchronisation. No C++ exception
+ *    crosses this interface. The library is stateless and re-entrant.
+ *  - Alignment: bits / vq / out / Q / K / V pointers 16-byte aligned; mu,
+ *    vscale and bias pointers 4-byte aligned (fp16 bias: 2-byte).
+ */
+#ifndef BINATTN_H
+#define BINATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BA_OK = 0,
+  BA_ERR_INVALID_ARG = 1,
+  BA_ERR_UNSUPPORTED = 2,
+  BA_ERR_HIP = 3
+} ba_status;
+
+typedef enum { BA_F16 = 0, BA_BF16 = 1, BA_F32 = 2 } ba_dtype;
+
+typedef enum {
+  BA_BIAS_NONE = 0,   /* no bias                                            */
+  BA_BIAS_DENSE = 1,  /* b[h,i,j] from a dense [H,N,N] slice per batch entry */
+  BA_BIAS_RELPOS = 2  /* b[h,i,j] = table[h, idx(i,j)], relative position     */
+} ba_bias_kind;
+
+/* Largest N accepted: the integer P.V sum must stay inside int32
+ * (255 * 127 * N < 2^31). */
+#define BA_MAX_TOKENS 65536
+
+/* Additive bias b_ij on the scores (bias enhancement: zh technical summary
+ * section 2.2 item 2; nl Methodologie 2; it/fr/pt section 2B). The pages
+ * allow a dense, a position-sensitive or a context-aware bias; a context-
+ * aware bias computed elsewhere can be passed as a per-batch DENSE bias.
+ *
+ *  DENSE : data = [H,N,N] elements for batch entry 0, entry b starts at
+ *          data + b*batch_stride elements (batch_stride 0 = one slice shared
+ *          by the whole batch, else >= H*N*N). dtype BA_F32 or BA_F16.
+ *  RELPOS: data = fp32 table [H, (2*grid_h-1)*(2*grid_w-1)]. Tokens
+ *          t >= n_prefix sit on a grid_h x grid_w grid at row
+ *          (t-n_prefix)/grid_w, column (t-n_prefix)%grid_w; the bias of
+ *          query i and key j is table[h, (r_i-r_j+grid_h-1)*(2*grid_w-1)
+ *          + (c_i-c_j+grid_w-1)], and 0 when i or j < n_prefix. Requires
+ *          N == n_prefix + grid_h*grid_w. dtype must be BA_F32.
+ */
+typedef struct {
+  ba_bias_kind kind;
+  const void* data;
+  ba_dtype dtype;
+  int64_t batch_stride;
+  int32_t grid_h, grid_w, n_prefix;
+} ba_bias;
+
+/* W = ceil(d/32): 32-bit words per packed token. Returns 0 for d < 1. */
+int ba_packed_words(int d);
+
+/* Scaled binary representation of Q and K (zh technical summary section 2.2
+ * item 1; nl Methodologie 2; it section 2B; fr section 2B; pt section 2B):
+ * each token x (d channels) becomes sign bits and one scale.
+ *   bits[t, w] bit c%32 of word w = c/32 is 1 iff x_c < 0 (so +0 and -0
+ *   count as +1); bits for c >= d are 0.
+ *   mu[t] = (sum_c |x_c|) / d  (one scale per token).
+ * q, k: [B,H,N,d] fp16 or bf16 (dt), device. qbits, kbits: uint32
+ * [B,H,N,W]; qmu, kmu: float [B,H,N]. */
+ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H,
+                     int N, int d, uint32_t* qbits, float* qmu,
+                     uint32_t* kbits, float* kmu, void* stream);
+
+/* Channel-wise 8-bit V (zh section 2.2 item 3; nl Methodologie 2): for each
+ * (b,h,c), amax = max_j |v_jc| over the N tokens; vq = clamp(rne(v * (127 /
+ * amax)), -127, 127) in float32; vscale = amax / 127; an all-zero channel
+ * gives vq = 0 and vscale = 0.
+ * v: [B,H,N,d] fp16 or bf16; vq: int8 [B,H,N,d]; vscale: float [B,H,d]. */
+ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
+                     int8_t* vq, float* vscale, void* stream);
+
+/* Fused BinaryAttention forward (zh sections 2.1-2.3; nl Methodologie 1-3;
+ * it section 2; fr section 2B; pt section 2B-2C), non-causal, self-attention
+ * (N queries and N keys per head). For each head and query i:
+ *   sigma_ij = d - 2*popcount(qbits_i XOR kbits_j)
+ *   s_ij     = qmu_i * kmu_j * sigma_ij / sqrt(d) + b_ij
+ *   m_i      = max_j s_ij,  p_ij = exp(s_ij - m_i),  l_i = sum_j p_ij
+ *   p8_ij    = rne(255 * p_ij)                  (unsigned 8 bit over [0,1])
+ *   A_ic     = sum_j p8_ij * vq_jc              (exact, int32)
+ *   out_ic   = A_ic * vscale_c / (255 * l_i)    rounded to out_dt
+ * m_i is the exact row maximum (the kernel finds it in a first pass over the
+ * keys), so p8 matches the plain definition up to float rounding.
+ * Inputs are the outputs of ba_pack_qk / ba_quant_v (or equivalent data);
+ * mu may be any non-negative per-token scale (e.g. a learned one).
+ * bias: NULL or kind BA_BIAS_NONE for no bias.
+ * out: [B,H,N,d] of out_dt, which must be BA_F16 or BA_BF16. */
+ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu,
+                           const uint32_t* kbits, const float* kmu,
+                           const int8_t* vq, const float* vscale,
+                           const ba_bias* bias, int B, int H, int N, int d,
+                           void* out, ba_dtype out_dt, void* stream);
+
+/* Integer Hamming similarity for inspection (zh sections 2.1 and 2.2 item 1;
+ * it section 2A; fr section 2A): for heads [bh_begin, bh_begin+bh_count) and
+ * query rows [row_begin, row_begin+row_count),
+ *   sigma[hb, r, j] = d - 2*popcount(qbits[bh_begin+hb, row_begin+r] XOR
+ *                                    kbits[bh_begin+hb, j])
+ * sigma: int32 [bh_count, row_count, N], device. The window must lie inside
+ * [0, B*H) x [0, N). */
+ba_status ba_debug_hamming_scores(const uint32_t* qbits, const uint32_t* kbits,
+                                  int B, int H, int N, int d, int bh_begin,
+                                  int bh_count, int row_begin, int row_count,
+                                  int32_t* sigma, void* stream);
+
+/* Static description of a status code. */
+const char* ba_status_string(ba_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BINATTN_H */

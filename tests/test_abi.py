@@ -1,0 +1,101 @@
+"""The C ABI library loads, exports every symbol include/binattn.h declares,
+and rejects bad arguments before any HIP call (so these run without a GPU:
+every call here is one that validation refuses)."""
+import ctypes
+
+import pytest
+
+import bit_qk_attention_amd as ba
+from bit_qk_attention_amd import ba_bias
+
+OK, INV, UNS = ba.BA_OK, ba.BA_ERR_INVALID_ARG, ba.BA_ERR_UNSUPPORTED
+P = 0x7F0000000000  # fake, 256-byte aligned device addresses (never dereferenced)
+
+
+def A(i):
+    return ctypes.c_void_p(P + i * (1 << 32))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ba.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = ba.header_symbols()
+    assert set(names) == {"ba_packed_words", "ba_pack_qk", "ba_quant_v", "ba_attention_fwd",
+                          "ba_debug_hamming_scores", "ba_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_small_helpers(L):
+    assert [L.ba_packed_words(d) for d in (0, 1, 32, 33, 64, 72, 128)] == [0, 1, 1, 2, 2, 3, 4]
+    for s in range(4):
+        assert isinstance(ba.status_string(s), str)
+    assert ba.status_string(99) == "unknown status"
+
+
+def pack(L, q=A(0), k=A(1), dt=ba.BA_BF16, B=1, H=1, N=8, d=64, qb=A(2), qm=A(3), kb=A(4), km=A(5)):
+    return L.ba_pack_qk(q, k, dt, B, H, N, d, qb, qm, kb, km, None)
+
+
+def test_pack_rejections(L):
+    assert pack(L, q=None) == INV
+    assert pack(L, km=None) == INV
+    assert pack(L, N=0) == INV and pack(L, B=-1) == INV and pack(L, d=0) == INV
+    assert pack(L, d=129) == UNS
+    assert pack(L, N=ba.BA_MAX_TOKENS + 1) == UNS
+    assert pack(L, dt=ba.BA_F32) == UNS and pack(L, dt=7) == UNS
+    assert pack(L, q=ctypes.c_void_p(P + 2)) == INV       # not 16-byte aligned
+    assert pack(L, qm=ctypes.c_void_p(P + 3 * (1 << 32) + 2)) == INV
+    assert pack(L, kb=A(2)) == INV                        # outputs overlap
+
+
+def quant(L, v=A(0), dt=ba.BA_F16, B=1, H=1, N=8, d=64, vq=A(1), vs=A(2)):
+    return L.ba_quant_v(v, dt, B, H, N, d, vq, vs, None)
+
+
+def test_quant_rejections(L):
+    assert quant(L, v=None) == INV and quant(L, vs=None) == INV
+    assert quant(L, H=0) == INV and quant(L, d=200) == UNS and quant(L, dt=ba.BA_F32) == UNS
+    assert quant(L, vq=ctypes.c_void_p(P + 1 * (1 << 32) + 8)) == INV
+    assert quant(L, vq=A(0)) == INV  # output aliases the input
+
+
+def attn(L, bias=None, B=2, H=2, N=16, d=64, out=A(9), out_dt=ba.BA_BF16, **kw):
+    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6))
+    args.update(kw)
+    pb = ctypes.byref(bias) if bias is not None else None
+    return L.ba_attention_fwd(args["qb"], args["qm"], args["kb"], args["km"], args["vq"], args["vs"],
+                              pb, B, H, N, d, out, out_dt, None)
+
+
+def test_attention_rejections(L):
+    assert attn(L, qb=None) == INV and attn(L, out=None) == INV
+    assert attn(L, d=0) == INV and attn(L, d=129) == UNS
+    assert attn(L, N=ba.BA_MAX_TOKENS + 1) == UNS
+    assert attn(L, out_dt=ba.BA_F32) == UNS and attn(L, out_dt=5) == UNS
+    assert attn(L, vs=ctypes.c_void_p(P + 6 * (1 << 32) + 1)) == INV
+    assert attn(L, out=A(5)) == INV  # output aliases vq
+    # dense bias
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_DENSE, None, ba.BA_F32, 0, 0, 0, 0)) == INV
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_DENSE, P + 7 * (1 << 32), ba.BA_BF16, 0, 0, 0, 0)) == UNS
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_DENSE, P + 7 * (1 << 32), ba.BA_F32, 100, 0, 0, 0)) == INV
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_DENSE, P + 9 * (1 << 32) - 64, ba.BA_F32, 0, 0, 0, 0)) == INV
+    # relative-position bias
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F16, 0, 4, 4, 0)) == UNS
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, 0)) == INV
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 0, 16, 0)) == INV
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, -1)) == INV
+    assert attn(L, bias=ba_bias(7, P + 7 * (1 << 32), ba.BA_F32, 0, 0, 0, 0)) == INV
+
+
+def test_hamming_rejections(L):
+    def ham(qb=A(0), kb=A(1), B=1, H=2, N=10, d=64, bh0=0, nbh=2, r0=0, nr=10, sig=A(2)):
+        return L.ba_debug_hamming_scores(qb, kb, B, H, N, d, bh0, nbh, r0, nr, sig, None)
+    assert ham(qb=None) == INV and ham(sig=None) == INV
+    assert ham(nbh=0) == INV and ham(nr=0) == INV
+    assert ham(bh0=1, nbh=2) == INV and ham(r0=5, nr=6) == INV and ham(bh0=-1) == INV
+    assert ham(d=129) == UNS
+    assert ham(sig=A(0)) == INV

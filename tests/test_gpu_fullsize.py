@@ -1,0 +1,44 @@
+"""Full-size workloads in the launch configuration the benchmark times:
+sampled output rows against the oracle, sampled Hamming windows bit-exact,
+and whole-tensor properties (finite, rows are convex combinations of the
+dequantised V, so |out| <= max|v8 * scale|)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_qk_attention_amd as ba
+import oracle
+from gpu_helpers import GpuRun, vmax
+from workloads import WORKLOADS, make
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_sampled(name):
+    inp = make(name)
+    s = inp.spec
+    print(f"[full-size] {name} B={s.B} H={s.H} N={s.N} d={s.d}", flush=True)
+    run = GpuRun(inp)
+    out = run.out.float()
+    assert torch.isfinite(out).all()
+    vq, vs = oracle.quant_v(inp.v, s.dtype)
+    deq_max = float((np.abs(vq).max(axis=2).astype(np.float64) * vs).max())
+    assert out.abs().max().item() <= deq_max * (1 + 1e-2)
+    rng = np.random.default_rng(s.seed)
+    BH = s.B * s.H
+    qb, _ = oracle.pack(inp.q, s.dtype)
+    kb, _ = oracle.pack(inp.k, s.dtype)
+    vm = vmax(inp)
+    for bh in sorted(set([0, BH - 1, int(rng.integers(0, BH))])):
+        for r0 in sorted(set([0, s.N - 8, int(rng.integers(0, s.N - 8))])):
+            ref = oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias,
+                                   bh0=bh, nbh=1, row0=r0, nrows=8)
+            got = out.reshape(BH, s.N, s.d)[bh, r0:r0 + 8].cpu().numpy()
+            err = np.abs(got - ref.out[0]).max() / vm
+            assert err <= TOL, (bh, r0, err)
+            sig = torch.empty((1, 8, s.N), dtype=torch.int32, device="cuda")
+            ba.ba_debug_hamming_scores(run.qbits, run.kbits, s.d, bh, 1, r0, 8, sig)
+            want = oracle.hamming(qb, kb, s.d, bh0=bh, nbh=1, row0=r0, nrows=8)
+            assert np.array_equal(sig.cpu().numpy(), want)
