@@ -1,0 +1,264 @@
+"""Benchmark of the BinaryAttention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
+
+One step = the whole hot path over one batch of synthetic input already
+resident in HBM: ba_pack_qk (sign bits + scales of Q and K), ba_quant_v
+(channel-wise int8 V) and ba_attention_fwd (fused attention), on one stream.
+The headline value is effective attention throughput 4*B*H*N^2*d / t_step
+(d the real head dim), for the DiT-XL/2 512px layer (B=8, H=16, N=1024,
+d=72, dense fp16 bias shared over the batch); the same figures for the
+64x64-token long sequence (B=2, H=16, N=4096, d=64) ride along under
+"secondary". Prints one JSON line (rank 0).
+
+roofline: the fused attention kernel, timed alone with HIP events on the
+stream it runs on: achieved = effective ops per launch / mean launch time,
+against the int8 MFMA dense peak (5.0 POP/s; the effective op count is the
+int8 op count of the P.V and +-1 Q.K products at the real d). traffic: HBM
+bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (profiles/), scaled
+by a copy-kernel calibration, or null if the kernel source changed since.
+
+cpu_baseline: the CPU oracle (plain C, fp64 softmax) on the host cores, on a
+bounded sample of the same workload (leading heads, leading query rows, all
+keys), scaled to the same effective-ops unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, tera-ops/s
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "bit_qk_attention_amd", "csrc", "attention.hip")
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(s) -> int:
+    """HBM bytes one attention launch must move at minimum: packed Q and K
+    (bits + scale), int8 V + scales, the output, and the bias (a shared
+    dense bias once, not per batch element; a relative-position table)."""
+    W = (s.d + 31) // 32
+    BH, N, d = s.B * s.H, s.N, s.d
+    nb = 2 * BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d + 2 * BH * N * d
+    if s.bias.startswith("dense"):
+        esz = 4 if s.bias == "dense_f32" else 2
+        nb += (1 if s.bias_shared else s.B) * s.H * N * N * esz
+    elif s.bias == "relpos":
+        gh, gw = s.grid
+        nb += s.H * (2 * gh - 1) * (2 * gw - 1) * 4
+    return nb
+
+
+def traffic_for(name: str):
+    """Measured HBM bytes per attention launch, if the counters were taken
+    on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"attn_fwd_{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, target_s: float = 12.0):
+    """Time the oracle on a bounded sample: leading heads and query rows."""
+    import oracle
+    import numpy as np
+    s = inp.spec
+    ob = None
+    if inp.bias_kind == 1:
+        ob = oracle.Bias(oracle.BIAS_DENSE, inp.bias_data, inp.bias_dtype, inp.bias_batch_stride)
+    elif inp.bias_kind == 2:
+        ob = oracle.Bias(oracle.BIAS_RELPOS, inp.bias_data, oracle.F32, 0, inp.grid_h, inp.grid_w, inp.n_prefix)
+    # calibrate on a small slice, then size the sample to ~target_s
+    rows = min(s.N, 64)
+    t0 = time.perf_counter()
+    oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=ob, bh0=0, nbh=1, row0=0, nrows=rows)
+    per_row = (time.perf_counter() - t0) / rows
+    total_rows = max(1, int(target_s / max(per_row, 1e-9)))
+    nbh = max(1, min(s.B * s.H, total_rows // s.N))
+    nrows = s.N if total_rows >= s.N else total_rows
+    t0 = time.perf_counter()
+    oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=ob, bh0=0, nbh=nbh, row0=0, nrows=nrows)
+    dt = time.perf_counter() - t0
+    ops = 4.0 * nbh * nrows * s.N * s.d
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS (effective)",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{nbh} head(s) x {nrows} query rows x all {s.N} keys of {s.name} "
+                      f"(pack + quantise + attention), {dt:.1f} s"}
+
+
+class Workload:
+    """Device-resident inputs and outputs of one workload."""
+
+    def __init__(self, name: str):
+        import numpy as np
+        import torch
+        import bit_qk_attention_amd as ba
+        import workloads
+        self.ba, self.torch = ba, torch
+        self.inp = inp = workloads.make(name)
+        s = self.spec = inp.spec
+        tdt = torch.float16 if s.dtype == workloads.F16 else torch.bfloat16
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+        self.q, self.k, self.v = dev(inp.q), dev(inp.k), dev(inp.v)
+        self.bias = None
+        if inp.bias_kind == workloads.BIAS_DENSE:
+            if inp.bias_dtype == workloads.F32:
+                bt = torch.from_numpy(inp.bias_data).cuda()
+            else:
+                bt = torch.from_numpy(inp.bias_data.view(np.int16)).view(torch.float16).cuda()
+            self.bias = ba.Bias(ba.BA_BIAS_DENSE, bt, inp.bias_batch_stride)
+        elif inp.bias_kind == workloads.BIAS_RELPOS:
+            bt = torch.from_numpy(inp.bias_data).cuda()
+            self.bias = ba.Bias(ba.BA_BIAS_RELPOS, bt, 0, inp.grid_h, inp.grid_w, inp.n_prefix)
+        B, H, N, d = s.B, s.H, s.N, s.d
+        W = ba.ba_packed_words(d)
+        self.qbits = torch.empty((B, H, N, W), dtype=torch.int32, device="cuda")
+        self.kbits = torch.empty_like(self.qbits)
+        self.qmu = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        self.kmu = torch.empty_like(self.qmu)
+        self.vq = torch.empty((B, H, N, d), dtype=torch.int8, device="cuda")
+        self.vscale = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+        self.out = torch.empty_like(self.q)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self):
+        ba = self.ba
+        ba.ba_pack_qk(self.q, self.k, self.qbits, self.qmu, self.kbits, self.kmu, self.stream)
+        ba.ba_quant_v(self.v, self.vq, self.vscale, self.stream)
+        self.attn()
+
+    def attn(self):
+        self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
+                                 self.bias, self.out, self.stream)
+
+    def time(self, fn, iters: int, warmup: int) -> float:
+        """Mean ms per call of fn over `iters` calls, HIP events on the stream."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(iters):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+
+def measure(name: str, steps: int, warmup: int) -> dict:
+    import workloads
+    torch = __import__("torch")
+    w = Workload(name)
+    s = w.spec
+    ops = workloads.eff_ops(s)
+    # whole step, bracketed by synchronisation on both sides
+    for _ in range(warmup):
+        w.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(w.stream)
+    for _ in range(steps):
+        w.step()
+    e1.record(w.stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = e0.elapsed_time(e1) / steps
+    # the dominant kernel alone
+    attn_ms = w.time(w.attn, iters=max(steps, 20), warmup=3)
+    nbytes = algorithmic_bytes(s)
+    return {
+        "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
+        "attn_ms": attn_ms, "tops": ops / (step_ms * 1e-3) / 1e12,
+        "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
+        "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
+    }
+
+
+def config_of(s) -> dict:
+    bias = {"none": "none", "dense_f32": "dense fp32 [H,N,N]", "dense_f16": "dense fp16 [H,N,N]",
+            "relpos": f"relative-position table fp32 [H,{(2 * s.grid[0] - 1) * (2 * s.grid[1] - 1)}]"}[s.bias]
+    if s.bias.startswith("dense") and s.bias_shared:
+        bias += " shared over batch"
+    return {"workload": s.name, "B": s.B, "H": s.H, "N": s.N, "d": s.d,
+            "io_dtype": "fp16" if s.dtype == 0 else "bf16", "bias": bias, "about": s.about}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dit_512")
+    ap.add_argument("--secondary", default="long_4k")
+    ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the attention shards by head with no communication; see DESIGN.md)", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import workloads
+    names = list(workloads.WORKLOADS) if args.all else [args.workload]
+    for name in names:
+        r = measure(name, args.steps, args.warmup)
+        s = r["spec"]
+        line = {
+            "metric": "effective attention TOPS (4*B*H*N^2*d / t_step), step = pack Q/K + quantise V + fused attention",
+            "value": round(r["tops"], 3), "unit": "TOPS",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(r["step_ms"], 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int8",
+            "dtype_detail": "Q.K: +-1 signs on fp4 MFMA (exact integer sums); softmax fp32; P.V u8 x int8 -> int32 MFMA",
+            "data": "synthetic (seeded N(0,1) activations of the workload's shape)",
+            "config": config_of(s),
+            "attn_ms": round(r["attn_ms"], 5), "attn_tops": round(r["attn_tops"], 3),
+            "roofline": {
+                "bound": "mfma", "achieved": round(r["attn_tops"], 3), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(r["attn_tops"] / INT8_PEAK_TOPS, 4),
+                "traffic": traffic_for(name),
+                "kernel": "attn_fwd_kernel", "ops_per_launch": r["ops"],
+                "note": "int8 tera-ops/s: effective ops 4*B*H*N^2*d per launch / mean launch time (HIP events)",
+            },
+            "hbm": {"alg_bytes_per_launch": r["alg_bytes"], "achieved_GBs": round(r["attn_gbs"], 1),
+                    "peak_GBs": HBM_PEAK_GBS, "frac": round(r["attn_gbs"] / HBM_PEAK_GBS, 4)},
+        }
+        if not args.all and args.secondary:
+            r2 = measure(args.secondary, args.steps, args.warmup)
+            line["secondary"] = {"config": config_of(r2["spec"]), "value": round(r2["tops"], 3),
+                                 "ms_per_step": round(r2["step_ms"], 5), "attn_ms": round(r2["attn_ms"], 5),
+                                 "attn_tops": round(r2["attn_tops"], 3),
+                                 "frac_int8_peak": round(r2["attn_tops"] / INT8_PEAK_TOPS, 4)}
+        line["cpu_baseline"] = None
+        if not args.all and not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(r["inp"])
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -116,6 +116,7 @@ ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32
     } else if (bias->kind == BA_BIAS_RELPOS) {
       if (bias->dtype != BA_F32) return BA_ERR_UNSUPPORTED;
       if (bias->grid_h < 1 || bias->grid_w < 1 || bias->n_prefix < 0) return BA_ERR_INVALID_ARG;
+      if (bias->grid_w > 256) return BA_ERR_UNSUPPORTED;  // table window must fit LDS
       if ((int64_t)bias->n_prefix + (int64_t)bias->grid_h * bias->grid_w != N) return BA_ERR_INVALID_ARG;
       if (!aligned(bias->data, 4)) return BA_ERR_INVALID_ARG;
       bias_bytes = (int64_t)H * (2 * bias->grid_h - 1) * (2 * bias->grid_w - 1) * 4;

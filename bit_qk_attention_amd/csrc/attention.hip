@@ -2,7 +2,7 @@
 //
 // Method (BinaryAttention: One-Bit QK-Attention for Vision and Diffusion
 // Transformers, gist.science summaries): zh technical summary section 2.1
-// (sign-vector dot product as Hamming distance), section 2.2 items 1-3
+// (sign-vector dot product as a Hamming distance), section 2.2 items 1-3
 // (scaled binary Q/K, additive bias, u8 P and channel-wise int8 V with
 // integer aggregation), section 2.3 (fused, tiled kernel). Same content in
 // nl Methodologie 1-3 and it/fr/pt section 2.
@@ -11,25 +11,30 @@
 // tensor-core MMAs that gfx950 does not have):
 //
 //  * One workgroup = 4 waves = 128 queries of one (batch, head); each wave
-//    owns 32 queries. Keys stream through LDS in tiles of 64.
+//    owns 32 queries. Keys stream through LDS in tiles of 64, double
+//    buffered: the next tile's global loads are in flight while the current
+//    tile is computed, and there is one barrier per tile.
 //  * Q.K similarity on the matrix cores: the +-1 sign vectors are encoded as
 //    fp4 (e2m1: +1 = 0x2, -1 = 0xA, 0 = 0x0) and multiplied with
 //    v_mfma_f32_32x32x64_f8f6f4 (fp4 runs at twice the int8 rate). The sums
-//    are integers |sigma| <= 128, exact in fp32, and equal
-//    d - 2*popcount(q xor k) because padding channels are encoded as 0 on
-//    the query side. The product is formed transposed, S^T = K Q^T, so each
-//    lane holds 16 keys of ONE query: the row max and row sum are in-lane
-//    reductions, and the probabilities already sit in the int8 MFMA operand
-//    layout needed for the next product.
+//    are integers |sigma| <= 128, exact in fp32, equal to
+//    d - 2*popcount(q xor k) because padding channels are 0 on the query
+//    side. The product is formed transposed, S^T = K Q^T, so each lane holds
+//    16 keys of ONE query: the row max and row sum are in-lane reductions
+//    and the probabilities already sit in the int8 MFMA operand layout of the
+//    next product.
 //  * Two passes over the keys: pass 1 finds the exact row max m_i, pass 2
-//    forms p8 = rne(255 * exp(s - m)), the float row sum, and P.V. There is
-//    no rescaling of the integer accumulator at all, and p8 follows the
-//    plain (unblocked) definition up to float rounding.
-//  * P.V on v_mfma_i32_32x32x32_i8, computed as O^T = V^T P^T. gfx950 int8
-//    MFMA is signed x signed, so the u8 probabilities enter as p8 - 128 (a
-//    byte XOR 0x80) and 128 * sum_j v8_jc is added back at the end (exact in
-//    int32). V tiles are transposed into LDS while staged; the per-channel
-//    sums come from the same pass with v_dot4.
+//    forms p8 = rne(255 * exp(s - m)), the float row sum and P.V. The integer
+//    accumulator is never rescaled, and p8 follows the plain (unblocked)
+//    definition up to float rounding.
+//  * P.V on v_mfma_i32_32x32x32_i8 as O^T = V^T P^T. The V^T operand comes
+//    straight from row-major V in LDS through the transposing LDS read
+//    (ds_read_b64_tr_b8: in each 16-lane group, output lane 8h+b receives
+//    byte b of the 8-byte rows addressed by lanes 2k+h, k = 0..7). gfx950
+//    int8 MFMA is signed x signed, so the u8 probabilities enter as p8 - 128
+//    (a byte XOR 0x80) and 128 * sum_j v8_jc is added back at the end; that
+//    column sum is one more MFMA per block with an all-ones operand (exact
+//    in int32).
 //  * Softmax in base 2: x = s*log2(e) - m*log2(e) + log2(255), so a single
 //    v_exp_f32 gives 255*exp(s - m); v_cvt_pk_u8_f32 rounds to nearest even
 //    and clamps to [0, 255].
@@ -43,7 +48,7 @@ constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kQW = 32;            // queries per wave
 constexpr int kQB = kWaves * kQW;  // queries per workgroup
 constexpr int kBC = 64;            // keys per LDS tile (two 32-key MFMA blocks)
-constexpr int kVStride = kBC + 16; // bytes per transposed V row in LDS
+constexpr int kTblMax = 2048;      // floats of relative-position window per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.9943534368588578f;
 
@@ -62,6 +67,9 @@ struct Params {
   int B, H, N, d, W;
   int nqb;          // query blocks per head
   float inv_sqrt_d;
+  int bias_vec;     // dense bias rows are 16-byte aligned (vector loads)
+  int v_vec;        // d % 8 == 0: V tiles copied in 8-byte pieces
+  int relpos_fast;  // relative-position rows never wrap inside 16 keys
   void* out;
 };
 
@@ -72,8 +80,8 @@ __device__ __forceinline__ uint32_t fp4_signs(uint32_t bits, int m) {
   return (((bits >> m) & 0x11111111u) << 3) | 0x22222222u;
 }
 
-// LDS swizzle of the 16-byte fp4 slots of one key row (avoids bank
-// conflicts between the lanes that read the A operand together).
+// LDS swizzle of the 16-byte fp4 slots of one key row (spreads the lanes
+// that read the A operand together over the LDS banks).
 template <int NKB>
 __device__ __forceinline__ int kslot(int key, int slot) {
   if (NKB == 1) return slot ^ ((key >> 4) & 1);
@@ -100,14 +108,27 @@ __device__ __forceinline__ uint16_t to_out(float x) {
   return OUTDT == BA_F16 ? f32_to_f16(x) : f32_to_bf16(x);
 }
 
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+template <int NKB, int NCB, int BIAS>
+struct Smem {
+  static constexpr int DV = 32 * NCB;  // V channels padded to the MFMA block
+  static constexpr int KROW = 32 * NKB;
+  static constexpr int VS = DV + 8;    // bytes per V row in LDS
+  static constexpr int NT = BIAS == BIAS_RELPOS ? kTblMax : 1;
+  uint8_t kx[2][kBC * KROW];
+  uint8_t vr[2][kBC * VS];
+  float mk[2][kBC];
+  float tbl[2][NT];
+};
+
 template <int NKB, int NCB, int BIAS, int OUTDT>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
-  constexpr int DV = 32 * NCB;
-  constexpr int KROW = 32 * NKB;  // bytes of fp4 per key row
-  __shared__ __attribute__((aligned(16))) uint8_t kx_s[kBC * KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t vt_s[DV * kVStride];
-  __shared__ __attribute__((aligned(16))) float muk_s[kBC];
-  __shared__ int colsum_s[DV];
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
+  using S = Smem<NKB, NCB, BIAS>;
+  constexpr int KROW = S::KROW, VS = S::VS;
+  constexpr bool DENSE = BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16;
+  __shared__ __attribute__((aligned(16))) S sm;
 
   const int N = p.N, d = p.d, W = p.W;
   const int tid = threadIdx.x;
@@ -119,9 +140,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
   int u = blockIdx.x;
   if ((nblk & 7) == 0) u = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
   int b, h, qb;
-  if (BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16) {
+  if (DENSE) {
     // batch innermost: the B workgroups that read the same bias rows run
-    // together on one XCD
+    // back to back on one XCD
     b = u % p.B;
     const int r = u / p.B;
     qb = r % p.nqb;
@@ -135,8 +156,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
   const int64_t bh = (int64_t)b * p.H + h;
   const int qi = qb * kQB + wave * kQW + ql;
   const bool qvalid = qi < N;
+  const int qc = qvalid ? qi : N - 1;  // clamped query index for addressing
 
-  // ---- prologue: query operand (fp4 signs, padding channels zero) ----
+  // ---- query operand: fp4 signs, padding channels zero ----
   v8i qop[NKB];
 #pragma unroll
   for (int kk = 0; kk < NKB; ++kk) {
@@ -145,12 +167,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
     v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      uint32_t e = fp4_signs(bits, m);
       uint32_t mask = 0;
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp)
         if (32 * w + m + 4 * pp < d) mask |= 0xFu << (4 * pp);
-      o[m] = (int)(e & mask);
+      o[m] = (int)(fp4_signs(bits, m) & mask);
     }
     qop[kk] = o;
   }
@@ -158,87 +179,203 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
   const float c0 = qmu * p.inv_sqrt_d;  // natural-log units (bias path)
   const float cq = c0 * kLog2e;         // base-2 units (no-bias path)
 
-  int rp = 0, cp = 0;  // relative-position grid coordinates of the query
-  if (BIAS == BIAS_RELPOS && qvalid && qi >= p.n_prefix) {
-    rp = (qi - p.n_prefix) / p.grid_w;
-    cp = (qi - p.n_prefix) % p.grid_w;
-  }
-  const int T = (2 * p.grid_h - 1) * (2 * p.grid_w - 1);
-
   const int ntiles = (N + kBC - 1) / kBC;
   const bool ragged = (N % kBC) != 0;
 
-  // stage one key tile: fp4 signs of K and mu_k
-  auto stage_k = [&](int t) {
-    for (int idx = tid; idx < kBC * 2 * NKB; idx += 256) {
-      const int key = idx / (2 * NKB), w = idx % (2 * NKB);
-      const int j = t * kBC + key;
-      const uint32_t bits = (j < N && w < W) ? p.kbits[(bh * N + j) * W + w] : 0u;
-      u4v o;
-      if (w < W) {
-        o[0] = fp4_signs(bits, 0); o[1] = fp4_signs(bits, 1);
-        o[2] = fp4_signs(bits, 2); o[3] = fp4_signs(bits, 3);
-      } else {
-        o[0] = o[1] = o[2] = o[3] = 0u;
-      }
-      *reinterpret_cast<u4v*>(kx_s + key * KROW + kslot<NKB>(key, w) * 16) = o;
+  // ---- relative-position bookkeeping ----
+  const int gh = p.grid_h, gw = p.grid_w, npre = p.n_prefix;
+  const int T2 = 2 * gw - 1;
+  int q_rr = 0, q_cc = 0;  // grid row/column of this lane's query
+  bool q_grid = false;     // query has a grid position
+  if (BIAS == BIAS_RELPOS && qc >= npre) {
+    q_grid = true;
+    q_rr = (qc - npre) / gw;
+    q_cc = (qc - npre) % gw;
+  }
+  // grid rows spanned by this workgroup's queries
+  int wq_lo = 0, wq_hi = -1;
+  if (BIAS == BIAS_RELPOS) {
+    const int q0 = qb * kQB, q1 = min(qb * kQB + kQB - 1, N - 1);
+    if (q1 >= npre) {
+      wq_lo = (max(q0, npre) - npre) / gw;
+      wq_hi = (q1 - npre) / gw;
+    }
+  }
+  // table rows dr_lo.. of the window tile t needs, and its size in floats
+  auto tbl_window = [&](int t, int& dr_lo, int& count) {
+    const int j0 = t * kBC, j1 = min(t * kBC + kBC - 1, N - 1);
+    dr_lo = 0;
+    count = 0;
+    if (wq_hi < wq_lo || j1 < npre) return;
+    const int rk_lo = (max(j0, npre) - npre) / gw, rk_hi = (j1 - npre) / gw;
+    dr_lo = wq_lo - rk_hi + gh - 1;
+    count = ((wq_hi - rk_lo + gh - 1) - dr_lo + 1) * T2;
+  };
+
+  // ---- staging registers (loaded a tile ahead) ----
+  uint32_t st_k = 0;
+  float st_mk = 0.0f;
+  uint2 st_v[4];
+  float st_t[BIAS == BIAS_RELPOS ? kTblMax / 256 : 1];
+  const int n8 = kBC * d / 8;  // 8-byte pieces of a V tile (v_vec)
+
+  auto load_tile = [&](int t, bool with_v) {
+    const int j0 = t * kBC;
+    if (tid < kBC * 2 * NKB) {
+      const int key = tid / (2 * NKB), w = tid % (2 * NKB);
+      const int j = j0 + key;
+      st_k = (j < N && w < W) ? p.kbits[(bh * N + j) * W + w] : 0u;
     }
     if (tid < kBC) {
-      const int j = t * kBC + tid;
-      muk_s[tid] = j < N ? p.kmu[bh * N + j] : 0.0f;
+      const int j = j0 + tid;
+      st_mk = j < N ? p.kmu[bh * N + j] : 0.0f;
+    }
+    if (with_v && p.v_vec) {
+      const int8_t* src = p.vq + (bh * N + j0) * d;
+      const int64_t rem = (int64_t)(N - j0) * d;  // valid bytes in this tile
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c8 = tid + 256 * r;
+        st_v[r] = make_uint2(0u, 0u);
+        if (c8 < n8 && (int64_t)c8 * 8 < rem) st_v[r] = *reinterpret_cast<const uint2*>(src + (int64_t)c8 * 8);
+      }
+    }
+    if (BIAS == BIAS_RELPOS) {
+      int dr_lo, count;
+      tbl_window(t, dr_lo, count);
+      const float* src = static_cast<const float*>(p.bias) + (int64_t)h * T2 * (2 * gh - 1) + (int64_t)dr_lo * T2;
+#pragma unroll
+      for (int r = 0; r < kTblMax / 256; ++r) {
+        const int x = tid + 256 * r;
+        st_t[r] = x < count ? src[x] : 0.0f;
+      }
     }
   };
 
-  // S^T block (32 keys x 32 queries) of key block kb of the staged tile
-  auto qk_block = [&](int kb) -> v16f {
+  auto store_tile = [&](int t, int buf, bool with_v) {
+    if (tid < kBC * 2 * NKB) {
+      const int key = tid / (2 * NKB), w = tid % (2 * NKB);
+      u4v o;
+      if (w < W) {
+        o[0] = fp4_signs(st_k, 0); o[1] = fp4_signs(st_k, 1);
+        o[2] = fp4_signs(st_k, 2); o[3] = fp4_signs(st_k, 3);
+      } else {
+        o[0] = o[1] = o[2] = o[3] = 0u;
+      }
+      *reinterpret_cast<u4v*>(sm.kx[buf] + key * KROW + kslot<NKB>(key, w) * 16) = o;
+    }
+    if (tid < kBC) sm.mk[buf][tid] = st_mk;
+    if (with_v) {
+      if (p.v_vec) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c8 = tid + 256 * r;
+          if (c8 < n8) {
+            const int off = c8 * 8, row = off / d, col = off % d;
+            *reinterpret_cast<uint2*>(sm.vr[buf] + row * VS + col) = st_v[r];
+          }
+        }
+      } else {
+        // any d: byte copy, rows past N zero
+        const int j0 = t * kBC;
+        for (int x = tid; x < kBC * d; x += 256) {
+          const int row = x / d, col = x % d;
+          const int j = j0 + row;
+          sm.vr[buf][row * VS + col] = j < N ? (uint8_t)p.vq[(bh * N + j) * d + col] : (uint8_t)0;
+        }
+      }
+    }
+    if (BIAS == BIAS_RELPOS) {
+#pragma unroll
+      for (int r = 0; r < kTblMax / 256; ++r) sm.tbl[buf][tid + 256 * r] = st_t[r];
+    }
+  };
+
+  // S^T block (32 keys x 32 queries) of key block kb of buffer buf
+  auto qk_block = [&](int buf, int kb) -> v16f {
     const int key = kb * 32 + key_of_pos(ql);
     v16f s = {};
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
-      const u4v a4 = *reinterpret_cast<const u4v*>(kx_s + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
-      v8i a = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+      const u4v a4 = *reinterpret_cast<const u4v*>(sm.kx[buf] + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
+      const v8i a = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
       s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qop[kk], s, 4, 4, 0, 0, 0, 0);
     }
     return s;
   };
 
-  // score in the units used by the max: t = sigma*mu_k (no bias) or
-  // u = t*c0 + b (natural-log units, bias)
-  auto scores = [&](int t, int kb, const v16f& sig, float* out16) {
-    const int jb = t * kBC + kb * 32 + 16 * g;  // first key of this lane's 16
-    float mk[16];
+  // Scores of this lane's 16 keys in key block kb of tile t:
+  // sigma * mu_k (no bias; the query scale is applied later) or
+  // sigma * mu_k * mu_q / sqrt(d) + b (natural-log units, with bias).
+  auto scores = [&](int t, int buf, int kb, const v16f& sig, float* sc) {
+    const int jl = kb * 32 + 16 * g;  // first key of the lane's 16, in the tile
+    const int jb = t * kBC + jl;
+    const float4* mkp = reinterpret_cast<const float4*>(sm.mk[buf] + jl);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float4 v = *reinterpret_cast<const float4*>(muk_s + kb * 32 + 16 * g + 4 * r);
-      mk[4 * r] = v.x; mk[4 * r + 1] = v.y; mk[4 * r + 2] = v.z; mk[4 * r + 3] = v.w;
+      const float4 m4 = mkp[r];
+      sc[4 * r + 0] = sig[4 * r + 0] * m4.x;
+      sc[4 * r + 1] = sig[4 * r + 1] * m4.y;
+      sc[4 * r + 2] = sig[4 * r + 2] * m4.z;
+      sc[4 * r + 3] = sig[4 * r + 3] * m4.w;
     }
+    if (DENSE) {
+      const int64_t row = (int64_t)b * p.bias_bstride + ((int64_t)h * N + qc) * N;
+      float bv[16];
+      if (p.bias_vec && !(ragged && t == ntiles - 1)) {
+        if (BIAS == BIAS_DENSE_F32) {
+          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.bias) + row + jb);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) out16[i] = sig[i] * mk[i];
-    if (BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16) {
-      const int64_t row = (int64_t)b * p.bias_bstride + ((int64_t)h * N + (qvalid ? qi : 0)) * N;
+          for (int r = 0; r < 4; ++r) {
+            const float4 v = src[r];
+            bv[4 * r] = v.x; bv[4 * r + 1] = v.y; bv[4 * r + 2] = v.z; bv[4 * r + 3] = v.w;
+          }
+        } else {
+          const u4v* src = reinterpret_cast<const u4v*>(static_cast<const uint16_t*>(p.bias) + row + jb);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = min(jb + i, N - 1);
-        float bv;
-        if (BIAS == BIAS_DENSE_F32) bv = static_cast<const float*>(p.bias)[row + j];
-        else bv = f16_to_f32(static_cast<const uint16_t*>(p.bias)[row + j]);
-        out16[i] = __builtin_fmaf(out16[i], c0, bv);
-      }
-    } else if (BIAS == BIAS_RELPOS) {
-      const float* tab = static_cast<const float*>(p.bias) + (int64_t)h * T;
-      const int gw = p.grid_w, npre = p.n_prefix;
-      int jr = 0, jc = 0;
-      if (jb >= npre) { jr = (jb - npre) / gw; jc = (jb - npre) % gw; }
+          for (int r = 0; r < 2; ++r) {
+            const u4v v = src[r];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = jb + i;
-        float bv = 0.0f;
-        if (qvalid && qi >= npre && j >= npre && j < N) {
-          bv = tab[(rp - jr + p.grid_h - 1) * (2 * gw - 1) + (cp - jc + gw - 1)];
+            for (int e = 0; e < 8; ++e) bv[8 * r + e] = f16_to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+          }
         }
-        if (j >= npre) { if (++jc == gw) { jc = 0; ++jr; } }
-        out16[i] = __builtin_fmaf(out16[i], c0, bv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = min(jb + i, N - 1);
+          bv[i] = BIAS == BIAS_DENSE_F32 ? static_cast<const float*>(p.bias)[row + j]
+                                         : f16_to_f32(static_cast<const uint16_t*>(p.bias)[row + j]);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c0, bv[i]);
+    } else if (BIAS == BIAS_RELPOS) {
+      int dr_lo, count;
+      tbl_window(t, dr_lo, count);
+      // local window index = aq - (r_j*T2 + c_j)
+      const int aq = (q_rr + gh - 1 - dr_lo) * T2 + q_cc + gw - 1;
+      const float* tb = sm.tbl[buf];
+      float bv[16];
+      const bool wave_grid = qb * kQB + wave * kQW >= npre;  // no prefix query in this wave
+      if (p.relpos_fast && wave_grid && jb >= npre && !(ragged && t == ntiles - 1)) {
+        // 16 keys on one grid row: a contiguous, reversed window
+        const int g0 = jb - npre;
+        const int base = aq - ((g0 / gw) * T2 + g0 % gw);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bv[i] = tb[base - i];
+      } else {
+        int rj = 0, cj = 0;
+        if (jb >= npre) { rj = (jb - npre) / gw; cj = (jb - npre) % gw; }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = jb + i;
+          const bool on = q_grid && j >= npre && j < N;
+          bv[i] = on ? tb[aq - (rj * T2 + cj)] : 0.0f;
+          if (j >= npre) { if (++cj == gw) { cj = 0; ++rj; } }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c0, bv[i]);
     }
   };
 
@@ -253,119 +390,92 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
   };
 
   // ================= pass 1: exact row maximum =================
-  float mrun = -INFINITY;
+  float m0 = -INFINITY, m1 = -INFINITY;
+  load_tile(0, false);
+  store_tile(0, 0, false);
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    stage_k(t);
-    __syncthreads();
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, false);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const v16f sig = qk_block(kb);
+      const v16f sig = qk_block(buf, kb);
       float sc[16];
-      scores(t, kb, sig, sc);
+      scores(t, buf, kb, sig, sc);
       mask_tail(t, kb, sc);
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mrun = fmaxf(mrun, fmaxf(sc[i], sc[i + 1]));
+      for (int i = 0; i < 16; i += 4) {
+        m0 = fmaxf(m0, fmaxf(sc[i], sc[i + 1]));
+        m1 = fmaxf(m1, fmaxf(sc[i + 2], sc[i + 3]));
+      }
     }
+    if (t + 1 < ntiles) store_tile(t + 1, buf ^ 1, false);
+    __syncthreads();
   }
+  float mrun = fmaxf(m0, m1);
   mrun = fmaxf(mrun, partner32(mrun, lane));
-  // x = score*scale + negm gives log2(255 * exp(s - m))
+  // x = score * scale2 + negm is log2(255 * exp(s - m))
   const float scale2 = (BIAS == BIAS_NONE) ? cq : kLog2e;
   const float negm = __builtin_fmaf(-scale2, mrun, kLog2_255);
 
   // ================= pass 2: u8 P, row sum, integer P.V =================
-  for (int i = tid; i < DV; i += 256) colsum_s[i] = 0;
-  // channels >= d of the transposed V tile stay zero
-  for (int i = tid; i < DV * kVStride / 4; i += 256) reinterpret_cast<uint32_t*>(vt_s)[i] = 0u;
-  float lrun = 0.0f;
-  v16i acc[NCB];
+  float l0 = 0.0f, l1 = 0.0f, l2 = 0.0f, l3 = 0.0f;
+  v16i acc[NCB], cs[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = (v16i){};
-  int csum[3][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  const int d4 = (d + 3) / 4;
-  const int nblk4 = (kBC / 4) * d4;
-  const bool dword_v = (d % 4) == 0;
+  for (int cb = 0; cb < NCB; ++cb) { acc[cb] = (v16i){}; cs[cb] = (v16i){}; }
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  // transposing-read address of this lane for the V^T operand: row
+  // 16*(lane/32) + (lane%16)/2 (+8 for the upper half), column
+  // 16*((lane/16)%2) + 8*(lane%2) (+32 per channel block)
+  const int tr_row = 16 * (lane >> 5) + ((lane & 15) >> 1);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 
+  load_tile(0, true);
+  store_tile(0, 0, true);
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    stage_k(t);
-    // V tile: 4 keys x 4 channels per thread, transposed into vt_s[c][key]
-#pragma unroll
-    for (int rr = 0; rr < 3; ++rr) {
-      const int blk = tid + 256 * rr;
-      if (blk < nblk4) {
-        const int kg = blk / d4, cg = blk % d4;
-        uint32_t r4[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int j = t * kBC + kg * 4 + k;
-          const int8_t* src = p.vq + (bh * N + j) * d + cg * 4;
-          uint32_t wv = 0u;
-          if (j < N) {
-            if (dword_v) {
-              wv = *reinterpret_cast<const uint32_t*>(src);
-            } else {
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                if (cg * 4 + c < d) wv |= (uint32_t)(uint8_t)src[c] << (8 * c);
-            }
-          }
-          r4[k] = wv;
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t o = ((r4[0] >> (8 * c)) & 0xFFu) | (((r4[1] >> (8 * c)) & 0xFFu) << 8) |
-                             (((r4[2] >> (8 * c)) & 0xFFu) << 16) | (((r4[3] >> (8 * c)) & 0xFFu) << 24);
-          const int ch = cg * 4 + c;
-          if (ch < DV) *reinterpret_cast<uint32_t*>(vt_s + ch * kVStride + kg * 4) = o;
-          csum[rr][c] = __builtin_amdgcn_sdot4((int)o, 0x01010101, csum[rr][c], false);
-        }
-      }
-    }
-    __syncthreads();
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, true);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const v16f sig = qk_block(kb);
+      const v16f sig = qk_block(buf, kb);
       float sc[16];
-      scores(t, kb, sig, sc);
+      scores(t, buf, kb, sig, sc);
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], scale2, negm);
       mask_tail(t, kb, sc);  // after the scaling: -inf * 0 would be NaN
       uint32_t pw[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        uint32_t wd = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ex = __builtin_amdgcn_exp2f(sc[4 * r + e]);
-          lrun += ex;
-          wd = __builtin_amdgcn_cvt_pk_u8_f32(ex, e, wd);
-        }
+        const float e0 = __builtin_amdgcn_exp2f(sc[4 * r + 0]);
+        const float e1 = __builtin_amdgcn_exp2f(sc[4 * r + 1]);
+        const float e2 = __builtin_amdgcn_exp2f(sc[4 * r + 2]);
+        const float e3 = __builtin_amdgcn_exp2f(sc[4 * r + 3]);
+        l0 += e0; l1 += e1; l2 += e2; l3 += e3;
+        uint32_t wd = __builtin_amdgcn_cvt_pk_u8_f32(e0, 0, 0u);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(e1, 1, wd);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(e2, 2, wd);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(e3, 3, wd);
         pw[r] = wd ^ 0x80808080u;  // u8 -> s8 (p8 - 128)
       }
       const v4i bop = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+      const uint8_t* vb = sm.vr[buf] + (kb * 32 + tr_row) * VS + tr_col;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const u4v a4 = *reinterpret_cast<const u4v*>(vt_s + (cb * 32 + ql) * kVStride + kb * 32 + 16 * g);
-        const v4i a = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3]};
+        const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + cb * 32));
+        const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + 8 * VS + cb * 32));
+        const v4i a = {lo[0], lo[1], hi[0], hi[1]};
         acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, acc[cb], 0, 0, 0);
+        cs[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, ones, cs[cb], 0, 0, 0);
       }
     }
+    if (t + 1 < ntiles) store_tile(t + 1, buf ^ 1, true);
+    __syncthreads();
   }
 
   // ================= epilogue =================
-#pragma unroll
-  for (int rr = 0; rr < 3; ++rr) {
-    const int blk = tid + 256 * rr;
-    if (blk < nblk4) {
-      const int cg = blk % d4;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (cg * 4 + c < DV) atomicAdd(&colsum_s[cg * 4 + c], csum[rr][c]);
-    }
-  }
+  float lrun = (l0 + l1) + (l2 + l3);
   lrun += partner32(lrun, lane);
-  __syncthreads();
   if (!qvalid) return;
   const float inv_l = 1.0f / lrun;
   uint16_t* outp = static_cast<uint16_t*>(p.out) + (bh * N + qi) * d;
@@ -373,11 +483,21 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = cb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (c < d) {
-        const int a = acc[cb][i] + 128 * colsum_s[c];
-        outp[c] = to_out<OUTDT>((float)a * vs[c] * inv_l);
+    for (int r = 0; r < 4; ++r) {
+      const int c = cb * 32 + 8 * r + 4 * g;  // 4 consecutive channels c..c+3
+      uint16_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = acc[cb][4 * r + e] + 128 * cs[cb][4 * r + e];
+        o[e] = (c + e < d) ? to_out<OUTDT>((float)a * vs[c + e] * inv_l) : (uint16_t)0;
+      }
+      if (c + 3 < d && (d & 3) == 0) {
+        *reinterpret_cast<uint2*>(outp + c) =
+            make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < d) outp[c + e] = o[e];
       }
     }
   }
@@ -413,10 +533,20 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.B = a.B; p.H = a.H; p.N = a.N; p.d = a.d; p.W = (a.d + 31) / 32;
   p.nqb = (a.N + kQB - 1) / kQB;
   p.inv_sqrt_d = (float)(1.0 / sqrt((double)a.d));
+  p.v_vec = (a.d % 8) == 0;
   p.out = a.out;
   int bias = BIAS_NONE;
-  if (a.bias_kind == BA_BIAS_DENSE) bias = a.bias_dtype == BA_F32 ? BIAS_DENSE_F32 : BIAS_DENSE_F16;
-  else if (a.bias_kind == BA_BIAS_RELPOS) bias = BIAS_RELPOS;
+  p.bias_vec = 0;
+  p.relpos_fast = 0;
+  if (a.bias_kind == BA_BIAS_DENSE) {
+    bias = a.bias_dtype == BA_F32 ? BIAS_DENSE_F32 : BIAS_DENSE_F16;
+    const int per16 = a.bias_dtype == BA_F32 ? 4 : 8;  // elements per 16 bytes
+    p.bias_vec = (a.N % per16 == 0) && (a.bias_bstride % per16 == 0) &&
+                 (reinterpret_cast<uintptr_t>(a.bias) % 16 == 0);
+  } else if (a.bias_kind == BA_BIAS_RELPOS) {
+    bias = BIAS_RELPOS;
+    p.relpos_fast = (a.grid_w % 16 == 0) && (a.n_prefix % 16 == 0);
+  }
   const int64_t nblocks = (int64_t)p.nqb * a.B * a.H;
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int ncb = (a.d + 31) / 32;

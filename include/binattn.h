@@ -72,7 +72,8 @@ typedef enum {
  *          (t-n_prefix)/grid_w, column (t-n_prefix)%grid_w; the bias of
  *          query i and key j is table[h, (r_i-r_j+grid_h-1)*(2*grid_w-1)
  *          + (c_i-c_j+grid_w-1)], and 0 when i or j < n_prefix. Requires
- *          N == n_prefix + grid_h*grid_w. dtype must be BA_F32.
+ *          N == n_prefix + grid_h*grid_w. dtype must be BA_F32;
+ *          grid_w <= 256 (else BA_ERR_UNSUPPORTED).
  */
 typedef struct {
   ba_bias_kind kind;

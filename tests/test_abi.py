@@ -89,6 +89,7 @@ def test_attention_rejections(L):
     assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 0, 16, 0)) == INV
     assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, -1)) == INV
     assert attn(L, bias=ba_bias(7, P + 7 * (1 << 32), ba.BA_F32, 0, 0, 0, 0)) == INV
+    assert attn(L, N=257 * 4, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 4, 257, 0)) == UNS
 
 
 def test_hamming_rejections(L):
