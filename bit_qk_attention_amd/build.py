@@ -14,6 +14,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbinattn.so")
 SOURCES = ["api.hip", "prepass.hip", "attention.hip"]
+# attention.hip: fmaxf without NaN canonicalisation (scores are never NaN;
+# masked keys are -inf, which stays honoured)
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -31,7 +34,8 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
     failed = False

@@ -31,10 +31,9 @@
 //    straight from row-major V in LDS through the transposing LDS read
 //    (ds_read_b64_tr_b8: in each 16-lane group, output lane 8h+b receives
 //    byte b of the 8-byte rows addressed by lanes 2k+h, k = 0..7). gfx950
-//    int8 MFMA is signed x signed, so the u8 probabilities enter as p8 - 128
-//    (a byte XOR 0x80) and 128 * sum_j v8_jc is added back at the end; that
-//    column sum is one more MFMA per block with an all-ones operand (exact
-//    in int32).
+//    int8 MFMA is signed x signed and p8 reaches 255, so each block adds
+//    V^T (127 - p8) (127 - p8 = p8 XOR 0x7F as a signed byte) and then
+//    V^T (-127); the accumulator ends at -sum_j p8_j v8_j, exact in int32.
 //  * Softmax in base 2: x = s*log2(e) - m*log2(e) + log2(255), so a single
 //    v_exp_f32 gives 255*exp(s - m); v_cvt_pk_u8_f32 rounds to nearest even
 //    and clamps to [0, 255].
@@ -107,6 +106,11 @@ template <int OUTDT>
 __device__ __forceinline__ uint16_t to_out(float x) {
   return OUTDT == BA_F16 ? f32_to_f16(x) : f32_to_bf16(x);
 }
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
@@ -212,32 +216,46 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     count = ((wq_hi - rk_lo + gh - 1) - dr_lo + 1) * T2;
   };
 
-  // ---- staging registers (loaded a tile ahead) ----
-  uint32_t st_k = 0;
+  // ---- staging (global -> registers a tile ahead -> LDS) ----
+  // Roles are wave-uniform: wave 0 loads the K sign words (lane = key, all
+  // 2*NKB words), wave 1 the key scales, every thread some 8-byte pieces of
+  // the V tile (d % 8 == 0), the same pieces of every tile. Only the last
+  // tile checks for keys past N.
+  uint32_t st_k[2 * NKB];
   float st_mk = 0.0f;
-  uint2 st_v[4];
+  constexpr int NPV = 2 * NCB;  // max 8-byte V pieces per thread (64 keys)
+  uint2 st_v[NPV];
   float st_t[BIAS == BIAS_RELPOS ? kTblMax / 256 : 1];
-  const int n8 = kBC * d / 8;  // 8-byte pieces of a V tile (v_vec)
+  int v_lds[NPV], v_row[NPV];
+  const int n8 = kBC * d / 8;
+#pragma unroll
+  for (int r = 0; r < NPV; ++r) {
+    const int c8 = tid + 256 * r;
+    const int off = c8 * 8, row = off / d, col = off % d;
+    v_row[r] = c8 < n8 ? row : (1 << 30);  // no piece: never loaded or stored
+    v_lds[r] = row * VS + col;
+  }
 
   auto load_tile = [&](int t, bool with_v) {
     const int j0 = t * kBC;
-    if (tid < kBC * 2 * NKB) {
-      const int key = tid / (2 * NKB), w = tid % (2 * NKB);
-      const int j = j0 + key;
-      st_k = (j < N && w < W) ? p.kbits[(bh * N + j) * W + w] : 0u;
-    }
-    if (tid < kBC) {
-      const int j = j0 + tid;
-      st_mk = j < N ? p.kmu[bh * N + j] : 0.0f;
+    const bool last = ragged && t == ntiles - 1;
+    if (wave == 0) {
+      const int j = j0 + lane;
+      const uint32_t* src = p.kbits + (bh * N + j) * W;
+#pragma unroll
+      for (int w = 0; w < 2 * NKB; ++w)
+        st_k[w] = (w < W && (!last || j < N)) ? src[w] : 0u;
+    } else if (wave == 1) {
+      const int j = j0 + lane;
+      st_mk = (!last || j < N) ? p.kmu[bh * N + j] : 0.0f;
     }
     if (with_v && p.v_vec) {
-      const int8_t* src = p.vq + (bh * N + j0) * d;
-      const int64_t rem = (int64_t)(N - j0) * d;  // valid bytes in this tile
+      const int8_t* src = p.vq + (bh * N + j0) * d + tid * 8;
+      const int nrows = last ? N - j0 : kBC;  // valid rows in this tile
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c8 = tid + 256 * r;
+      for (int r = 0; r < NPV; ++r) {
         st_v[r] = make_uint2(0u, 0u);
-        if (c8 < n8 && (int64_t)c8 * 8 < rem) st_v[r] = *reinterpret_cast<const uint2*>(src + (int64_t)c8 * 8);
+        if (v_row[r] < nrows) st_v[r] = *reinterpret_cast<const uint2*>(src + 2048 * r);
       }
     }
     if (BIAS == BIAS_RELPOS) {
@@ -253,28 +271,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   };
 
   auto store_tile = [&](int t, int buf, bool with_v) {
-    if (tid < kBC * 2 * NKB) {
-      const int key = tid / (2 * NKB), w = tid % (2 * NKB);
-      u4v o;
-      if (w < W) {
-        o[0] = fp4_signs(st_k, 0); o[1] = fp4_signs(st_k, 1);
-        o[2] = fp4_signs(st_k, 2); o[3] = fp4_signs(st_k, 3);
-      } else {
-        o[0] = o[1] = o[2] = o[3] = 0u;
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < 2 * NKB; ++w) {
+        u4v o;
+        o[0] = fp4_signs(st_k[w], 0); o[1] = fp4_signs(st_k[w], 1);
+        o[2] = fp4_signs(st_k[w], 2); o[3] = fp4_signs(st_k[w], 3);
+        *reinterpret_cast<u4v*>(sm.kx[buf] + lane * KROW + kslot<NKB>(lane, w) * 16) = o;
       }
-      *reinterpret_cast<u4v*>(sm.kx[buf] + key * KROW + kslot<NKB>(key, w) * 16) = o;
+    } else if (wave == 1) {
+      sm.mk[buf][lane] = st_mk;
     }
-    if (tid < kBC) sm.mk[buf][tid] = st_mk;
     if (with_v) {
       if (p.v_vec) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c8 = tid + 256 * r;
-          if (c8 < n8) {
-            const int off = c8 * 8, row = off / d, col = off % d;
-            *reinterpret_cast<uint2*>(sm.vr[buf] + row * VS + col) = st_v[r];
-          }
-        }
+        for (int r = 0; r < NPV; ++r)
+          if (v_row[r] < kBC) *reinterpret_cast<uint2*>(sm.vr[buf] + v_lds[r]) = st_v[r];
       } else {
         // any d: byte copy, rows past N zero
         const int j0 = t * kBC;
@@ -307,7 +319,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // Scores of this lane's 16 keys in key block kb of tile t:
   // sigma * mu_k (no bias; the query scale is applied later) or
   // sigma * mu_k * mu_q / sqrt(d) + b (natural-log units, with bias).
-  auto scores = [&](int t, int buf, int kb, const v16f& sig, float* sc) {
+  // TAIL: the last tile when N is not a multiple of the tile; keys past N
+  // get -inf.
+  auto scores = [&](auto tail, int t, int buf, int kb, const v16f& sig, float* sc) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const bool last = ragged && t == ntiles - 1;  // keys past N in this tile
     const int jl = kb * 32 + 16 * g;  // first key of the lane's 16, in the tile
     const int jb = t * kBC + jl;
     const float4* mkp = reinterpret_cast<const float4*>(sm.mk[buf] + jl);
@@ -322,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     if (DENSE) {
       const int64_t row = (int64_t)b * p.bias_bstride + ((int64_t)h * N + qc) * N;
       float bv[16];
-      if (p.bias_vec && !(ragged && t == ntiles - 1)) {
+      if (!last && p.bias_vec) {
         if (BIAS == BIAS_DENSE_F32) {
           const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.bias) + row + jb);
 #pragma unroll
@@ -357,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       const float* tb = sm.tbl[buf];
       float bv[16];
       const bool wave_grid = qb * kQB + wave * kQW >= npre;  // no prefix query in this wave
-      if (p.relpos_fast && wave_grid && jb >= npre && !(ragged && t == ntiles - 1)) {
+      if (!last && p.relpos_fast && wave_grid && jb >= npre) {
         // 16 keys on one grid row: a contiguous, reversed window
         const int g0 = jb - npre;
         const int base = aq - ((g0 / gw) * T2 + g0 % gw);
@@ -377,41 +393,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c0, bv[i]);
     }
-  };
-
-  // keys past N in the last (ragged) tile get -inf
-  auto mask_tail = [&](int t, int kb, float* v16) {
-    if (ragged && t == ntiles - 1) {
-      const int jb = t * kBC + kb * 32 + 16 * g;
+    if (TAIL) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (jb + i >= N) v16[i] = -INFINITY;
+        if (jb + i >= N) sc[i] = -INFINITY;
     }
   };
 
   // ================= pass 1: exact row maximum =================
   float m0 = -INFINITY, m1 = -INFINITY;
+  auto max16 = [&](const float* sc) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      m0 = fmaxf(fmaxf(m0, sc[i]), sc[i + 1]);
+      m1 = fmaxf(fmaxf(m1, sc[i + 2]), sc[i + 3]);
+    }
+  };
+  auto pass1_tile = [&](auto tail, int t) {
+    const int buf = t & 1;
+    const v16f sig0 = qk_block(buf, 0);
+    const v16f sig1 = qk_block(buf, 1);
+    float sc[16];
+    scores(tail, t, buf, 0, sig0, sc);
+    max16(sc);
+    scores(tail, t, buf, 1, sig1, sc);
+    max16(sc);
+  };
   load_tile(0, false);
   store_tile(0, 0, false);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  const int nfull = ragged ? ntiles - 1 : ntiles;
+  for (int t = 0; t < nfull; ++t) {
     if (t + 1 < ntiles) load_tile(t + 1, false);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const v16f sig = qk_block(buf, kb);
-      float sc[16];
-      scores(t, buf, kb, sig, sc);
-      mask_tail(t, kb, sc);
-#pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        m0 = fmaxf(m0, fmaxf(sc[i], sc[i + 1]));
-        m1 = fmaxf(m1, fmaxf(sc[i + 2], sc[i + 3]));
-      }
-    }
-    if (t + 1 < ntiles) store_tile(t + 1, buf ^ 1, false);
+    pass1_tile(BoolC<false>(), t);
+    if (t + 1 < ntiles) store_tile(t + 1, (t & 1) ^ 1, false);
     __syncthreads();
   }
+  if (ragged) pass1_tile(BoolC<true>(), ntiles - 1);
+
   float mrun = fmaxf(m0, m1);
   mrun = fmaxf(mrun, partner32(mrun, lane));
   // x = score * scale2 + negm is log2(255 * exp(s - m))
@@ -420,64 +439,85 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
 
   // ================= pass 2: u8 P, row sum, integer P.V =================
   float l0 = 0.0f, l1 = 0.0f, l2 = 0.0f, l3 = 0.0f;
-  v16i acc[NCB], cs[NCB];
+  v16i acc[NCB];  // ends at -sum_j p8_j v8_j
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) { acc[cb] = (v16i){}; cs[cb] = (v16i){}; }
-  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = (v16i){};
+  const v4i m127 = {(int)0x81818181, (int)0x81818181, (int)0x81818181, (int)0x81818181};  // -127 bytes
   // transposing-read address of this lane for the V^T operand: row
   // 16*(lane/32) + (lane%16)/2 (+8 for the upper half), column
   // 16*((lane/16)%2) + 8*(lane%2) (+32 per channel block)
   const int tr_row = 16 * (lane >> 5) + ((lane & 15) >> 1);
   const int tr_col = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 
+  // u8 probabilities of one key block, as the s8 MFMA operand 127 - p8.
+  // Tail keys (past N) are masked after the scaling: -inf * 0 would be NaN.
+  auto probs = [&](auto tail, int t, int kb, float* sc) -> v4i {
+    constexpr bool TAIL = decltype(tail)::value;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], scale2, negm);
+    if (TAIL) {
+      const int jb = t * kBC + kb * 32 + 16 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (jb + i >= N) sc[i] = -INFINITY;
+    }
+    uint32_t pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e0 = __builtin_amdgcn_exp2f(sc[4 * r + 0]);
+      const float e1 = __builtin_amdgcn_exp2f(sc[4 * r + 1]);
+      const float e2 = __builtin_amdgcn_exp2f(sc[4 * r + 2]);
+      const float e3 = __builtin_amdgcn_exp2f(sc[4 * r + 3]);
+      l0 += e0; l1 += e1; l2 += e2; l3 += e3;
+      uint32_t wd = __builtin_amdgcn_cvt_pk_u8_f32(e0, 0, 0u);
+      wd = __builtin_amdgcn_cvt_pk_u8_f32(e1, 1, wd);
+      wd = __builtin_amdgcn_cvt_pk_u8_f32(e2, 2, wd);
+      wd = __builtin_amdgcn_cvt_pk_u8_f32(e3, 3, wd);
+      pw[r] = wd ^ 0x7F7F7F7Fu;  // u8 p8 -> s8 (127 - p8)
+    }
+    return (v4i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+  };
+  // P.V of one key block: acc += V^T (127 - p8) + V^T (-127)
+  auto pv = [&](int buf, int kb, const v4i& bop) {
+    const uint8_t* vb = sm.vr[buf] + (kb * 32 + tr_row) * VS + tr_col;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + cb * 32));
+      const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + 8 * VS + cb * 32));
+      const v4i a = {lo[0], lo[1], hi[0], hi[1]};
+      acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, m127, acc[cb], 0, 0, 0);
+    }
+  };
+  auto pass2_tile = [&](auto tail, int t) {
+    const int buf = t & 1;
+    const v16f sig0 = qk_block(buf, 0);
+    const v16f sig1 = qk_block(buf, 1);
+    float sc[16];
+    scores(BoolC<false>(), t, buf, 0, sig0, sc);
+    const v4i p0 = probs(tail, t, 0, sc);
+    pv(buf, 0, p0);
+    scores(BoolC<false>(), t, buf, 1, sig1, sc);
+    const v4i p1 = probs(tail, t, 1, sc);
+    pv(buf, 1, p1);
+  };
+
   load_tile(0, true);
   store_tile(0, 0, true);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  for (int t = 0; t < nfull; ++t) {
     if (t + 1 < ntiles) load_tile(t + 1, true);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const v16f sig = qk_block(buf, kb);
-      float sc[16];
-      scores(t, buf, kb, sig, sc);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], scale2, negm);
-      mask_tail(t, kb, sc);  // after the scaling: -inf * 0 would be NaN
-      uint32_t pw[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e0 = __builtin_amdgcn_exp2f(sc[4 * r + 0]);
-        const float e1 = __builtin_amdgcn_exp2f(sc[4 * r + 1]);
-        const float e2 = __builtin_amdgcn_exp2f(sc[4 * r + 2]);
-        const float e3 = __builtin_amdgcn_exp2f(sc[4 * r + 3]);
-        l0 += e0; l1 += e1; l2 += e2; l3 += e3;
-        uint32_t wd = __builtin_amdgcn_cvt_pk_u8_f32(e0, 0, 0u);
-        wd = __builtin_amdgcn_cvt_pk_u8_f32(e1, 1, wd);
-        wd = __builtin_amdgcn_cvt_pk_u8_f32(e2, 2, wd);
-        wd = __builtin_amdgcn_cvt_pk_u8_f32(e3, 3, wd);
-        pw[r] = wd ^ 0x80808080u;  // u8 -> s8 (p8 - 128)
-      }
-      const v4i bop = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
-      const uint8_t* vb = sm.vr[buf] + (kb * 32 + tr_row) * VS + tr_col;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + cb * 32));
-        const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + 8 * VS + cb * 32));
-        const v4i a = {lo[0], lo[1], hi[0], hi[1]};
-        acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, acc[cb], 0, 0, 0);
-        cs[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, ones, cs[cb], 0, 0, 0);
-      }
-    }
-    if (t + 1 < ntiles) store_tile(t + 1, buf ^ 1, true);
+    pass2_tile(BoolC<false>(), t);
+    if (t + 1 < ntiles) store_tile(t + 1, (t & 1) ^ 1, true);
     __syncthreads();
   }
+  if (ragged) pass2_tile(BoolC<true>(), ntiles - 1);
 
   // ================= epilogue =================
   float lrun = (l0 + l1) + (l2 + l3);
   lrun += partner32(lrun, lane);
   if (!qvalid) return;
-  const float inv_l = 1.0f / lrun;
+  const float ninv_l = -1.0f / lrun;  // the accumulator holds -A
   uint16_t* outp = static_cast<uint16_t*>(p.out) + (bh * N + qi) * d;
   const float* vs = p.vscale + bh * d;
 #pragma unroll
@@ -488,8 +528,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       uint16_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int a = acc[cb][4 * r + e] + 128 * cs[cb][4 * r + e];
-        o[e] = (c + e < d) ? to_out<OUTDT>((float)a * vs[c + e] * inv_l) : (uint16_t)0;
+        o[e] = (c + e < d) ? to_out<OUTDT>((float)acc[cb][4 * r + e] * vs[c + e] * ninv_l) : (uint16_t)0;
       }
       if (c + 3 < d && (d & 3) == 0) {
         *reinterpret_cast<uint2*>(outp + c) =
