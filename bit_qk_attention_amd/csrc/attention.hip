@@ -67,7 +67,8 @@ struct Params {
   int nqb;          // query blocks per head
   float inv_sqrt_d;
   int bias_vec;     // dense bias rows are 16-byte aligned (vector loads)
-  int v_vec;        // d % 8 == 0: V tiles copied in 8-byte pieces
+  int v_dma;        // V tiles go global -> LDS directly (16-byte pieces)
+  int v_swz_shift;  // 16-byte chunk swizzle of V rows: -1 none, else shift
   int relpos_fast;  // relative-position rows never wrap inside 16 keys
   void* out;
 };
@@ -115,24 +116,37 @@ struct BoolC {
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// One LDS tile buffer. The kernel keeps two as separate __shared__ objects
+// and selects them at compile time, so the compiler can tell a DMA into one
+// from reads of the other and does not wait for the prefetch.
 template <int NKB, int NCB, int BIAS>
-struct Smem {
+struct TileBuf {
   static constexpr int DV = 32 * NCB;  // V channels padded to the MFMA block
   static constexpr int KROW = 32 * NKB;
-  static constexpr int VS = DV + 8;    // bytes per V row in LDS
+  static constexpr int VS = DV + 8;    // bytes per V row, generic (byte-copy) layout
   static constexpr int NT = BIAS == BIAS_RELPOS ? kTblMax : 1;
-  uint8_t kx[2][kBC * KROW];
-  uint8_t vr[2][kBC * VS];
-  float mk[2][kBC];
-  float tbl[2][NT];
+  uint8_t kx[kBC * KROW];
+  uint8_t vr[kBC * VS];  // also holds a 64 x d tile at stride d (d <= DV)
+  float mk[kBC];
+  float tbl[NT];
 };
 
 template <int NKB, int NCB, int BIAS, int OUTDT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
-  using S = Smem<NKB, NCB, BIAS>;
+  using S = TileBuf<NKB, NCB, BIAS>;
   constexpr int KROW = S::KROW, VS = S::VS;
   constexpr bool DENSE = BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16;
-  __shared__ __attribute__((aligned(16))) S sm;
+  __shared__ __attribute__((aligned(16))) S sb0;
+  __shared__ __attribute__((aligned(16))) S sb1;
+  auto pick = [&](auto bufc) -> S& {
+    if constexpr (decltype(bufc)::value == 0) return sb0;
+    else return sb1;
+  };
 
   const int N = p.N, d = p.d, W = p.W;
   const int tid = threadIdx.x;
@@ -216,100 +230,132 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     count = ((wq_hi - rk_lo + gh - 1) - dr_lo + 1) * T2;
   };
 
-  // ---- staging (global -> registers a tile ahead -> LDS) ----
-  // Roles are wave-uniform: wave 0 loads the K sign words (lane = key, all
-  // 2*NKB words), wave 1 the key scales, every thread some 8-byte pieces of
-  // the V tile (d % 8 == 0), the same pieces of every tile. Only the last
-  // tile checks for keys past N.
-  uint32_t st_k[2 * NKB];
-  float st_mk = 0.0f;
-  constexpr int NPV = 2 * NCB;  // max 8-byte V pieces per thread (64 keys)
-  uint2 st_v[NPV];
-  float st_t[BIAS == BIAS_RELPOS ? kTblMax / 256 : 1];
-  int v_lds[NPV], v_row[NPV];
-  const int n8 = kBC * d / 8;
+  // ---- staging ----
+  // Full tiles: V, the key scales and the relative-position window rows go
+  // global -> LDS with global_load_lds (no registers, no VALU); wave 0 loads
+  // the K sign words into registers a tile ahead and expands them to fp4 in
+  // LDS. The ragged last tile is staged synchronously with bounds checks.
+  //
+  // V layout in LDS (v_dma): row stride d; with v_swz_shift >= 0 the 16-byte
+  // chunks of row r are permuted, chunk c stored at c ^ vswz(r), so that the
+  // 8 consecutive rows one transposing read touches fall in distinct banks.
+  // The permutation is applied on the global side (each lane of a DMA picks
+  // its source chunk). Generic d (not v_dma): stride VS, no swizzle.
+  const int vstride = p.v_dma ? d : VS;
+  const int nchk = d >> 4;  // 16-byte chunks per row (swizzled layouts)
+  auto vswz = [&](int row) -> int {
+    return p.v_swz_shift >= 0 ? ((row >> p.v_swz_shift) & (nchk - 1)) : 0;
+  };
+  auto vaddr = [&](int row, int col) -> int {  // LDS byte offset of V[row][col]
+    return p.v_swz_shift >= 0 ? row * vstride + 16 * ((col >> 4) ^ vswz(row)) + (col & 15)
+                              : row * vstride + col;
+  };
+  // DMA sources: wave w fills the 1 KB LDS chunks w and w + 4 of the tile
+  int v_src[2];
+  bool v_on[2];
 #pragma unroll
-  for (int r = 0; r < NPV; ++r) {
-    const int c8 = tid + 256 * r;
-    const int off = c8 * 8, row = off / d, col = off % d;
-    v_row[r] = c8 < n8 ? row : (1 << 30);  // no piece: never loaded or stored
-    v_lds[r] = row * VS + col;
+  for (int i = 0; i < 2; ++i) {
+    const int dst = 1024 * (wave + 4 * i) + 16 * lane;  // LDS byte of this lane
+    v_on[i] = dst < kBC * d;
+    const int row = dst / max(d, 1), pc = (dst % max(d, 1)) >> 4;
+    v_src[i] = p.v_swz_shift >= 0 ? row * d + 16 * (pc ^ vswz(row)) : dst;
   }
+  typedef __attribute__((address_space(1))) const void gptr_t;
+  typedef __attribute__((address_space(3))) void lptr_t;
 
-  auto load_tile = [&](int t, bool with_v) {
-    const int j0 = t * kBC;
-    const bool last = ragged && t == ntiles - 1;
+  uint32_t st_k[2 * NKB];
+  auto load_k = [&](int t) {
     if (wave == 0) {
-      const int j = j0 + lane;
+      const bool last = ragged && t == ntiles - 1;
+      const int j = t * kBC + lane;
       const uint32_t* src = p.kbits + (bh * N + j) * W;
 #pragma unroll
-      for (int w = 0; w < 2 * NKB; ++w)
-        st_k[w] = (w < W && (!last || j < N)) ? src[w] : 0u;
-    } else if (wave == 1) {
-      const int j = j0 + lane;
-      st_mk = (!last || j < N) ? p.kmu[bh * N + j] : 0.0f;
-    }
-    if (with_v && p.v_vec) {
-      const int8_t* src = p.vq + (bh * N + j0) * d + tid * 8;
-      const int nrows = last ? N - j0 : kBC;  // valid rows in this tile
-#pragma unroll
-      for (int r = 0; r < NPV; ++r) {
-        st_v[r] = make_uint2(0u, 0u);
-        if (v_row[r] < nrows) st_v[r] = *reinterpret_cast<const uint2*>(src + 2048 * r);
-      }
-    }
-    if (BIAS == BIAS_RELPOS) {
-      int dr_lo, count;
-      tbl_window(t, dr_lo, count);
-      const float* src = static_cast<const float*>(p.bias) + (int64_t)h * T2 * (2 * gh - 1) + (int64_t)dr_lo * T2;
-#pragma unroll
-      for (int r = 0; r < kTblMax / 256; ++r) {
-        const int x = tid + 256 * r;
-        st_t[r] = x < count ? src[x] : 0.0f;
-      }
+      for (int w = 0; w < 2 * NKB; ++w) st_k[w] = (w < W && (!last || j < N)) ? src[w] : 0u;
     }
   };
-
-  auto store_tile = [&](int t, int buf, bool with_v) {
+  auto store_k = [&](auto bufc) {
+    S& sb = pick(bufc);
     if (wave == 0) {
 #pragma unroll
       for (int w = 0; w < 2 * NKB; ++w) {
         u4v o;
         o[0] = fp4_signs(st_k[w], 0); o[1] = fp4_signs(st_k[w], 1);
         o[2] = fp4_signs(st_k[w], 2); o[3] = fp4_signs(st_k[w], 3);
-        *reinterpret_cast<u4v*>(sm.kx[buf] + lane * KROW + kslot<NKB>(lane, w) * 16) = o;
+        *reinterpret_cast<u4v*>(sb.kx + lane * KROW + kslot<NKB>(lane, w) * 16) = o;
       }
-    } else if (wave == 1) {
-      sm.mk[buf][lane] = st_mk;
-    }
-    if (with_v) {
-      if (p.v_vec) {
-#pragma unroll
-        for (int r = 0; r < NPV; ++r)
-          if (v_row[r] < kBC) *reinterpret_cast<uint2*>(sm.vr[buf] + v_lds[r]) = st_v[r];
-      } else {
-        // any d: byte copy, rows past N zero
-        const int j0 = t * kBC;
-        for (int x = tid; x < kBC * d; x += 256) {
-          const int row = x / d, col = x % d;
-          const int j = j0 + row;
-          sm.vr[buf][row * VS + col] = j < N ? (uint8_t)p.vq[(bh * N + j) * d + col] : (uint8_t)0;
-        }
-      }
-    }
-    if (BIAS == BIAS_RELPOS) {
-#pragma unroll
-      for (int r = 0; r < kTblMax / 256; ++r) sm.tbl[buf][tid + 256 * r] = st_t[r];
     }
   };
+  // relative-position window rows of tile t (always in bounds of the table)
+  auto dma_tbl = [&](int t, auto bufc) {
+    S& sb = pick(bufc);
+    if (BIAS == BIAS_RELPOS) {
+      int dr_lo, count;
+      tbl_window(t, dr_lo, count);
+      const float* src = static_cast<const float*>(p.bias) + (int64_t)h * T2 * (2 * gh - 1) + (int64_t)dr_lo * T2;
+#pragma unroll
+      for (int i = 0; i < kTblMax / 256; ++i) {
+        const int x0 = 64 * (wave + 4 * i);
+        if (x0 + lane < count)
+          __builtin_amdgcn_global_load_lds((gptr_t*)(src + x0 + lane), (lptr_t*)(sb.tbl + x0), 4, 0, 0);
+      }
+    }
+  };
+  // full tile t (all keys < N): V, mu_k and the table window by DMA
+  auto dma_tile = [&](int t, auto bufc, bool with_v) {
+    S& sb = pick(bufc);
+    const int j0 = t * kBC;
+    if (with_v && p.v_dma) {
+      const int8_t* src = p.vq + (bh * N + j0) * d;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (v_on[i])
+          __builtin_amdgcn_global_load_lds((gptr_t*)(src + v_src[i]), (lptr_t*)(sb.vr + 1024 * (wave + 4 * i)), 16, 0, 0);
+    }
+    if (wave == 1)
+      __builtin_amdgcn_global_load_lds((gptr_t*)(p.kmu + bh * N + j0 + lane), (lptr_t*)(sb.mk), 4, 0, 0);
+    dma_tbl(t, bufc);
+  };
+  // V tile t through registers, rows past N zero (ragged tile; any d)
+  auto copy_v_checked = [&](int t, auto bufc) {
+    S& sb = pick(bufc);
+    const int j0 = t * kBC;
+    if (p.v_dma) {
+      for (int x = tid; x < kBC * d / 8; x += 256) {
+        const int off = 8 * x, row = off / d, col = off % d;
+        uint2 v = make_uint2(0u, 0u);
+        if (j0 + row < N) v = *reinterpret_cast<const uint2*>(p.vq + (bh * N + j0) * d + off);
+        *reinterpret_cast<uint2*>(sb.vr + vaddr(row, col)) = v;
+      }
+    } else {
+      for (int x = tid; x < kBC * d; x += 256) {
+        const int row = x / d, col = x % d;
+        const int j = j0 + row;
+        sb.vr[row * VS + col] = j < N ? (uint8_t)p.vq[(bh * N + j) * d + col] : (uint8_t)0;
+      }
+    }
+  };
+  // synchronous staging of tile t with bounds checks (the ragged tile)
+  auto stage_checked = [&](int t, auto bufc, bool with_v) {
+    S& sb = pick(bufc);
+    load_k(t);
+    store_k(bufc);
+    if (wave == 1) {
+      const int j = t * kBC + lane;
+      sb.mk[lane] = j < N ? p.kmu[bh * N + j] : 0.0f;
+    }
+    if (with_v) copy_v_checked(t, bufc);
+    dma_tbl(t, bufc);
+  };
+  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
-  // S^T block (32 keys x 32 queries) of key block kb of buffer buf
-  auto qk_block = [&](int buf, int kb) -> v16f {
+  // S^T block (32 keys x 32 queries) of key block kb of the selected buffer
+  auto qk_block = [&](auto bufc, int kb) -> v16f {
+    S& sb = pick(bufc);
     const int key = kb * 32 + key_of_pos(ql);
     v16f s = {};
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
-      const u4v a4 = *reinterpret_cast<const u4v*>(sm.kx[buf] + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
+      const u4v a4 = *reinterpret_cast<const u4v*>(sb.kx + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
       const v8i a = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
       s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qop[kk], s, 4, 4, 0, 0, 0, 0);
     }
@@ -321,12 +367,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // sigma * mu_k * mu_q / sqrt(d) + b (natural-log units, with bias).
   // TAIL: the last tile when N is not a multiple of the tile; keys past N
   // get -inf.
-  auto scores = [&](auto tail, int t, int buf, int kb, const v16f& sig, float* sc) {
+  auto scores = [&](auto tail, int t, auto bufc, int kb, const v16f& sig, float* sc) {
+    S& sb = pick(bufc);
     constexpr bool TAIL = decltype(tail)::value;
     const bool last = ragged && t == ntiles - 1;  // keys past N in this tile
     const int jl = kb * 32 + 16 * g;  // first key of the lane's 16, in the tile
     const int jb = t * kBC + jl;
-    const float4* mkp = reinterpret_cast<const float4*>(sm.mk[buf] + jl);
+    const float4* mkp = reinterpret_cast<const float4*>(sb.mk + jl);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float4 m4 = mkp[r];
@@ -370,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       tbl_window(t, dr_lo, count);
       // local window index = aq - (r_j*T2 + c_j)
       const int aq = (q_rr + gh - 1 - dr_lo) * T2 + q_cc + gw - 1;
-      const float* tb = sm.tbl[buf];
+      const float* tb = sb.tbl;
       float bv[16];
       const bool wave_grid = qb * kQB + wave * kQW >= npre;  // no prefix query in this wave
       if (!last && p.relpos_fast && wave_grid && jb >= npre) {
@@ -409,27 +456,68 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       m1 = fmaxf(fmaxf(m1, sc[i + 2]), sc[i + 3]);
     }
   };
-  auto pass1_tile = [&](auto tail, int t) {
-    const int buf = t & 1;
-    const v16f sig0 = qk_block(buf, 0);
-    const v16f sig1 = qk_block(buf, 1);
+  auto pass1_tile = [&](auto tail, int t, auto bufc) {
+    const v16f sig0 = qk_block(bufc, 0);
+    const v16f sig1 = qk_block(bufc, 1);
     float sc[16];
-    scores(tail, t, buf, 0, sig0, sc);
+    scores(tail, t, bufc, 0, sig0, sc);
     max16(sc);
-    scores(tail, t, buf, 1, sig1, sc);
+    scores(tail, t, bufc, 1, sig1, sc);
     max16(sc);
   };
-  load_tile(0, false);
-  store_tile(0, 0, false);
-  __syncthreads();
   const int nfull = ragged ? ntiles - 1 : ntiles;
-  for (int t = 0; t < nfull; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1, false);
-    pass1_tile(BoolC<false>(), t);
-    if (t + 1 < ntiles) store_tile(t + 1, (t & 1) ^ 1, false);
+  // tile 0 -> buffer 0
+  auto stage_first = [&](bool with_v) {
+    if (nfull > 0) {
+      dma_tile(0, IntC<0>(), with_v);
+      if (with_v && !p.v_dma) copy_v_checked(0, IntC<0>());
+      load_k(0);
+      store_k(IntC<0>());
+    } else {
+      stage_checked(0, IntC<0>(), with_v);
+    }
+    wait_dma();
     __syncthreads();
-  }
-  if (ragged) pass1_tile(BoolC<true>(), ntiles - 1);
+  };
+  // Full tiles alternate between the buffers (tile t in buffer t % 2, the
+  // loop unrolled by two so the buffer is known at compile time); the next
+  // full tile is staged while this one is computed. Then the ragged tile,
+  // staged synchronously.
+  auto run_pass = [&](bool with_v, auto body) {
+    stage_first(with_v);
+    auto step = [&](int t, auto cur, auto nxt) {
+      const bool next_full = t + 1 < nfull;
+      if (next_full) {
+        dma_tile(t + 1, nxt, with_v);
+        load_k(t + 1);
+      }
+      body(BoolC<false>(), t, cur);
+      if (next_full) {
+        store_k(nxt);
+        if (with_v && !p.v_dma) copy_v_checked(t + 1, nxt);
+      }
+      wait_dma();
+      __syncthreads();
+    };
+    for (int t = 0; t < nfull; t += 2) {
+      step(t, IntC<0>(), IntC<1>());
+      if (t + 1 < nfull) step(t + 1, IntC<1>(), IntC<0>());
+    }
+    if (ragged) {
+      const int t = ntiles - 1;
+      auto tail = [&](auto cur) {
+        if (nfull > 0) {
+          stage_checked(t, cur, with_v);
+          wait_dma();
+          __syncthreads();
+        }
+        body(BoolC<true>(), t, cur);
+      };
+      if (t & 1) tail(IntC<1>());
+      else tail(IntC<0>());
+    }
+  };
+  run_pass(false, pass1_tile);
 
   float mrun = fmaxf(m0, m1);
   mrun = fmaxf(mrun, partner32(mrun, lane));
@@ -478,40 +566,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     return (v4i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
   };
   // P.V of one key block: acc += V^T (127 - p8) + V^T (-127)
-  auto pv = [&](int buf, int kb, const v4i& bop) {
-    const uint8_t* vb = sm.vr[buf] + (kb * 32 + tr_row) * VS + tr_col;
+  auto pv = [&](auto bufc, int kb, const v4i& bop) {
+    S& sb = pick(bufc);
+    const uint8_t* vb = sb.vr;
+    const int r0 = kb * 32 + tr_row, r1 = r0 + 8;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + cb * 32));
-      const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + 8 * VS + cb * 32));
+      const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + vaddr(r0, tr_col + 32 * cb)));
+      const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + vaddr(r1, tr_col + 32 * cb)));
       const v4i a = {lo[0], lo[1], hi[0], hi[1]};
       acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, acc[cb], 0, 0, 0);
       acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, m127, acc[cb], 0, 0, 0);
     }
   };
-  auto pass2_tile = [&](auto tail, int t) {
-    const int buf = t & 1;
-    const v16f sig0 = qk_block(buf, 0);
-    const v16f sig1 = qk_block(buf, 1);
+  auto pass2_tile = [&](auto tail, int t, auto bufc) {
+    const v16f sig0 = qk_block(bufc, 0);
+    const v16f sig1 = qk_block(bufc, 1);
     float sc[16];
-    scores(BoolC<false>(), t, buf, 0, sig0, sc);
+    scores(BoolC<false>(), t, bufc, 0, sig0, sc);
     const v4i p0 = probs(tail, t, 0, sc);
-    pv(buf, 0, p0);
-    scores(BoolC<false>(), t, buf, 1, sig1, sc);
+    pv(bufc, 0, p0);
+    scores(BoolC<false>(), t, bufc, 1, sig1, sc);
     const v4i p1 = probs(tail, t, 1, sc);
-    pv(buf, 1, p1);
+    pv(bufc, 1, p1);
   };
 
-  load_tile(0, true);
-  store_tile(0, 0, true);
-  __syncthreads();
-  for (int t = 0; t < nfull; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1, true);
-    pass2_tile(BoolC<false>(), t);
-    if (t + 1 < ntiles) store_tile(t + 1, (t & 1) ^ 1, true);
-    __syncthreads();
-  }
-  if (ragged) pass2_tile(BoolC<true>(), ntiles - 1);
+  __syncthreads();  // pass 1 is done with both buffers
+  run_pass(true, pass2_tile);
 
   // ================= epilogue =================
   float lrun = (l0 + l1) + (l2 + l3);
@@ -572,7 +653,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.B = a.B; p.H = a.H; p.N = a.N; p.d = a.d; p.W = (a.d + 31) / 32;
   p.nqb = (a.N + kQB - 1) / kQB;
   p.inv_sqrt_d = (float)(1.0 / sqrt((double)a.d));
-  p.v_vec = (a.d % 8) == 0;
+  // V tiles by DMA: 16-byte pieces must be 16-byte aligned in global memory
+  // (tile starts are (bh*N + 64t)*d bytes from a 16-byte aligned base)
+  p.v_dma = (a.d % 16 == 0) || (a.d % 8 == 0 && a.N % 2 == 0);
+  p.v_swz_shift = -1;
+  if (p.v_dma && (a.d == 32 || a.d == 64 || a.d == 128)) p.v_swz_shift = a.d == 32 ? 2 : a.d == 64 ? 1 : 0;
   p.out = a.out;
   int bias = BIAS_NONE;
   p.bias_vec = 0;
