@@ -48,6 +48,16 @@ constexpr int kQW = 32;            // queries per wave
 constexpr int kQB = kWaves * kQW;  // queries per workgroup
 constexpr int kBC = 64;            // keys per LDS tile (two 32-key MFMA blocks)
 constexpr int kTblMax = 2048;      // floats of relative-position window per tile
+
+// Workgroups per CU the register allocation must allow (4 waves each; 2 ->
+// up to 256 VGPRs per wave, 3 -> 168, 4 -> 128), per instantiation, from
+// measurements on MI355X: without a bias and d <= 64 the extra occupancy
+// wins even though a few values spill outside the key loops; the relative-
+// position gather prefers 3; the dense-bias loads need the registers.
+template <int NCB, int BIAS>
+constexpr int min_blocks() {
+  return BIAS == 3 ? 3 : (BIAS == 0 ? (NCB <= 2 ? 4 : 3) : 2);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.9943534368588578f;
 
@@ -137,7 +147,7 @@ struct TileBuf {
 };
 
 template <int NKB, int NCB, int BIAS, int OUTDT>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kernel(Params p) {
   using S = TileBuf<NKB, NCB, BIAS>;
   constexpr int KROW = S::KROW, VS = S::VS;
   constexpr bool DENSE = BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16;
@@ -580,15 +590,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     }
   };
   auto pass2_tile = [&](auto tail, int t, auto bufc) {
-    const v16f sig0 = qk_block(bufc, 0);
-    const v16f sig1 = qk_block(bufc, 1);
-    float sc[16];
-    scores(BoolC<false>(), t, bufc, 0, sig0, sc);
-    const v4i p0 = probs(tail, t, 0, sc);
-    pv(bufc, 0, p0);
-    scores(BoolC<false>(), t, bufc, 1, sig1, sc);
-    const v4i p1 = probs(tail, t, 1, sc);
-    pv(bufc, 1, p1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const v16f sig = qk_block(bufc, kb);
+      float sc[16];
+      scores(BoolC<false>(), t, bufc, kb, sig, sc);
+      const v4i pk = probs(tail, t, kb, sc);
+      pv(bufc, kb, pk);
+    }
   };
 
   __syncthreads();  // pass 1 is done with both buffers

@@ -14,13 +14,13 @@
 namespace binattn {
 
 // ---------------------------------------------------------------------------
-// pack_qk: one thread per token. Loads the token's d 16-bit values (16-byte
-// vector loads when d % 8 == 0), sets bit c iff x_c < 0, and computes
-// mu = sum|x| / d with a float64 sum (exact for fp16/bf16 inputs of ordinary
-// range) and one float64 division rounded once to float.
+// pack_qk, any d: one thread per token. Loads the token's d 16-bit values,
+// sets bit c iff x_c < 0, and computes mu = sum|x| / d with a float64 sum
+// (exact for fp16/bf16 inputs of ordinary range) and one float64 division
+// rounded once to float.
 // grid.y selects Q (0) or K (1).
 // ---------------------------------------------------------------------------
-template <int DT, bool VEC>
+template <int DT>
 __global__ __launch_bounds__(256) void pack_qk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
     int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
@@ -36,42 +36,89 @@ __global__ __launch_bounds__(256) void pack_qk_kernel(
     uint32_t word = 0;
     const int c0 = w * 32;
     const int nc = min(32, d - c0);
-    if (VEC) {
-      for (int g = 0; g < nc; g += 8) {
-        const u4v raw = *reinterpret_cast<const u4v*>(x + c0 + g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t h = (uint16_t)(raw[e >> 1] >> ((e & 1) * 16));
-          word |= neg_bit<DT>(h) << (g + e);
-          asum += (double)fabsf(to_f32<DT>(h));
-        }
-      }
-    } else {
-      for (int c = 0; c < nc; ++c) {
-        const uint16_t h = x[c0 + c];
-        word |= neg_bit<DT>(h) << c;
-        asum += (double)fabsf(to_f32<DT>(h));
-      }
+    for (int c = 0; c < nc; ++c) {
+      const uint16_t h = x[c0 + c];
+      word |= neg_bit<DT>(h) << c;
+      asum += (double)fabsf(to_f32<DT>(h));
     }
     bits[t * W + w] = word;
   }
   mu[t] = (float)(asum / (double)d);
 }
 
+// pack_qk for d % 8 == 0: the threads of a block cooperate on whole tokens.
+// Thread i loads the 16 bytes at element 8i of the block's token range (one
+// fully coalesced 4 KB read per block), i.e. channels 8p..8p+7 of token i/P
+// (P = d/8 pieces per token); it forms their 8 sign bits and a float64
+// partial sum of |x|. The pieces are combined through LDS: each 32-bit word
+// from its 4 pieces, mu from the P partial sums in channel order.
+template <int DT>
+__global__ __launch_bounds__(256) void pack_qk_coop_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
+    int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
+    uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
+  __shared__ uint32_t bits_s[256];
+  __shared__ double sum_s[256];
+  const uint16_t* x = blockIdx.y == 0 ? q : k;
+  uint32_t* bits = blockIdx.y == 0 ? qbits : kbits;
+  float* mu = blockIdx.y == 0 ? qmu : kmu;
+  const int P = d >> 3;                  // pieces per token (1..16)
+  const int Tb = 256 / P;                // whole tokens per block
+  const int W = (d + 31) >> 5;
+  const int64_t tok0 = (int64_t)blockIdx.x * Tb;
+  const int i = threadIdx.x;
+  uint32_t b8 = 0;
+  double s = 0.0;
+  if (i < Tb * P && tok0 + i / P < ntok) {
+    const u4v raw = *reinterpret_cast<const u4v*>(x + tok0 * d + 8 * i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t h = (uint16_t)(raw[e >> 1] >> ((e & 1) * 16));
+      b8 |= neg_bit<DT>(h) << e;
+      s += (double)fabsf(to_f32<DT>(h));
+    }
+  }
+  bits_s[i] = b8;
+  sum_s[i] = s;
+  __syncthreads();
+  for (int j = i; j < Tb * W; j += 256) {
+    const int tl = j / W, w = j % W;
+    if (tok0 + tl < ntok) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int pc = 4 * w + pp;
+        if (pc < P) word |= bits_s[tl * P + pc] << (8 * pp);
+      }
+      bits[(tok0 + tl) * W + w] = word;
+    }
+  }
+  if (i < Tb && tok0 + i < ntok) {
+    double acc = 0.0;
+    for (int pc = 0; pc < P; ++pc) acc += sum_s[i * P + pc];
+    mu[tok0 + i] = (float)(acc / (double)d);
+  }
+}
+
 hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t ntok,
                           int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
                           float* kmu, hipStream_t s) {
-  const dim3 grid((unsigned)((ntok + 255) / 256), 2);
-  const bool vec = (d % 8) == 0;
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
-  if (dt == BA_F16) {
-    if (vec) hipLaunchKernelGGL((pack_qk_kernel<BA_F16, true>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
-    else     hipLaunchKernelGGL((pack_qk_kernel<BA_F16, false>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
-  } else {
-    if (vec) hipLaunchKernelGGL((pack_qk_kernel<BA_BF16, true>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
-    else     hipLaunchKernelGGL((pack_qk_kernel<BA_BF16, false>), grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+  if (d % 8 == 0) {
+    const int Tb = 256 / (d / 8);
+    const dim3 grid((unsigned)((ntok + Tb - 1) / Tb), 2);
+    if (dt == BA_F16)
+      hipLaunchKernelGGL(pack_qk_coop_kernel<BA_F16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+    else
+      hipLaunchKernelGGL(pack_qk_coop_kernel<BA_BF16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+    return hipGetLastError();
   }
+  const dim3 grid((unsigned)((ntok + 255) / 256), 2);
+  if (dt == BA_F16)
+    hipLaunchKernelGGL(pack_qk_kernel<BA_F16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+  else
+    hipLaunchKernelGGL(pack_qk_kernel<BA_BF16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
   return hipGetLastError();
 }
 
@@ -114,7 +161,20 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
     const bool active = r0 < rows;
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (active) {
-      for (int j = r0; j < N; j += rows) {
+      // 8 rows in flight per thread
+      int j = r0;
+      for (; j + 7 * rows < N; j += 8 * rows) {
+        u4v raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * d + c0 + piece * 8);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(raw[u][e >> 1] >> ((e & 1) * 16)))));
+      }
+      for (; j < N; j += rows) {
         const u4v raw = *reinterpret_cast<const u4v*>(vh + (int64_t)j * d + c0 + piece * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -134,9 +194,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
       float inv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) inv[e] = inv_s[piece * 8 + e];
-      for (int j = r0; j < N; j += rows) {
-        const int64_t off = (int64_t)j * d + c0 + piece * 8;
-        const u4v raw = *reinterpret_cast<const u4v*>(vh + off);
+      auto quant8 = [&](const u4v& raw) -> uint2 {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -145,7 +203,21 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
           const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
           if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
         }
-        *reinterpret_cast<uint2*>(qh + off) = make_uint2(lo, hi);
+        return make_uint2(lo, hi);
+      };
+      int j = r0;
+      for (; j + 7 * rows < N; j += 8 * rows) {
+        u4v raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * d + c0 + piece * 8);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          *reinterpret_cast<uint2*>(qh + (int64_t)(j + u * rows) * d + c0 + piece * 8) = quant8(raw[u]);
+      }
+      for (; j < N; j += rows) {
+        const int64_t off = (int64_t)j * d + c0 + piece * 8;
+        *reinterpret_cast<uint2*>(qh + off) = quant8(*reinterpret_cast<const u4v*>(vh + off));
       }
     }
   } else {
