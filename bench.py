@@ -213,6 +213,9 @@ def main() -> int:
     ap.add_argument("--secondary", default="long_4k")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (read BYTES, write BYTES) five "
+                         "times: the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -222,6 +225,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes 4n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n}))
+        return 0
     import workloads
     names = list(workloads.WORKLOADS) if args.all else [args.workload]
     for name in names:

@@ -1,0 +1,103 @@
+"""Summaries of rocprofv3 output for the BinaryAttention kernels.
+
+    # per-kernel time table from a --kernel-trace --stats run
+    python -m bit_qk_attention_amd.profiling stats <dir>/..._kernel_stats.csv
+
+    # HBM traffic of one kernel from two --pmc runs (FETCH_SIZE, WRITE_SIZE),
+    # calibrated against a plain copy of known size profiled the same way
+    python -m bit_qk_attention_amd.profiling traffic --kernel attn_fwd \\
+        --fetch <a>/..._counter_collection.csv --write <b>/..._counter_collection.csv \\
+        --copy-fetch <c>/... --copy-write <d>/... --copy-bytes N --out file.json
+
+FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch. The copy kernel
+reads and writes exactly N bytes, so the counter's reading for it gives a
+scale factor (N / measured) applied to the kernel's reading.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(_HERE, "csrc", "attention.hip")
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def stats_table(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        short = name.split("(")[0].replace("void ", "").replace("binattn::", "")
+        out.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
+def per_dispatch(path: str, kernel: str, counter: str) -> list[float]:
+    """Counter value (summed over instances) of each dispatch of `kernel`."""
+    acc = collections.defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            acc[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return [acc[k] for k in sorted(acc)]
+
+
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2] if xs else float("nan")
+
+
+def traffic(kernel, fetch, write, copy_fetch, copy_write, copy_bytes, copy_kernel="copy"):
+    kf = median(per_dispatch(fetch, kernel, "FETCH_SIZE")) * 1024
+    kw = median(per_dispatch(write, kernel, "WRITE_SIZE")) * 1024
+    cf = median(per_dispatch(copy_fetch, copy_kernel, "FETCH_SIZE")) * 1024
+    cw = median(per_dispatch(copy_write, copy_kernel, "WRITE_SIZE")) * 1024
+    f_scale = copy_bytes / cf
+    w_scale = copy_bytes / cw
+    return {
+        "kernel": kernel, "kernel_sha": kernel_sha(),
+        "fetch_bytes_raw": kf, "write_bytes_raw": kw,
+        "copy_bytes": copy_bytes, "copy_fetch_raw": cf, "copy_write_raw": cw,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "bytes_per_launch": kf * f_scale + kw * w_scale,
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    b = sub.add_parser("traffic")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--copy-fetch", required=True)
+    b.add_argument("--copy-write", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--copy-kernel", default="copy")
+    b.add_argument("--out")
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        print(stats_table(args.csv))
+        return 0
+    rec = traffic(args.kernel, args.fetch, args.write, args.copy_fetch, args.copy_write,
+                  args.copy_bytes, args.copy_kernel)
+    text = json.dumps(rec, indent=1)
+    if args.out:
+        open(args.out, "w").write(text + "\n")
+    print(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
