@@ -56,12 +56,15 @@ constexpr int kTblMax = 2048;      // floats of relative-position window per til
 // position gather prefers 3; the dense-bias loads need the registers.
 template <int NCB, int BIAS>
 constexpr int min_blocks() {
-  return BIAS == 3 ? 3 : (BIAS == 0 ? (NCB <= 2 ? 4 : 3) : 2);
+  return BIAS == 0 && NCB <= 2 ? 3 : 2;
 }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.9943534368588578f;
 
-enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3 };
+// Bias variants. Dense rows that allow 16-byte vector access take the
+// specialised paths (fp32: vector loads; fp16: tiles staged in LDS by DMA);
+// any other dense bias takes per-element bounds-checked loads.
+enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3, BIAS_DENSE_ANY = 4 };
 
 struct Params {
   const uint32_t* qbits;
@@ -76,10 +79,12 @@ struct Params {
   int B, H, N, d, W;
   int nqb;          // query blocks per head
   float inv_sqrt_d;
-  int bias_vec;     // dense bias rows are 16-byte aligned (vector loads)
+  int bias_f16;     // dense bias element type (BIAS_DENSE_ANY): fp16, else fp32
+  int out_f16;      // output type: fp16, else bf16
   int v_dma;        // V tiles go global -> LDS directly (16-byte pieces)
   int v_swz_shift;  // 16-byte chunk swizzle of V rows: -1 none, else shift
   int relpos_fast;  // relative-position rows never wrap inside 16 keys
+  int mk_vec;       // key scales of a head start 16-byte aligned (N % 4 == 0)
   void* out;
 };
 
@@ -87,7 +92,7 @@ struct Params {
 // 32w + m + 4p at nibble p (0..7); the same channel order is used for the
 // query and the key operand, so the dot product is unchanged.
 __device__ __forceinline__ uint32_t fp4_signs(uint32_t bits, int m) {
-  return (((bits >> m) & 0x11111111u) << 3) | 0x22222222u;
+  return ((bits << (3 - m)) & 0x88888888u) | 0x22222222u;
 }
 
 // LDS swizzle of the 16-byte fp4 slots of one key row (spreads the lanes
@@ -113,10 +118,6 @@ __device__ __forceinline__ float partner32(float x, int lane) {
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
-template <int OUTDT>
-__device__ __forceinline__ uint16_t to_out(float x) {
-  return OUTDT == BA_F16 ? f32_to_f16(x) : f32_to_bf16(x);
-}
 
 template <bool B>
 struct BoolC {
@@ -131,36 +132,81 @@ struct IntC {
   static constexpr int value = V;
 };
 
-// One LDS tile buffer. The kernel keeps two as separate __shared__ objects
-// and selects them at compile time, so the compiler can tell a DMA into one
-// from reads of the other and does not wait for the prefetch.
-template <int NKB, int NCB, int BIAS>
-struct TileBuf {
-  static constexpr int DV = 32 * NCB;  // V channels padded to the MFMA block
+// LDS stages. Key-side data of one 64-key tile and its V rows live in
+// separate __shared__ objects, one per stage, selected at compile time: the
+// compiler then tells a DMA into one stage from reads of another and does
+// not wait for the prefetch before reading.
+template <int NKB, int BIAS>
+struct KeyStage {
   static constexpr int KROW = 32 * NKB;
-  static constexpr int VS = DV + 8;    // bytes per V row, generic (byte-copy) layout
-  static constexpr int NT = BIAS == BIAS_RELPOS ? kTblMax : 1;
-  uint8_t kx[kBC * KROW];
-  uint8_t vr[kBC * VS];  // also holds a 64 x d tile at stride d (d <= DV)
+  static constexpr int NT = BIAS == BIAS_RELPOS ? kTblMax : 4;
+  static constexpr int NB = BIAS == BIAS_DENSE_F16 ? kQB * kBC : 8;
+  uint8_t kx[kBC * KROW];  // fp4 K operand
+  uint32_t kraw[256];      // K sign words as loaded, one per thread
+  uint16_t bt[NB];         // fp16 dense bias tile: 128 query rows x 64 keys
   float mk[kBC];
   float tbl[NT];
 };
+template <int NCB>
+struct VStage {
+  static constexpr int DV = 32 * NCB;  // V channels padded to the MFMA block
+  static constexpr int VS = DV + 8;    // bytes per V row, generic (byte-copy) layout
+  uint8_t vr[kBC * VS];  // also holds a 64 x d tile at stride d (d <= DV)
+};
+// Stages per pass: pass 1 cycles through three (loads two tiles ahead);
+// pass 2, which also stages V, through three where the LDS budget of the
+// target occupancy allows, else two (one tile ahead).
+template <int NKB, int NCB, int BIAS>
+struct StageCfg {
+  static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS>);
+  static constexpr int VSZ = (int)sizeof(VStage<NCB>);
+  static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS>() - 2048;  // less the pass-1 reduction buffer
+  static constexpr int NS2 = 3 * KS + 3 * VSZ <= BUDGET ? 3 : 2;
+  static constexpr int NS1 = 3 * KS + NS2 * VSZ <= BUDGET ? 3 : 2;
+};
 
-template <int NKB, int NCB, int BIAS, int OUTDT>
+// 16-byte chunk (8 keys) permutation of the fp16 bias rows in LDS: the 16
+// consecutive rows that one 16-lane read group touches land in distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int bswz(int row) { return (row ^ (row >> 3)) & 7; }
+
+template <int NKB, int NCB, int BIAS>
 __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kernel(Params p) {
-  using S = TileBuf<NKB, NCB, BIAS>;
-  constexpr int KROW = S::KROW, VS = S::VS;
-  constexpr bool DENSE = BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16;
-  __shared__ __attribute__((aligned(16))) S sb0;
-  __shared__ __attribute__((aligned(16))) S sb1;
-  auto pick = [&](auto bufc) -> S& {
-    if constexpr (decltype(bufc)::value == 0) return sb0;
-    else return sb1;
+  using KS = KeyStage<NKB, BIAS>;
+  using VSt = VStage<NCB>;
+  using Cfg = StageCfg<NKB, NCB, BIAS>;
+  constexpr int KROW = KS::KROW, VS = VSt::VS;
+  constexpr int NS1 = Cfg::NS1, NS2 = Cfg::NS2;
+  constexpr bool DENSE = BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16 || BIAS == BIAS_DENSE_ANY;
+  // pass 1 with the keys split over the waves (no staging) when there is no
+  // bias; with a bias, staged tiles (a dense bias read row-wise per wave
+  // would touch half-used 128-byte lines)
+  constexpr bool P1_SPLIT = BIAS == BIAS_NONE;
+  __shared__ float p1red[4][4][kQW];  // per-wave partial row maxima (pass 1 split)
+  __shared__ __attribute__((aligned(16))) KS ks0;
+  __shared__ __attribute__((aligned(16))) KS ks1;
+  __shared__ __attribute__((aligned(16))) KS ks2;
+  __shared__ __attribute__((aligned(16))) VSt vs0;
+  __shared__ __attribute__((aligned(16))) VSt vs1;
+  __shared__ __attribute__((aligned(16))) VSt vs2;
+  auto pick = [&](auto bufc) -> KS& {
+    constexpr int i = decltype(bufc)::value;
+    if constexpr (i == 0) return ks0;
+    else if constexpr (i == 1) return ks1;
+    else return ks2;
+  };
+  auto pick_v = [&](auto bufc) -> VSt& {
+    constexpr int i = decltype(bufc)::value;
+    if constexpr (i == 0) return vs0;
+    else if constexpr (i == 1) return vs1;
+    else return vs2;
   };
 
   const int N = p.N, d = p.d, W = p.W;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it in a scalar register so that the
+  // per-wave staging branches are scalar branches, not exec-mask regions
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ql = lane & 31, g = lane >> 5;
 
   // ---- work item: (b, h, query block), XCD-aware order ----
@@ -187,22 +233,25 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const int qc = qvalid ? qi : N - 1;  // clamped query index for addressing
 
   // ---- query operand: fp4 signs, padding channels zero ----
-  v8i qop[NKB];
+  // Word w of a query covers channels 32w..32w+31; of those, the first
+  // min(max(d - 32w, 0), 32) are real. Dword m of the fp4 operand holds
+  // channel 32w + m + 4p at nibble p, so its nibble mask is bit m + 4p of
+  // the real-channel mask spread to four bits.
+  auto q_operand = [&](int q, bool valid, v8i* op) {
 #pragma unroll
-  for (int kk = 0; kk < NKB; ++kk) {
-    const int w = 2 * kk + g;
-    const uint32_t bits = (qvalid && w < W) ? p.qbits[(bh * N + qi) * W + w] : 0u;
-    v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kk = 0; kk < NKB; ++kk) {
+      const int w = 2 * kk + g;
+      const uint32_t bits = (valid && w < W) ? p.qbits[(bh * N + q) * W + w] : 0u;
+      const int nv = min(max(d - 32 * w, 0), 32);
+      const uint32_t vm = nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+      v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t mask = 0;
-#pragma unroll
-      for (int pp = 0; pp < 8; ++pp)
-        if (32 * w + m + 4 * pp < d) mask |= 0xFu << (4 * pp);
-      o[m] = (int)(fp4_signs(bits, m) & mask);
+      for (int m = 0; m < 4; ++m) o[m] = (int)(fp4_signs(bits, m) & (((vm >> m) & 0x11111111u) * 0xFu));
+      op[kk] = o;
     }
-    qop[kk] = o;
-  }
+  };
+  v8i qop[NKB];
+  q_operand(qi, qvalid, qop);
   const float qmu = qvalid ? p.qmu[bh * N + qi] : 0.0f;
   const float c0 = qmu * p.inv_sqrt_d;  // natural-log units (bias path)
   const float cq = c0 * kLog2e;         // base-2 units (no-bias path)
@@ -241,10 +290,13 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   };
 
   // ---- staging ----
-  // Full tiles: V, the key scales and the relative-position window rows go
-  // global -> LDS with global_load_lds (no registers, no VALU); wave 0 loads
-  // the K sign words into registers a tile ahead and expands them to fp4 in
-  // LDS. The ragged last tile is staged synchronously with bounds checks.
+  // Full tiles go global -> LDS with global_load_lds (no registers): V, the
+  // key scales and the relative-position window rows first, then the K sign
+  // words and the fp16 bias tile, a fixed number of instructions per wave,
+  // so that a wait for all but that last group leaves only the newest tile
+  // in flight. Each thread DMAs one K word and, once its own load has
+  // landed, expands it to the fp4 operand (no barrier between the two). The
+  // ragged last tile is staged synchronously with bounds checks.
   //
   // V layout in LDS (v_dma): row stride d; with v_swz_shift >= 0 the 16-byte
   // chunks of row r are permuted, chunk c stored at c ^ vswz(r), so that the
@@ -273,31 +325,39 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   typedef __attribute__((address_space(1))) const void gptr_t;
   typedef __attribute__((address_space(3))) void lptr_t;
 
-  uint32_t st_k[2 * NKB];
-  auto load_k = [&](int t) {
-    if (wave == 0) {
-      const bool last = ragged && t == ntiles - 1;
-      const int j = t * kBC + lane;
-      const uint32_t* src = p.kbits + (bh * N + j) * W;
-#pragma unroll
-      for (int w = 0; w < 2 * NKB; ++w) st_k[w] = (w < W && (!last || j < N)) ? src[w] : 0u;
+  // K sign words of a tile, spread over all 256 threads: thread tid expands
+  // word kw_w of key kw_key (NKB == 2: all four 16-byte fp4 slots of the
+  // key, one per thread; NKB == 1: two threads share a word, 8 bytes each).
+  // Padding words (kw_w >= W) expand whatever was loaded: the query operand
+  // is zero in those channels.
+  const int kw_key = tid >> 2;
+  const int kw_w = NKB == 2 ? (tid & 3) : ((tid >> 1) & 1);
+  const int kw_half = NKB == 2 ? 0 : (tid & 1);
+  const int kw_src = kw_key * W + min(kw_w, W - 1);  // word offset within a full tile
+  auto expand_k = [&](auto bufc, uint32_t bits) {
+    KS& sb = pick(bufc);
+    uint8_t* dst = sb.kx + kw_key * KROW + kslot<NKB>(kw_key, kw_w) * 16;
+    if (NKB == 2) {
+      u4v o;
+      o[0] = fp4_signs(bits, 0); o[1] = fp4_signs(bits, 1);
+      o[2] = fp4_signs(bits, 2); o[3] = fp4_signs(bits, 3);
+      *reinterpret_cast<u4v*>(dst) = o;
+    } else {
+      const int m = 2 * kw_half;
+      *reinterpret_cast<uint2*>(dst + 8 * kw_half) = make_uint2(fp4_signs(bits, m), fp4_signs(bits, m + 1));
     }
   };
-  auto store_k = [&](auto bufc) {
-    S& sb = pick(bufc);
-    if (wave == 0) {
-#pragma unroll
-      for (int w = 0; w < 2 * NKB; ++w) {
-        u4v o;
-        o[0] = fp4_signs(st_k[w], 0); o[1] = fp4_signs(st_k[w], 1);
-        o[2] = fp4_signs(st_k[w], 2); o[3] = fp4_signs(st_k[w], 3);
-        *reinterpret_cast<u4v*>(sb.kx + lane * KROW + kslot<NKB>(lane, w) * 16) = o;
-      }
-    }
+  // this thread's K word of a full tile, DMA'd into the stage (needs the
+  // thread's own vmcnt wait only)
+  auto finish_k = [&](auto bufc) { expand_k(bufc, pick(bufc).kraw[tid]); };
+  // bounds-checked K word of tile t, loaded and expanded synchronously
+  auto stage_k_checked = [&](int t, auto bufc) {
+    const int j = t * kBC + kw_key;
+    expand_k(bufc, (kw_w < W && j < N) ? p.kbits[(bh * N + j) * W + kw_w] : 0u);
   };
   // relative-position window rows of tile t (always in bounds of the table)
   auto dma_tbl = [&](int t, auto bufc) {
-    S& sb = pick(bufc);
+    KS& sb = pick(bufc);
     if (BIAS == BIAS_RELPOS) {
       int dr_lo, count;
       tbl_window(t, dr_lo, count);
@@ -310,24 +370,43 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       }
     }
   };
-  // full tile t (all keys < N): V, mu_k and the table window by DMA
+  // full tile t (all keys < N), all by DMA: V, mu_k and the table window,
+  // then the last group (kLastGroup instructions in every wave): the K words
+  // and the fp16 bias tile
+  constexpr int kLastGroup = 1 + (BIAS == BIAS_DENSE_F16 ? 4 : 0);
   auto dma_tile = [&](int t, auto bufc, bool with_v) {
-    S& sb = pick(bufc);
+    KS& sb = pick(bufc);
     const int j0 = t * kBC;
     if (with_v && p.v_dma) {
+      VSt& vb = pick_v(bufc);
       const int8_t* src = p.vq + (bh * N + j0) * d;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         if (v_on[i])
-          __builtin_amdgcn_global_load_lds((gptr_t*)(src + v_src[i]), (lptr_t*)(sb.vr + 1024 * (wave + 4 * i)), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gptr_t*)(src + v_src[i]), (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16, 0, 0);
     }
     if (wave == 1)
       __builtin_amdgcn_global_load_lds((gptr_t*)(p.kmu + bh * N + j0 + lane), (lptr_t*)(sb.mk), 4, 0, 0);
     dma_tbl(t, bufc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_global_load_lds((gptr_t*)(p.kbits + (bh * N + j0) * W + kw_src),
+                                     (lptr_t*)(sb.kraw + 64 * wave), 4, 0, 0);
+    if (BIAS == BIAS_DENSE_F16) {
+      // wave w fills its own 32 query rows, 8 rows (1 KB) per instruction
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wave * kQW + 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ bswz(row);
+        const int q = min(qb * kQB + row, N - 1);
+        const uint16_t* src = static_cast<const uint16_t*>(p.bias) + (int64_t)b * p.bias_bstride +
+                              ((int64_t)h * N + q) * N + j0 + 8 * chunk;
+        __builtin_amdgcn_global_load_lds((gptr_t*)src, (lptr_t*)(sb.bt + (wave * kQW + 8 * i) * kBC), 16, 0, 0);
+      }
+    }
   };
   // V tile t through registers, rows past N zero (ragged tile; any d)
   auto copy_v_checked = [&](int t, auto bufc) {
-    S& sb = pick(bufc);
+    VSt& sb = pick_v(bufc);
     const int j0 = t * kBC;
     if (p.v_dma) {
       for (int x = tid; x < kBC * d / 8; x += 256) {
@@ -346,9 +425,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   };
   // synchronous staging of tile t with bounds checks (the ragged tile)
   auto stage_checked = [&](int t, auto bufc, bool with_v) {
-    S& sb = pick(bufc);
-    load_k(t);
-    store_k(bufc);
+    KS& sb = pick(bufc);
+    stage_k_checked(t, bufc);
     if (wave == 1) {
       const int j = t * kBC + lane;
       sb.mk[lane] = j < N ? p.kmu[bh * N + j] : 0.0f;
@@ -356,31 +434,43 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     if (with_v) copy_v_checked(t, bufc);
     dma_tbl(t, bufc);
   };
-  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  // s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt not waited for)
+  auto wait_vm0 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  auto wait_vm_last = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70 | kLastGroup); };
 
-  // S^T block (32 keys x 32 queries) of key block kb of the selected buffer
-  auto qk_block = [&](auto bufc, int kb) -> v16f {
-    S& sb = pick(bufc);
+  // fp4 K operand (NKB x 16 bytes per lane) of key block kb of the selected
+  // buffer, and the S^T block (32 keys x 32 queries) it gives
+  auto k_operand = [&](auto bufc, int kb, u4v* a) {
+    KS& sb = pick(bufc);
     const int key = kb * 32 + key_of_pos(ql);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+      a[kk] = *reinterpret_cast<const u4v*>(sb.kx + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
+  };
+  auto qk_mfma = [&](const u4v* a) -> v16f {
     v16f s = {};
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
-      const u4v a4 = *reinterpret_cast<const u4v*>(sb.kx + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
-      const v8i a = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
-      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qop[kk], s, 4, 4, 0, 0, 0, 0);
+      const v8i op = {(int)a[kk][0], (int)a[kk][1], (int)a[kk][2], (int)a[kk][3], 0, 0, 0, 0};
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op, qop[kk], s, 4, 4, 0, 0, 0, 0);
     }
     return s;
+  };
+  auto qk_block = [&](auto bufc, int kb) -> v16f {
+    u4v a[NKB];
+    k_operand(bufc, kb, a);
+    return qk_mfma(a);
   };
 
   // Scores of this lane's 16 keys in key block kb of tile t:
   // sigma * mu_k (no bias; the query scale is applied later) or
   // sigma * mu_k * mu_q / sqrt(d) + b (natural-log units, with bias).
-  // TAIL: the last tile when N is not a multiple of the tile; keys past N
-  // get -inf.
-  auto scores = [&](auto tail, int t, auto bufc, int kb, const v16f& sig, float* sc) {
-    S& sb = pick(bufc);
+  // TAIL: the last tile when N is not a multiple of the tile (bias loads are
+  // bounds-checked); MASK: keys past N get -inf.
+  auto scores = [&](auto tail, auto mask, int t, auto bufc, int kb, const v16f& sig, float* sc) {
+    KS& sb = pick(bufc);
     constexpr bool TAIL = decltype(tail)::value;
-    const bool last = ragged && t == ntiles - 1;  // keys past N in this tile
+    constexpr bool MASK = decltype(mask)::value;
     const int jl = kb * 32 + 16 * g;  // first key of the lane's 16, in the tile
     const int jb = t * kBC + jl;
     const float4* mkp = reinterpret_cast<const float4*>(sb.mk + jl);
@@ -395,29 +485,32 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     if (DENSE) {
       const int64_t row = (int64_t)b * p.bias_bstride + ((int64_t)h * N + qc) * N;
       float bv[16];
-      if (!last && p.bias_vec) {
-        if (BIAS == BIAS_DENSE_F32) {
+      if ((BIAS == BIAS_DENSE_F16 || BIAS == BIAS_DENSE_F32) && !TAIL) {
+        if (BIAS == BIAS_DENSE_F16) {
+          // staged in LDS by dma_tile
+          const int rl = wave * kQW + ql;
+          const u4v* src = reinterpret_cast<const u4v*>(sb.bt + rl * kBC);
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const u4v v = src[(4 * kb + 2 * g + r) ^ bswz(rl)];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[8 * r + e] = f16_to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+          }
+        } else if (BIAS == BIAS_DENSE_F32) {
           const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.bias) + row + jb);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float4 v = src[r];
             bv[4 * r] = v.x; bv[4 * r + 1] = v.y; bv[4 * r + 2] = v.z; bv[4 * r + 3] = v.w;
           }
-        } else {
-          const u4v* src = reinterpret_cast<const u4v*>(static_cast<const uint16_t*>(p.bias) + row + jb);
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const u4v v = src[r];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bv[8 * r + e] = f16_to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
-          }
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = min(jb + i, N - 1);
-          bv[i] = BIAS == BIAS_DENSE_F32 ? static_cast<const float*>(p.bias)[row + j]
-                                         : f16_to_f32(static_cast<const uint16_t*>(p.bias)[row + j]);
+          const bool f16 = BIAS == BIAS_DENSE_F16 || (BIAS == BIAS_DENSE_ANY && p.bias_f16);
+          bv[i] = f16 ? f16_to_f32(static_cast<const uint16_t*>(p.bias)[row + j])
+                      : static_cast<const float*>(p.bias)[row + j];
         }
       }
 #pragma unroll
@@ -430,7 +523,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       const float* tb = sb.tbl;
       float bv[16];
       const bool wave_grid = qb * kQB + wave * kQW >= npre;  // no prefix query in this wave
-      if (!last && p.relpos_fast && wave_grid && jb >= npre) {
+      if (!TAIL && p.relpos_fast && wave_grid && t * kBC >= npre) {
         // 16 keys on one grid row: a contiguous, reversed window
         const int g0 = jb - npre;
         const int base = aq - ((g0 / gw) * T2 + g0 % gw);
@@ -450,7 +543,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c0, bv[i]);
     }
-    if (TAIL) {
+    if (MASK) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (jb + i >= N) sc[i] = -INFINITY;
@@ -470,67 +563,227 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     const v16f sig0 = qk_block(bufc, 0);
     const v16f sig1 = qk_block(bufc, 1);
     float sc[16];
-    scores(tail, t, bufc, 0, sig0, sc);
+    scores(tail, tail, t, bufc, 0, sig0, sc);
     max16(sc);
-    scores(tail, t, bufc, 1, sig1, sc);
+    scores(tail, tail, t, bufc, 1, sig1, sc);
     max16(sc);
+    // keep the running max here, ahead of the end-of-tile wait, rather than
+    // let the compiler sink it past the wait
+    const float ma = m0, mb = m1;
+    asm volatile("" ::"v"(ma), "v"(mb));
   };
   const int nfull = ragged ? ntiles - 1 : ntiles;
-  // tile 0 -> buffer 0
-  auto stage_first = [&](bool with_v) {
+  // Full tiles cycle through NS stages (tile t in stage t % NS, the loop
+  // unrolled by NS so the stage is known at compile time): tile t + NS - 1
+  // is loaded while tile t is computed, and the end of step t waits only
+  // for tile t + 1. Then the ragged tile, staged synchronously.
+  auto run_pass = [&](auto nsc, bool with_v, auto body) {
+    constexpr int NS = decltype(nsc)::value;
     if (nfull > 0) {
       dma_tile(0, IntC<0>(), with_v);
+      if constexpr (NS == 3) {
+        if (nfull > 1) dma_tile(1, IntC<1>(), with_v);
+      }
+      if (NS == 3 && nfull > 1) wait_vm_last();
+      else wait_vm0();
+      finish_k(IntC<0>());
       if (with_v && !p.v_dma) copy_v_checked(0, IntC<0>());
-      load_k(0);
-      store_k(IntC<0>());
     } else {
       stage_checked(0, IntC<0>(), with_v);
+      wait_vm0();
     }
-    wait_dma();
     __syncthreads();
-  };
-  // Full tiles alternate between the buffers (tile t in buffer t % 2, the
-  // loop unrolled by two so the buffer is known at compile time); the next
-  // full tile is staged while this one is computed. Then the ragged tile,
-  // staged synchronously.
-  auto run_pass = [&](bool with_v, auto body) {
-    stage_first(with_v);
-    auto step = [&](int t, auto cur, auto nxt) {
-      const bool next_full = t + 1 < nfull;
-      if (next_full) {
-        dma_tile(t + 1, nxt, with_v);
-        load_k(t + 1);
-      }
+    auto step = [&](int t, auto cur) {
+      constexpr int c = decltype(cur)::value;
+      constexpr int nx = (c + 1) % NS, far = (c + NS - 1) % NS;
+      const bool issue = t + NS - 1 < nfull;
+      if (issue) dma_tile(t + NS - 1, IntC<far>(), with_v);
       body(BoolC<false>(), t, cur);
-      if (next_full) {
-        store_k(nxt);
-        if (with_v && !p.v_dma) copy_v_checked(t + 1, nxt);
+      if (t + 1 < nfull) {
+        if (NS == 3 && issue) wait_vm_last();
+        else wait_vm0();
+        finish_k(IntC<nx>());
+        if (with_v && !p.v_dma) copy_v_checked(t + 1, IntC<nx>());
       }
-      wait_dma();
       __syncthreads();
     };
-    for (int t = 0; t < nfull; t += 2) {
-      step(t, IntC<0>(), IntC<1>());
-      if (t + 1 < nfull) step(t + 1, IntC<1>(), IntC<0>());
+    for (int t = 0; t < nfull; t += NS) {
+      step(t, IntC<0>());
+      if (t + 1 < nfull) step(t + 1, IntC<1>());
+      if constexpr (NS == 3) {
+        if (t + 2 < nfull) step(t + 2, IntC<2>());
+      }
     }
     if (ragged) {
       const int t = ntiles - 1;
       auto tail = [&](auto cur) {
         if (nfull > 0) {
           stage_checked(t, cur, with_v);
-          wait_dma();
+          wait_vm0();
           __syncthreads();
         }
         body(BoolC<true>(), t, cur);
       };
-      if (t & 1) tail(IntC<1>());
-      else tail(IntC<0>());
+      const int sidx = t % NS;
+      if (sidx == 0) tail(IntC<0>());
+      else if (sidx == 1) tail(IntC<1>());
+      else if constexpr (NS == 3) tail(IntC<2>());
     }
   };
-  run_pass(false, pass1_tile);
-
-  float mrun = fmaxf(m0, m1);
-  mrun = fmaxf(mrun, partner32(mrun, lane));
+  float mrun;
+  if constexpr (P1_SPLIT) {
+    // Pass 1 splits the keys, not the queries, over the waves: wave w takes
+    // the 32-key blocks w, w + 4, ... against all 128 queries of the
+    // workgroup (four MFMA query groups), straight from global memory into
+    // registers: no shared staging and no barrier, and each block's K words
+    // are expanded once for four query groups. A wave's next block is loaded
+    // while the current one is computed. The four partial maxima of each
+    // query are combined through LDS at the end.
+    v8i qop4[4][NKB];
+    float c04[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int qq = qb * kQB + kQW * q + ql;
+      q_operand(qq, qq < N, qop4[q]);
+      c04[q] = qq < N ? p.qmu[bh * N + qq] * p.inv_sqrt_d : 0.0f;
+    }
+    struct Blk {
+      uint32_t kw[NKB];
+      float4 mk[4];
+      u4v bb[BIAS == BIAS_DENSE_F16 ? 4 : 1][2];
+    };
+    const float* kmu_bh = p.kmu + bh * N;
+    const uint16_t* bias_bh = static_cast<const uint16_t*>(p.bias) + (int64_t)b * p.bias_bstride + (int64_t)h * N * N;
+    // full block: every key < N
+    auto load_blk = [&](int blk, Blk& r) {
+      const int k0 = blk * 32;
+      const int myk = k0 + key_of_pos(ql);  // key of this lane's A-operand row
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) {
+        const int w = 2 * kk + g;
+        r.kw[kk] = w < W ? p.kbits[(bh * N + myk) * W + w] : 0u;
+      }
+      if (p.mk_vec) {
+        const float4* src = reinterpret_cast<const float4*>(kmu_bh + k0 + 16 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.mk[i] = src[i];
+      } else {
+        const float* src = kmu_bh + k0 + 16 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.mk[i] = make_float4(src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]);
+      }
+      if constexpr (BIAS == BIAS_DENSE_F16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = min(qb * kQB + kQW * q + ql, N - 1);
+          const u4v* src = reinterpret_cast<const u4v*>(bias_bh + (int64_t)row * N + k0 + 16 * g);
+          r.bb[q][0] = src[0];
+          r.bb[q][1] = src[1];
+        }
+      }
+    };
+    // the ragged last block: loads clamped to key N - 1 (those keys are masked)
+    auto load_blk_tail = [&](int blk, Blk& r) {
+      const int k0 = blk * 32;
+      const int myk = min(k0 + key_of_pos(ql), N - 1);
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) {
+        const int w = 2 * kk + g;
+        r.kw[kk] = w < W ? p.kbits[(bh * N + myk) * W + w] : 0u;
+      }
+      float mv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mv[i] = kmu_bh[min(k0 + 16 * g + i, N - 1)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.mk[i] = make_float4(mv[4 * i], mv[4 * i + 1], mv[4 * i + 2], mv[4 * i + 3]);
+      if constexpr (BIAS == BIAS_DENSE_F16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = min(qb * kQB + kQW * q + ql, N - 1);
+          const uint16_t* src = bias_bh + (int64_t)row * N;
+          uint32_t hw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            hw[e] = (uint32_t)src[min(k0 + 16 * g + 2 * e, N - 1)] | ((uint32_t)src[min(k0 + 16 * g + 2 * e + 1, N - 1)] << 16);
+          r.bb[q][0] = (u4v){hw[0], hw[1], hw[2], hw[3]};
+          r.bb[q][1] = (u4v){hw[4], hw[5], hw[6], hw[7]};
+        }
+      }
+    };
+    float mx[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx[q][0] = mx[q][1] = -INFINITY;
+    auto comp_blk = [&](auto tail, int blk, const Blk& r) {
+      constexpr bool TAIL = decltype(tail)::value;
+      v8i a[NKB];
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk)
+        a[kk] = (v8i){(int)fp4_signs(r.kw[kk], 0), (int)fp4_signs(r.kw[kk], 1), (int)fp4_signs(r.kw[kk], 2),
+                      (int)fp4_signs(r.kw[kk], 3), 0, 0, 0, 0};
+      const int jb = blk * 32 + 16 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v16f sg = {};
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk)
+          sg = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk], qop4[q][kk], sg, 4, 4, 0, 0, 0, 0);
+        float sc[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[4 * i + 0] = sg[4 * i + 0] * r.mk[i].x;
+          sc[4 * i + 1] = sg[4 * i + 1] * r.mk[i].y;
+          sc[4 * i + 2] = sg[4 * i + 2] * r.mk[i].z;
+          sc[4 * i + 3] = sg[4 * i + 3] * r.mk[i].w;
+        }
+        if constexpr (BIAS == BIAS_DENSE_F16) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t wd = r.bb[q][e >> 3][(e >> 1) & 3];
+            sc[e] = __builtin_fmaf(sc[e], c04[q], f16_to_f32((uint16_t)(wd >> (16 * (e & 1)))));
+          }
+        }
+        if (TAIL) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (jb + i >= N) sc[i] = -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          mx[q][0] = fmaxf(fmaxf(mx[q][0], sc[i]), sc[i + 1]);
+          mx[q][1] = fmaxf(fmaxf(mx[q][1], sc[i + 2]), sc[i + 3]);
+        }
+      }
+    };
+    const int nfb = N >> 5;  // full 32-key blocks
+    Blk ra, rb;
+    if (wave < nfb) load_blk(wave, ra);
+    for (int blk = wave; blk < nfb; blk += 8) {
+      const bool hb = blk + 4 < nfb;
+      if (hb) load_blk(blk + 4, rb);
+      comp_blk(BoolC<false>(), blk, ra);
+      if (hb) {
+        if (blk + 8 < nfb) load_blk(blk + 8, ra);
+        comp_blk(BoolC<false>(), blk + 4, rb);
+      }
+    }
+    if ((N & 31) != 0 && wave == (nfb & 3)) {
+      Blk rt;
+      load_blk_tail(nfb, rt);
+      comp_blk(BoolC<true>(), nfb, rt);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v = fmaxf(mx[q][0], mx[q][1]);
+      v = fmaxf(v, partner32(v, lane));
+      if (g == 0) p1red[wave][q][ql] = v;
+    }
+    __syncthreads();
+    mrun = fmaxf(fmaxf(p1red[0][wave][ql], p1red[1][wave][ql]), fmaxf(p1red[2][wave][ql], p1red[3][wave][ql]));
+  } else {
+    run_pass(IntC<NS1>(), false, pass1_tile);
+    mrun = fmaxf(m0, m1);
+    mrun = fmaxf(mrun, partner32(mrun, lane));
+  }
   // x = score * scale2 + negm is log2(255 * exp(s - m))
   const float scale2 = (BIAS == BIAS_NONE) ? cq : kLog2e;
   const float negm = __builtin_fmaf(-scale2, mrun, kLog2_255);
@@ -575,33 +828,75 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     }
     return (v4i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
   };
-  // P.V of one key block: acc += V^T (127 - p8) + V^T (-127)
-  auto pv = [&](auto bufc, int kb, const v4i& bop) {
-    S& sb = pick(bufc);
+  // V^T operand (NCB x 16 bytes per lane) of key block kb, read from LDS
+  auto read_vt = [&](auto bufc, int kb, v4i* vt) {
+    VSt& sb = pick_v(bufc);
     const uint8_t* vb = sb.vr;
     const int r0 = kb * 32 + tr_row, r1 = r0 + 8;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + vaddr(r0, tr_col + 32 * cb)));
       const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + vaddr(r1, tr_col + 32 * cb)));
-      const v4i a = {lo[0], lo[1], hi[0], hi[1]};
-      acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, m127, acc[cb], 0, 0, 0);
+      vt[cb] = (v4i){lo[0], lo[1], hi[0], hi[1]};
     }
   };
-  auto pass2_tile = [&](auto tail, int t, auto bufc) {
+  // P.V of one key block: acc += V^T (127 - p8) + V^T (-127)
+  auto pv_regs = [&](const v4i* vt, const v4i& bop) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const v16f sig = qk_block(bufc, kb);
-      float sc[16];
-      scores(BoolC<false>(), t, bufc, kb, sig, sc);
-      const v4i pk = probs(tail, t, kb, sc);
-      pv(bufc, kb, pk);
+    for (int cb = 0; cb < NCB; ++cb) {
+      acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vt[cb], bop, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vt[cb], m127, acc[cb], 0, 0, 0);
     }
+  };
+  // A wave issues in order, so the matrix products of a tile are spread
+  // through the VALU work that does not depend on them: block 1's Q.K and
+  // the previous tile's deferred P.V run under block 0's softmax, block 0's
+  // P.V under block 1's. Block 1's P.V is deferred to the next tile, its
+  // operands carried in registers across the barrier (zero at the start:
+  // the first deferred product adds 0).
+  v4i vt_held[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) vt_held[cb] = (v4i){0, 0, 0, 0};
+  v4i p_held = (v4i){0, 0, 0, 0};
+  constexpr int kValuPerMfma = 10;
+  auto pass2_tile = [&](auto tail, int t, auto bufc) {
+    u4v a0[NKB], a1[NKB];
+    k_operand(bufc, 0, a0);
+    k_operand(bufc, 1, a1);
+    const v16f sig0 = qk_mfma(a0);
+    __builtin_amdgcn_sched_barrier(0);
+    const v16f sig1 = qk_mfma(a1);
+    pv_regs(vt_held, p_held);
+    v4i vt0[NCB];
+    read_vt(bufc, 0, vt0);
+    float sc[16];
+    scores(tail, BoolC<false>(), t, bufc, 0, sig0, sc);
+    const v4i p0 = probs(tail, t, 0, sc);
+#pragma unroll
+    for (int i = 0; i < NKB + 2 * NCB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);    // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv_regs(vt0, p0);
+    scores(tail, BoolC<false>(), t, bufc, 1, sig1, sc);
+    p_held = probs(tail, t, 1, sc);
+    read_vt(bufc, 1, vt_held);
+#pragma unroll
+    for (int i = 0; i < 2 * NCB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+    }
+    // block 1's probabilities (and the row sums) are consumed only in the
+    // next tile: pin their computation here, beside block 0's P.V, rather
+    // than let it sink past the end-of-tile wait
+    asm volatile("" ::"v"(p_held), "v"(l0), "v"(l1), "v"(l2), "v"(l3));
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   __syncthreads();  // pass 1 is done with both buffers
-  run_pass(true, pass2_tile);
+  run_pass(IntC<NS2>(), true, pass2_tile);
+  pv_regs(vt_held, p_held);
 
   // ================= epilogue =================
   float lrun = (l0 + l1) + (l2 + l3);
@@ -618,7 +913,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       uint16_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[e] = (c + e < d) ? to_out<OUTDT>((float)acc[cb][4 * r + e] * vs[c + e] * ninv_l) : (uint16_t)0;
+        const float x = (float)acc[cb][4 * r + e] * vs[c + e] * ninv_l;
+        o[e] = (c + e < d) ? (p.out_f16 ? f32_to_f16(x) : f32_to_bf16(x)) : (uint16_t)0;
       }
       if (c + 3 < d && (d & 3) == 0) {
         *reinterpret_cast<uint2*>(outp + c) =
@@ -633,21 +929,19 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 }
 
 template <int NKB, int NCB, int BIAS>
-hipError_t launch_t(const Params& p, int nblocks, int out_dt, hipStream_t s) {
-  if (out_dt == BA_F16)
-    hipLaunchKernelGGL((attn_fwd_kernel<NKB, NCB, BIAS, BA_F16>), dim3(nblocks), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<NKB, NCB, BIAS, BA_BF16>), dim3(nblocks), dim3(256), 0, s, p);
+hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((attn_fwd_kernel<NKB, NCB, BIAS>), dim3(nblocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int NKB, int NCB>
-hipError_t launch_bias(const Params& p, int bias, int nblocks, int out_dt, hipStream_t s) {
+hipError_t launch_bias(const Params& p, int bias, int nblocks, hipStream_t s) {
   switch (bias) {
-    case BIAS_NONE: return launch_t<NKB, NCB, BIAS_NONE>(p, nblocks, out_dt, s);
-    case BIAS_DENSE_F32: return launch_t<NKB, NCB, BIAS_DENSE_F32>(p, nblocks, out_dt, s);
-    case BIAS_DENSE_F16: return launch_t<NKB, NCB, BIAS_DENSE_F16>(p, nblocks, out_dt, s);
-    default: return launch_t<NKB, NCB, BIAS_RELPOS>(p, nblocks, out_dt, s);
+    case BIAS_NONE: return launch_t<NKB, NCB, BIAS_NONE>(p, nblocks, s);
+    case BIAS_DENSE_F32: return launch_t<NKB, NCB, BIAS_DENSE_F32>(p, nblocks, s);
+    case BIAS_DENSE_F16: return launch_t<NKB, NCB, BIAS_DENSE_F16>(p, nblocks, s);
+    case BIAS_DENSE_ANY: return launch_t<NKB, NCB, BIAS_DENSE_ANY>(p, nblocks, s);
+    default: return launch_t<NKB, NCB, BIAS_RELPOS>(p, nblocks, s);
   }
 }
 
@@ -668,14 +962,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.v_swz_shift = -1;
   if (p.v_dma && (a.d == 32 || a.d == 64 || a.d == 128)) p.v_swz_shift = a.d == 32 ? 2 : a.d == 64 ? 1 : 0;
   p.out = a.out;
+  p.out_f16 = a.out_dt == BA_F16;
+  p.mk_vec = (a.N % 4) == 0 && reinterpret_cast<uintptr_t>(a.kmu) % 16 == 0;
   int bias = BIAS_NONE;
-  p.bias_vec = 0;
+  p.bias_f16 = 0;
   p.relpos_fast = 0;
   if (a.bias_kind == BA_BIAS_DENSE) {
-    bias = a.bias_dtype == BA_F32 ? BIAS_DENSE_F32 : BIAS_DENSE_F16;
     const int per16 = a.bias_dtype == BA_F32 ? 4 : 8;  // elements per 16 bytes
-    p.bias_vec = (a.N % per16 == 0) && (a.bias_bstride % per16 == 0) &&
-                 (reinterpret_cast<uintptr_t>(a.bias) % 16 == 0);
+    const bool vec = (a.N % per16 == 0) && (a.bias_bstride % per16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(a.bias) % 16 == 0);
+    p.bias_f16 = a.bias_dtype == BA_F16;
+    bias = !vec ? BIAS_DENSE_ANY : (a.bias_dtype == BA_F32 ? BIAS_DENSE_F32 : BIAS_DENSE_F16);
   } else if (a.bias_kind == BA_BIAS_RELPOS) {
     bias = BIAS_RELPOS;
     p.relpos_fast = (a.grid_w % 16 == 0) && (a.n_prefix % 16 == 0);
@@ -684,10 +981,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int ncb = (a.d + 31) / 32;
   switch (ncb) {
-    case 1: return launch_bias<1, 1>(p, bias, (int)nblocks, a.out_dt, s);
-    case 2: return launch_bias<1, 2>(p, bias, (int)nblocks, a.out_dt, s);
-    case 3: return launch_bias<2, 3>(p, bias, (int)nblocks, a.out_dt, s);
-    default: return launch_bias<2, 4>(p, bias, (int)nblocks, a.out_dt, s);
+    case 1: return launch_bias<1, 1>(p, bias, (int)nblocks, s);
+    case 2: return launch_bias<1, 2>(p, bias, (int)nblocks, s);
+    case 3: return launch_bias<2, 3>(p, bias, (int)nblocks, s);
+    default: return launch_bias<2, 4>(p, bias, (int)nblocks, s);
   }
 }
 
