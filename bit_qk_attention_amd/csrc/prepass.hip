@@ -47,56 +47,64 @@ __global__ __launch_bounds__(256) void pack_qk_kernel(
 }
 
 // pack_qk for d % 8 == 0: the threads of a block cooperate on whole tokens.
-// Thread i loads the 16 bytes at element 8i of the block's token range (one
-// fully coalesced 4 KB read per block), i.e. channels 8p..8p+7 of token i/P
-// (P = d/8 pieces per token); it forms their 8 sign bits and a float64
-// partial sum of |x|. The pieces are combined through LDS: each 32-bit word
-// from its 4 pieces, mu from the P partial sums in channel order.
+// The block's token range is a contiguous run of 16-byte chunks (8 channels
+// each, P = d/8 per token); thread i loads chunks i + 256u, u < kPackU (each
+// load of the block one fully coalesced 4 KB run, kPackU of them in flight
+// per thread), forms each chunk's 8 sign bits and a float64 partial sum of
+// |x|. The pieces are combined through LDS: each 32-bit word from its 4
+// chunks, mu from the P partial sums in channel order.
+constexpr int kPackU = 4;
 template <int DT>
 __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
     int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
     uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
-  __shared__ uint32_t bits_s[256];
-  __shared__ double sum_s[256];
+  __shared__ uint32_t bits_s[256 * kPackU];
+  __shared__ double sum_s[256 * kPackU];
   const uint16_t* x = blockIdx.y == 0 ? q : k;
   uint32_t* bits = blockIdx.y == 0 ? qbits : kbits;
   float* mu = blockIdx.y == 0 ? qmu : kmu;
-  const int P = d >> 3;                  // pieces per token (1..16)
-  const int Tb = 256 / P;                // whole tokens per block
+  const int P = d >> 3;                  // chunks per token (1..16)
+  const int TB = 256 * kPackU / P;       // whole tokens per block
   const int W = (d + 31) >> 5;
-  const int64_t tok0 = (int64_t)blockIdx.x * Tb;
+  const int64_t tok0 = (int64_t)blockIdx.x * TB;
+  const int nchunk = (int)min((int64_t)TB, ntok - tok0) * P;  // valid chunks of this block
   const int i = threadIdx.x;
-  uint32_t b8 = 0;
-  double s = 0.0;
-  if (i < Tb * P && tok0 + i / P < ntok) {
-    const u4v raw = *reinterpret_cast<const u4v*>(x + tok0 * d + 8 * i);
+  u4v raw[kPackU];
+#pragma unroll
+  for (int u = 0; u < kPackU; ++u) {
+    const int c = i + 256 * u;
+    raw[u] = c < nchunk ? *reinterpret_cast<const u4v*>(x + tok0 * d + 8 * c) : (u4v){0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < kPackU; ++u) {
+    uint32_t b8 = 0;
+    double s = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint16_t h = (uint16_t)(raw[e >> 1] >> ((e & 1) * 16));
+      const uint16_t h = (uint16_t)(raw[u][e >> 1] >> ((e & 1) * 16));
       b8 |= neg_bit<DT>(h) << e;
       s += (double)fabsf(to_f32<DT>(h));
     }
+    bits_s[i + 256 * u] = b8;
+    sum_s[i + 256 * u] = s;
   }
-  bits_s[i] = b8;
-  sum_s[i] = s;
   __syncthreads();
-  for (int j = i; j < Tb * W; j += 256) {
+  const int ntb = nchunk / P;  // valid tokens of this block
+  for (int j = i; j < ntb * W; j += 256) {
     const int tl = j / W, w = j % W;
-    if (tok0 + tl < ntok) {
-      uint32_t word = 0;
+    uint32_t word = 0;
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int pc = 4 * w + pp;
-        if (pc < P) word |= bits_s[tl * P + pc] << (8 * pp);
-      }
-      bits[(tok0 + tl) * W + w] = word;
+    for (int pp = 0; pp < 4; ++pp) {
+      const int pc = 4 * w + pp;
+      if (pc < P) word |= bits_s[tl * P + pc] << (8 * pp);
     }
+    bits[(tok0 + tl) * W + w] = word;
   }
-  if (i < Tb && tok0 + i < ntok) {
+  for (int tl = i; tl < ntb; tl += 256) {
     double acc = 0.0;
-    for (int pc = 0; pc < P; ++pc) acc += sum_s[i * P + pc];
-    mu[tok0 + i] = (float)(acc / (double)d);
+    for (int pc = 0; pc < P; ++pc) acc += sum_s[tl * P + pc];
+    mu[tok0 + tl] = (float)(acc / (double)d);
   }
 }
 
@@ -106,8 +114,8 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t nto
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   if (d % 8 == 0) {
-    const int Tb = 256 / (d / 8);
-    const dim3 grid((unsigned)((ntok + Tb - 1) / Tb), 2);
+    const int TB = 256 * kPackU / (d / 8);
+    const dim3 grid((unsigned)((ntok + TB - 1) / TB), 2);
     if (dt == BA_F16)
       hipLaunchKernelGGL(pack_qk_coop_kernel<BA_F16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
     else
@@ -242,8 +250,81 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
   }
 }
 
+// quant_v for heads that fit in the registers of one 1024-thread block
+// (d % 8 == 0, N <= kQvRows * R): one block per head reads the head once.
+// The head is row-major N x d, so thread t < R*P (P = d/8 16-byte pieces
+// per row, R = 1024/P rows per sweep) owns piece t % P of rows t / P + k*R:
+// every load of the block is one contiguous run of 16*R*P bytes. Channel
+// maxima go through an LDS atomic max on the float bits (non-negative), then
+// the held values are quantised and written as int8.
+constexpr int kQvRows = 12;  // rows per thread held in registers
+template <int DT>
+__global__ __launch_bounds__(1024) void quant_v_head_kernel(
+    const uint16_t* __restrict__ v, int N, int d, int8_t* __restrict__ vq, float* __restrict__ vscale) {
+  __shared__ uint32_t amax_bits[128];
+  __shared__ float inv_s[128];
+  const int bh = blockIdx.x;
+  const int P = d >> 3, R = 1024 / P;
+  const int t = threadIdx.x;
+  const int piece = t % P, r0 = t / P;
+  const bool active = r0 < R;
+  if (t < d) amax_bits[t] = 0u;
+  __syncthreads();
+  const uint16_t* vh = v + (int64_t)bh * N * d + 8 * piece;
+  int8_t* qh = vq + (int64_t)bh * N * d + 8 * piece;
+  u4v x[kQvRows];
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < kQvRows; ++k) {
+    const int r = r0 + k * R;
+    x[k] = (active && r < N) ? *reinterpret_cast<const u4v*>(vh + (int64_t)r * d) : (u4v){0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < kQvRows; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16)))));
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicMax(&amax_bits[8 * piece + e], __float_as_uint(m[e]));
+  }
+  __syncthreads();
+  if (t < d) {
+    const float a = __uint_as_float(amax_bits[t]);
+    inv_s[t] = a > 0.0f ? 127.0f / a : 0.0f;
+    vscale[(int64_t)bh * d + t] = a / 127.0f;
+  }
+  __syncthreads();
+  float inv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
+#pragma unroll
+  for (int k = 0; k < kQvRows; ++k) {
+    const int r = r0 + k * R;
+    if (active && r < N) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float y = __builtin_rintf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16))) * inv[e]);
+        y = fminf(fmaxf(y, -127.0f), 127.0f);
+        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
+        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+      }
+      *reinterpret_cast<uint2*>(qh + (int64_t)r * d) = make_uint2(lo, hi);
+    }
+  }
+}
+
 hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
                           int8_t* vq, float* vscale, hipStream_t s) {
+  if (d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
+    const uint16_t* v16 = static_cast<const uint16_t*>(v);
+    if (dt == BA_F16)
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale);
+    else
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale);
+    return hipGetLastError();
+  }
   // widest channel group (whole rows when possible) that still gives
   // >= 1024 blocks; at least 8 channels per group, at most 128.
   int CG = d;
