@@ -82,9 +82,10 @@ __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
     double s = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint16_t h = (uint16_t)(raw[u][e >> 1] >> ((e & 1) * 16));
-      b8 |= neg_bit<DT>(h) << e;
-      s += (double)fabsf(to_f32<DT>(h));
+      // x < 0 as a float compare: false for -0 and NaN, true for -inf
+      const float xf = to_f32<DT>((uint16_t)(raw[u][e >> 1] >> ((e & 1) * 16)));
+      b8 |= xf < 0.0f ? (1u << e) : 0u;
+      s += (double)fabsf(xf);
     }
     bits_s[i + 256 * u] = b8;
     sum_s[i + 256 * u] = s;
