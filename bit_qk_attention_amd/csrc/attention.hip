@@ -119,6 +119,20 @@ __device__ __forceinline__ float partner32(float x, int lane) {
 }
 
 
+// Value of lane I of this lane's 16-lane row (DPP row_newbcast; the
+// compiler folds it into the consuming VALU instruction).
+template <int I>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF, true));
+}
+// sc[i] = sig[i] * (lane i of the row's value of mrow). In the S^T layout
+// register i of lane l holds key 16*(l/32) + i of the block, so with lane l
+// holding the scale of key 16*(l/32) + l%16 this is sig * mu_k per key.
+template <int... I>
+__device__ __forceinline__ void mul_key_scales(float* sc, const v16f& sig, float mrow, std::integer_sequence<int, I...>) {
+  ((sc[I] = sig[I] * row_bcast<I>(mrow)), ...);
+}
+
 template <bool B>
 struct BoolC {
   static constexpr bool value = B;
@@ -473,14 +487,20 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     constexpr bool MASK = decltype(mask)::value;
     const int jl = kb * 32 + 16 * g;  // first key of the lane's 16, in the tile
     const int jb = t * kBC + jl;
-    const float4* mkp = reinterpret_cast<const float4*>(sb.mk + jl);
+    if constexpr (BIAS == BIAS_RELPOS || BIAS == BIAS_DENSE_ANY) {
+      // (the product feeds two bias paths here; a row broadcast would not
+      // fold into it, so the 16 scales are read as vectors)
+      const float4* mkp = reinterpret_cast<const float4*>(sb.mk + jl);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4 m4 = mkp[r];
-      sc[4 * r + 0] = sig[4 * r + 0] * m4.x;
-      sc[4 * r + 1] = sig[4 * r + 1] * m4.y;
-      sc[4 * r + 2] = sig[4 * r + 2] * m4.z;
-      sc[4 * r + 3] = sig[4 * r + 3] * m4.w;
+      for (int r = 0; r < 4; ++r) {
+        const float4 m4 = mkp[r];
+        sc[4 * r + 0] = sig[4 * r + 0] * m4.x;
+        sc[4 * r + 1] = sig[4 * r + 1] * m4.y;
+        sc[4 * r + 2] = sig[4 * r + 2] * m4.z;
+        sc[4 * r + 3] = sig[4 * r + 3] * m4.w;
+      }
+    } else {
+      mul_key_scales(sc, sig, sb.mk[jl + (lane & 15)], std::make_integer_sequence<int, 16>{});
     }
     if (DENSE) {
       const int64_t row = (int64_t)b * p.bias_bstride + ((int64_t)h * N + qc) * N;
@@ -559,14 +579,55 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       m1 = fmaxf(fmaxf(m1, sc[i + 2]), sc[i + 3]);
     }
   };
+  // key scales and fp16 bias words of this lane's 16 keys in block kb, read
+  // from the stage ahead of use (full tiles of the fp16 dense-bias path)
+  struct KeyVals {
+    float mk;  // scale of key 16 * g + lane % 16 of the block
+    u4v bb[2];
+  };
+  auto load_keyvals = [&](auto bufc, int kb, KeyVals& r) {
+    KS& sb = pick(bufc);
+    r.mk = sb.mk[kb * 32 + 16 * g + (lane & 15)];
+    const int rl = wave * kQW + ql;
+    const u4v* src = reinterpret_cast<const u4v*>(sb.bt + rl * kBC);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.bb[i] = src[(4 * kb + 2 * g + i) ^ bswz(rl)];
+  };
+  auto scores_kv = [&](const v16f& sig, const KeyVals& r, float* sc) {
+    mul_key_scales(sc, sig, r.mk, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t wd = r.bb[e >> 3][(e >> 1) & 3];
+      sc[e] = __builtin_fmaf(sc[e], c0, f16_to_f32((uint16_t)(wd >> (16 * (e & 1)))));
+    }
+  };
   auto pass1_tile = [&](auto tail, int t, auto bufc) {
-    const v16f sig0 = qk_block(bufc, 0);
-    const v16f sig1 = qk_block(bufc, 1);
+    constexpr bool TAIL = decltype(tail)::value;
     float sc[16];
-    scores(tail, tail, t, bufc, 0, sig0, sc);
-    max16(sc);
-    scores(tail, tail, t, bufc, 1, sig1, sc);
-    max16(sc);
+    if constexpr (BIAS == BIAS_DENSE_F16 && !TAIL) {
+      // every LDS read of the tile is issued first (K operands, then key
+      // scales and bias), so one wait covers them rather than one per use
+      u4v a0[NKB], a1[NKB];
+      k_operand(bufc, 0, a0);
+      k_operand(bufc, 1, a1);
+      KeyVals kv0, kv1;
+      load_keyvals(bufc, 0, kv0);
+      load_keyvals(bufc, 1, kv1);
+      __builtin_amdgcn_sched_barrier(0);
+      const v16f sig0 = qk_mfma(a0);
+      const v16f sig1 = qk_mfma(a1);
+      scores_kv(sig0, kv0, sc);
+      max16(sc);
+      scores_kv(sig1, kv1, sc);
+      max16(sc);
+    } else {
+      const v16f sig0 = qk_block(bufc, 0);
+      const v16f sig1 = qk_block(bufc, 1);
+      scores(tail, tail, t, bufc, 0, sig0, sc);
+      max16(sc);
+      scores(tail, tail, t, bufc, 1, sig1, sc);
+      max16(sc);
+    }
     // keep the running max here, ahead of the end-of-tile wait, rather than
     // let the compiler sink it past the wait
     const float ma = m0, mb = m1;
@@ -649,7 +710,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     }
     struct Blk {
       uint32_t kw[NKB];
-      float4 mk[4];
+      float4 mk[4];  // scales of keys 16 * g .. 16 * g + 15 of the block
       u4v bb[BIAS == BIAS_DENSE_F16 ? 4 : 1][2];
     };
     const float* kmu_bh = p.kmu + bh * N;
@@ -964,6 +1025,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.out = a.out;
   p.out_f16 = a.out_dt == BA_F16;
   p.mk_vec = (a.N % 4) == 0 && reinterpret_cast<uintptr_t>(a.kmu) % 16 == 0;
+
   int bias = BIAS_NONE;
   p.bias_f16 = 0;
   p.relpos_fast = 0;
