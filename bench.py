@@ -46,11 +46,12 @@ def kernel_sha() -> str:
 
 def algorithmic_bytes(s) -> int:
     """HBM bytes one attention launch must move at minimum: packed Q and K
-    (bits + scale), int8 V + scales, the output, and the bias (a shared
-    dense bias once, not per batch element; a relative-position table)."""
+    (bits + scale), int8 V + channel scales + channel sums, the output, and
+    the bias (a shared dense bias once, not per batch element; a relative-
+    position table)."""
     W = (s.d + 31) // 32
     BH, N, d = s.B * s.H, s.N, s.d
-    nb = 2 * BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d + 2 * BH * N * d
+    nb = 2 * BH * N * (4 * W + 4) + BH * N * d + 8 * BH * d + 2 * BH * N * d
     if s.bias.startswith("dense"):
         esz = 4 if s.bias == "dense_f32" else 2
         nb += (1 if s.bias_shared else s.B) * s.H * N * N * esz
@@ -135,17 +136,18 @@ class Workload:
         self.kmu = torch.empty_like(self.qmu)
         self.vq = torch.empty((B, H, N, d), dtype=torch.int8, device="cuda")
         self.vscale = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+        self.vsum = torch.empty((B, H, d), dtype=torch.int32, device="cuda")
         self.out = torch.empty_like(self.q)
         self.stream = torch.cuda.current_stream()
 
     def step(self):
         ba = self.ba
         ba.ba_pack_qk(self.q, self.k, self.qbits, self.qmu, self.kbits, self.kmu, self.stream)
-        ba.ba_quant_v(self.v, self.vq, self.vscale, self.stream)
+        ba.ba_quant_v(self.v, self.vq, self.vscale, self.vsum, self.stream)
         self.attn()
 
     def attn(self):
-        self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
+        self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale, self.vsum,
                                  self.bias, self.out, self.stream)
 
     def time(self, fn, iters: int, warmup: int) -> float:

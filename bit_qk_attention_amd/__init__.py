@@ -53,9 +53,9 @@ def lib() -> ctypes.CDLL:
         L.ba_packed_words.restype = I
         L.ba_pack_qk.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P]
         L.ba_pack_qk.restype = I
-        L.ba_quant_v.argtypes = [P, I, I, I, I, I, P, P, P]
+        L.ba_quant_v.argtypes = [P, I, I, I, I, I, P, P, P, P]
         L.ba_quant_v.restype = I
-        L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
+        L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
         L.ba_attention_fwd.restype = I
         L.ba_debug_hamming_scores.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
         L.ba_debug_hamming_scores.restype = I
@@ -151,22 +151,23 @@ def ba_pack_qk(q, k, qbits, qmu, kbits, kmu, stream=None) -> None:
                                           _ptr(kbits), _ptr(kmu), _stream(stream)))
 
 
-def ba_quant_v(v, vq, vscale, stream=None) -> None:
-    """v [B,H,N,d] fp16/bf16 -> vq int8 [B,H,N,d], vscale float32 [B,H,d]."""
-    _require_gpu(v, vq, vscale)
+def ba_quant_v(v, vq, vscale, vsum, stream=None) -> None:
+    """v [B,H,N,d] fp16/bf16 -> vq int8 [B,H,N,d], vscale float32 [B,H,d],
+    vsum int32 [B,H,d] (channel sums of vq)."""
+    _require_gpu(v, vq, vscale, vsum)
     B, H, N, d = v.shape
     _check("ba_quant_v", lib().ba_quant_v(_ptr(v), _dt(v), B, H, N, d, _ptr(vq), _ptr(vscale),
-                                          _stream(stream)))
+                                          _ptr(vsum), _stream(stream)))
 
 
-def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream=None) -> None:
+def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream=None) -> None:
     """Fused forward; out [B,H,N,d] fp16/bf16 defines the shape and output dtype."""
-    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, out)
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum, out)
     B, H, N, d = out.shape
     cb = (bias or Bias()).to_c()
     _check("ba_attention_fwd", lib().ba_attention_fwd(
-        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), ctypes.byref(cb),
-        B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
+        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), _ptr(vsum),
+        ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
 
 
 def ba_debug_hamming_scores(qbits, kbits, d, bh_begin, bh_count, row_begin, row_count, sigma,
@@ -198,16 +199,17 @@ def quant_v(v, stream=None):
     B, H, N, d = v.shape
     vq = torch.empty((B, H, N, d), dtype=torch.int8, device=v.device)
     vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
-    ba_quant_v(v, vq, vscale, stream)
-    return vq, vscale
+    vsum = torch.empty((B, H, d), dtype=torch.int32, device=v.device)
+    ba_quant_v(v, vq, vscale, vsum, stream)
+    return vq, vscale, vsum
 
 
 def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
     """Whole forward pass: pack Q/K, quantise V, fused attention."""
     torch = _torch()
     qbits, qmu, kbits, kmu = pack_qk(q, k, stream)
-    vq, vscale = quant_v(v, stream)
+    vq, vscale, vsum = quant_v(v, stream)
     if out is None:
         out = torch.empty_like(q)
-    ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream)
+    ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream)
     return out

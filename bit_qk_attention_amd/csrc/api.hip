@@ -70,34 +70,41 @@ ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H, in
 }
 
 ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d, int8_t* vq,
-                     float* vscale, void* stream) {
-  if (!v || !vq || !vscale) return BA_ERR_INVALID_ARG;
+                     float* vscale, int32_t* vsum, void* stream) {
+  if (!v || !vq || !vscale || !vsum) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
-  if (!aligned(v, 16) || !aligned(vq, 16) || !aligned(vscale, 4)) return BA_ERR_INVALID_ARG;
-  const int64_t n = (int64_t)B * H * N * d;
-  if (overlap(vq, n, v, 2 * n) || overlap(vscale, (int64_t)B * H * d * 4, v, 2 * n) ||
-      overlap(vq, n, vscale, (int64_t)B * H * d * 4))
+  if (!aligned(v, 16) || !aligned(vq, 16) || !aligned(vscale, 4) || !aligned(vsum, 4))
     return BA_ERR_INVALID_ARG;
-  return from_hip(launch_quant_v(v, dt, B * H, N, d, vq, vscale, static_cast<hipStream_t>(stream)));
+  const int64_t n = (int64_t)B * H * N * d;
+  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale, of vsum
+  const void* outs[3] = {vq, vscale, vsum};
+  const int64_t osz[3] = {n, nc, nc};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], osz[i], v, 2 * n)) return BA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
+  }
+  return from_hip(launch_quant_v(v, dt, B * H, N, d, vq, vscale, vsum, static_cast<hipStream_t>(stream)));
 }
 
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,
                            const float* kmu, const int8_t* vq, const float* vscale,
-                           const ba_bias* bias, int B, int H, int N, int d, void* out,
-                           ba_dtype out_dt, void* stream) {
-  if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !out) return BA_ERR_INVALID_ARG;
+                           const int32_t* vsum, const ba_bias* bias, int B, int H, int N,
+                           int d, void* out, ba_dtype out_dt, void* stream) {
+  if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum || !out) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (!dtype16(out_dt)) return BA_ERR_UNSUPPORTED;
   if (!aligned(qbits, 16) || !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(out, 16) ||
-      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4))
+      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(vsum, 4))
     return BA_ERR_INVALID_ARG;
   const int64_t ntok = (int64_t)B * H * N;
   const int64_t W = (d + 31) / 32;
   AttnArgs a = {};
   a.qbits = qbits; a.qmu = qmu; a.kbits = kbits; a.kmu = kmu; a.vq = vq; a.vscale = vscale;
+  a.vsum = vsum;
   a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt;
   a.bias_kind = BA_BIAS_NONE;
   int64_t bias_bytes = 0;
@@ -128,10 +135,10 @@ ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32
     a.bias = bias->data;
   }
   const int64_t out_bytes = ntok * d * 2;
-  const void* ins[7] = {qbits, qmu, kbits, kmu, vq, vscale, a.bias};
-  const int64_t isz[7] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
-                          (int64_t)B * H * d * 4, bias_bytes};
-  for (int i = 0; i < 7; ++i)
+  const void* ins[8] = {qbits, qmu, kbits, kmu, vq, vscale, vsum, a.bias};
+  const int64_t isz[8] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
+                          (int64_t)B * H * d * 4, (int64_t)B * H * d * 4, bias_bytes};
+  for (int i = 0; i < 8; ++i)
     if (overlap(out, out_bytes, ins[i], isz[i])) return BA_ERR_INVALID_ARG;
   return from_hip(launch_attention(a, static_cast<hipStream_t>(stream)));
 }

@@ -31,9 +31,10 @@
 //    straight from row-major V in LDS through the transposing LDS read
 //    (ds_read_b64_tr_b8: in each 16-lane group, output lane 8h+b receives
 //    byte b of the 8-byte rows addressed by lanes 2k+h, k = 0..7). gfx950
-//    int8 MFMA is signed x signed and p8 reaches 255, so each block adds
-//    V^T (127 - p8) (127 - p8 = p8 XOR 0x7F as a signed byte) and then
-//    V^T (-127); the accumulator ends at -sum_j p8_j v8_j, exact in int32.
+//    int8 MFMA is signed x signed and p8 reaches 255, so the product uses
+//    the signed byte 127 - p8 (= p8 XOR 0x7F): the accumulator ends at
+//    sum_j (127 - p8_j) v8_j, and sum_j p8_j v8_j = 127 * vsum - that, with
+//    vsum the channel sums of v8 (from the V quantisation). Exact in int32.
 //  * Softmax in base 2: x = s*log2(e) - m*log2(e) + log2(255), so a single
 //    v_exp_f32 gives 255*exp(s - m); v_cvt_pk_u8_f32 rounds to nearest even
 //    and clamps to [0, 255].
@@ -73,6 +74,7 @@ struct Params {
   const float* kmu;
   const int8_t* vq;
   const float* vscale;
+  const int32_t* vsum;
   const void* bias;
   int64_t bias_bstride;
   int grid_h, grid_w, n_prefix;
@@ -851,10 +853,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 
   // ================= pass 2: u8 P, row sum, integer P.V =================
   float l0 = 0.0f, l1 = 0.0f, l2 = 0.0f, l3 = 0.0f;
-  v16i acc[NCB];  // ends at -sum_j p8_j v8_j
+  v16i acc[NCB];  // ends at sum_j (127 - p8_j) v8_j
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = (v16i){};
-  const v4i m127 = {(int)0x81818181, (int)0x81818181, (int)0x81818181, (int)0x81818181};  // -127 bytes
   // transposing-read address of this lane for the V^T operand: row
   // 16*(lane/32) + (lane%16)/2 (+8 for the upper half), column
   // 16*((lane/16)%2) + 8*(lane%2) (+32 per channel block)
@@ -901,13 +902,11 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       vt[cb] = (v4i){lo[0], lo[1], hi[0], hi[1]};
     }
   };
-  // P.V of one key block: acc += V^T (127 - p8) + V^T (-127)
+  // P.V of one key block: acc += V^T (127 - p8)
   auto pv_regs = [&](const v4i* vt, const v4i& bop) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb)
       acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vt[cb], bop, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vt[cb], m127, acc[cb], 0, 0, 0);
-    }
   };
   // A wave issues in order, so the matrix products of a tile are spread
   // through the VALU work that does not depend on them: block 1's Q.K and
@@ -934,7 +933,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     scores(tail, BoolC<false>(), t, bufc, 0, sig0, sc);
     const v4i p0 = probs(tail, t, 0, sc);
 #pragma unroll
-    for (int i = 0; i < NKB + 2 * NCB; ++i) {
+    for (int i = 0; i < NKB + NCB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);    // VALU
     }
@@ -944,7 +943,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     p_held = probs(tail, t, 1, sc);
     read_vt(bufc, 1, vt_held);
 #pragma unroll
-    for (int i = 0; i < 2 * NCB; ++i) {
+    for (int i = 0; i < NCB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
@@ -963,9 +962,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   float lrun = (l0 + l1) + (l2 + l3);
   lrun += partner32(lrun, lane);
   if (!qvalid) return;
-  const float ninv_l = -1.0f / lrun;  // the accumulator holds -A
+  const float inv_l = 1.0f / lrun;
   uint16_t* outp = static_cast<uint16_t*>(p.out) + (bh * N + qi) * d;
   const float* vs = p.vscale + bh * d;
+  const int32_t* vsm = p.vsum + bh * d;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -974,7 +974,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       uint16_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = (float)acc[cb][4 * r + e] * vs[c + e] * ninv_l;
+        const int ce = min(c + e, d - 1);
+        const int a = 127 * vsm[ce] - acc[cb][4 * r + e];  // sum_j p8_j v8_j
+        const float x = (float)a * vs[ce] * inv_l;
         o[e] = (c + e < d) ? (p.out_f16 ? f32_to_f16(x) : f32_to_bf16(x)) : (uint16_t)0;
       }
       if (c + 3 < d && (d & 3) == 0) {
@@ -1011,7 +1013,7 @@ hipError_t launch_bias(const Params& p, int bias, int nblocks, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   Params p;
   p.qbits = a.qbits; p.qmu = a.qmu; p.kbits = a.kbits; p.kmu = a.kmu;
-  p.vq = a.vq; p.vscale = a.vscale;
+  p.vq = a.vq; p.vscale = a.vscale; p.vsum = a.vsum;
   p.bias = a.bias; p.bias_bstride = a.bias_bstride;
   p.grid_h = a.grid_h; p.grid_w = a.grid_w; p.n_prefix = a.n_prefix;
   p.B = a.B; p.H = a.H; p.N = a.N; p.d = a.d; p.W = (a.d + 31) / 32;

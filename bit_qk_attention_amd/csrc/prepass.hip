@@ -135,8 +135,8 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t nto
 // quant_v: one block per (head, channel group of CG channels). The block
 // reads the group's columns of all N tokens twice: pass 1 takes the per-
 // channel max |v| (an LDS atomic max on the float bits, valid because the
-// values are non-negative), pass 2 quantises with inv = 127/amax and writes
-// int8. With CG == d a wave reads whole rows (fully coalesced); smaller
+// values are non-negative), pass 2 quantises with inv = 127/amax, writes
+// int8 and gathers the channel sums of the int8 values (LDS atomic adds). With CG == d a wave reads whole rows (fully coalesced); smaller
 // groups keep enough blocks in flight when there are few heads, and the
 // block order keeps the groups of one head on one XCD so they share L2.
 // VEC: d % 8 == 0, each thread handles 8 consecutive channels.
@@ -144,9 +144,10 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t nto
 template <int DT>
 __global__ __launch_bounds__(256) void quant_v_kernel(
     const uint16_t* __restrict__ v, int nbh, int N, int d, int CG,
-    int8_t* __restrict__ vq, float* __restrict__ vscale) {
+    int8_t* __restrict__ vq, float* __restrict__ vscale, int32_t* __restrict__ vsum) {
   __shared__ uint32_t amax_bits[128];
   __shared__ float inv_s[128];
+  __shared__ int32_t sum_s[128];
   const int ngroups = (d + CG - 1) / CG;
   const int nblk = nbh * ngroups;
   // XCD-aware order: consecutive block ids go to different XCDs, so hand each
@@ -156,7 +157,10 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
   const int bh = u / ngroups;
   const int c0 = (u % ngroups) * CG;
   const int cg = min(CG, d - c0);
-  for (int i = threadIdx.x; i < cg; i += blockDim.x) amax_bits[i] = 0u;
+  for (int i = threadIdx.x; i < cg; i += blockDim.x) {
+    amax_bits[i] = 0u;
+    sum_s[i] = 0;
+  }
   __syncthreads();
 
   const uint16_t* vh = v + (int64_t)bh * N * d;
@@ -203,12 +207,14 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
       float inv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) inv[e] = inv_s[piece * 8 + e];
+      int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       auto quant8 = [&](const u4v& raw) -> uint2 {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
           y = fminf(fmaxf(y, -127.0f), 127.0f);
+          csum[e] += (int)y;
           const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
           if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
         }
@@ -228,6 +234,8 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
         const int64_t off = (int64_t)j * d + c0 + piece * 8;
         *reinterpret_cast<uint2*>(qh + off) = quant8(*reinterpret_cast<const u4v*>(vh + off));
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicAdd(&sum_s[piece * 8 + e], csum[e]);
     }
   } else {
     // generic d: one thread per (row, channel) element, scalar accesses
@@ -247,8 +255,11 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
       float y = __builtin_rintf(to_f32<DT>(vh[(int64_t)j * d + c0 + c]) * inv_s[c]);
       y = fminf(fmaxf(y, -127.0f), 127.0f);
       qh[(int64_t)j * d + c0 + c] = (int8_t)(int)y;
+      atomicAdd(&sum_s[c], (int)y);
     }
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < cg; i += blockDim.x) vsum[(int64_t)bh * d + c0 + i] = sum_s[i];
 }
 
 // quant_v for heads that fit in the registers of one 1024-thread block
@@ -257,19 +268,25 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
 // per row, R = 1024/P rows per sweep) owns piece t % P of rows t / P + k*R:
 // every load of the block is one contiguous run of 16*R*P bytes. Channel
 // maxima go through an LDS atomic max on the float bits (non-negative), then
-// the held values are quantised and written as int8.
+// the held values are quantised and written as int8, and their channel sums
+// gathered with LDS atomic adds.
 constexpr int kQvRows = 12;  // rows per thread held in registers
 template <int DT>
 __global__ __launch_bounds__(1024) void quant_v_head_kernel(
-    const uint16_t* __restrict__ v, int N, int d, int8_t* __restrict__ vq, float* __restrict__ vscale) {
+    const uint16_t* __restrict__ v, int N, int d, int8_t* __restrict__ vq, float* __restrict__ vscale,
+    int32_t* __restrict__ vsum) {
   __shared__ uint32_t amax_bits[128];
   __shared__ float inv_s[128];
+  __shared__ int32_t sum_s[128];
   const int bh = blockIdx.x;
   const int P = d >> 3, R = 1024 / P;
   const int t = threadIdx.x;
   const int piece = t % P, r0 = t / P;
   const bool active = r0 < R;
-  if (t < d) amax_bits[t] = 0u;
+  if (t < d) {
+    amax_bits[t] = 0u;
+    sum_s[t] = 0;
+  }
   __syncthreads();
   const uint16_t* vh = v + (int64_t)bh * N * d + 8 * piece;
   int8_t* qh = vq + (int64_t)bh * N * d + 8 * piece;
@@ -299,6 +316,7 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
   float inv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
+  int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k) {
     const int r = r0 + k * R;
@@ -308,22 +326,29 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
       for (int e = 0; e < 8; ++e) {
         float y = __builtin_rintf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16))) * inv[e]);
         y = fminf(fmaxf(y, -127.0f), 127.0f);
+        csum[e] += (int)y;
         const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
         if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
       }
       *reinterpret_cast<uint2*>(qh + (int64_t)r * d) = make_uint2(lo, hi);
     }
   }
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicAdd(&sum_s[8 * piece + e], csum[e]);
+  }
+  __syncthreads();
+  if (t < d) vsum[(int64_t)bh * d + t] = sum_s[t];
 }
 
 hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
-                          int8_t* vq, float* vscale, hipStream_t s) {
+                          int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s) {
   if (d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     if (dt == BA_F16)
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale, vsum);
     else
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale, vsum);
     return hipGetLastError();
   }
   // widest channel group (whole rows when possible) that still gives
@@ -341,9 +366,9 @@ hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
   const int64_t nblk = (int64_t)nbh * ngroups;
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   if (dt == BA_F16)
-    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale);
+    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale, vsum);
   else
-    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale);
+    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale, vsum);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@
  *    faults surface at the caller's next synchronisation. No C++ exception
  *    crosses this interface. The library is stateless and re-entrant.
  *  - Alignment: bits / vq / out / Q / K / V pointers 16-byte aligned; mu,
- *    vscale and bias pointers 4-byte aligned (fp16 bias: 2-byte).
+ *    vscale, vsum and bias pointers 4-byte aligned (fp16 bias: 2-byte).
  */
 #ifndef BINATTN_H
 #define BINATTN_H
@@ -101,10 +101,12 @@ ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H,
 /* Channel-wise 8-bit V (zh section 2.2 item 3; nl Methodologie 2): for each
  * (b,h,c), amax = max_j |v_jc| over the N tokens; vq = clamp(rne(v * (127 /
  * amax)), -127, 127) in float32; vscale = amax / 127; an all-zero channel
- * gives vq = 0 and vscale = 0.
- * v: [B,H,N,d] fp16 or bf16; vq: int8 [B,H,N,d]; vscale: float [B,H,d]. */
+ * gives vq = 0 and vscale = 0. vsum = sum_j vq_jc, the channel sums of the
+ * quantised V (exact; ba_attention_fwd uses them, see there).
+ * v: [B,H,N,d] fp16 or bf16; vq: int8 [B,H,N,d]; vscale: float [B,H,d];
+ * vsum: int32 [B,H,d]. */
 ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
-                     int8_t* vq, float* vscale, void* stream);
+                     int8_t* vq, float* vscale, int32_t* vsum, void* stream);
 
 /* Fused BinaryAttention forward (zh sections 2.1-2.3; nl Methodologie 1-3;
  * it section 2; fr section 2B; pt section 2B-2C), non-causal, self-attention
@@ -117,6 +119,9 @@ ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
  *   out_ic   = A_ic * vscale_c / (255 * l_i)    rounded to out_dt
  * m_i is the exact row maximum (the kernel finds it in a first pass over the
  * keys), so p8 matches the plain definition up to float rounding.
+ * The matrix cores multiply signed bytes only, so the kernel accumulates
+ * sum_j (127 - p8_ij) * vq_jc and forms A_ic = 127 * vsum_c - that sum;
+ * vsum must therefore be the channel sums of vq (as ba_quant_v writes them).
  * Inputs are the outputs of ba_pack_qk / ba_quant_v (or equivalent data);
  * mu may be any non-negative per-token scale (e.g. a learned one).
  * bias: NULL or kind BA_BIAS_NONE for no bias.
@@ -124,7 +129,8 @@ ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu,
                            const uint32_t* kbits, const float* kmu,
                            const int8_t* vq, const float* vscale,
-                           const ba_bias* bias, int B, int H, int N, int d,
+                           const int32_t* vsum, const ba_bias* bias,
+                           int B, int H, int N, int d,
                            void* out, ba_dtype out_dt, void* stream);
 
 /* Integer Hamming similarity for inspection (zh sections 2.1 and 2.2 item 1;

@@ -145,6 +145,15 @@ def quant_v(v: np.ndarray, dtype: int):
     return vq, vs
 
 
+def channel_sums(vq: np.ndarray) -> np.ndarray:
+    """vq int8 [B,H,N,d] -> int32 [B,H,d]: sum over the tokens of each channel.
+
+    Plain integer sums of the quantised V; the library's fused kernel uses them
+    to undo the 127 - p8 offset of its signed-byte product (the relation
+    sum_j p8_j v_j = 127 * sum_j v_j - sum_j (127 - p8_j) v_j)."""
+    return np.asarray(vq, np.int8).astype(np.int64).sum(axis=2).astype(np.int32)
+
+
 def hamming(qbits, kbits, d, bh0=0, nbh=None, row0=0, nrows=None):
     """qbits, kbits: uint32 [B,H,N,W] -> sigma int32 [nbh, nrows, N]."""
     qbits = np.ascontiguousarray(qbits, np.uint32)

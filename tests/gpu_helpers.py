@@ -45,11 +45,11 @@ class GpuRun:
         self.q, self.k, self.v = (to_dev(x, s.dtype) for x in (inp.q, inp.k, inp.v))
         self.lib_bias, self.ora_bias = dev_bias(inp)
         self.qbits, self.qmu, self.kbits, self.kmu = ba.pack_qk(self.q, self.k)
-        self.vq, self.vscale = ba.quant_v(self.v)
+        self.vq, self.vscale, self.vsum = ba.quant_v(self.v)
         odt = tdtype(s.dtype if out_dt is None else out_dt)
         self.out = torch.empty(self.q.shape, dtype=odt, device="cuda")
         ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
-                            self.lib_bias, self.out)
+                            self.vsum, self.lib_bias, self.out)
         torch.cuda.synchronize()
 
     def out_f32(self) -> np.ndarray:
@@ -58,7 +58,7 @@ class GpuRun:
     def rerun(self):
         out = torch.empty_like(self.out)
         ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
-                            self.lib_bias, out)
+                            self.vsum, self.lib_bias, out)
         torch.cuda.synchronize()
         return out
 

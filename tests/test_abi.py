@@ -52,27 +52,30 @@ def test_pack_rejections(L):
     assert pack(L, kb=A(2)) == INV                        # outputs overlap
 
 
-def quant(L, v=A(0), dt=ba.BA_F16, B=1, H=1, N=8, d=64, vq=A(1), vs=A(2)):
-    return L.ba_quant_v(v, dt, B, H, N, d, vq, vs, None)
+def quant(L, v=A(0), dt=ba.BA_F16, B=1, H=1, N=8, d=64, vq=A(1), vs=A(2), vsum=A(3)):
+    return L.ba_quant_v(v, dt, B, H, N, d, vq, vs, vsum, None)
 
 
 def test_quant_rejections(L):
-    assert quant(L, v=None) == INV and quant(L, vs=None) == INV
+    assert quant(L, v=None) == INV and quant(L, vs=None) == INV and quant(L, vsum=None) == INV
+    assert quant(L, vsum=ctypes.c_void_p(P + 3 * (1 << 32) + 2)) == INV  # not 4-byte aligned
+    assert quant(L, vsum=A(2)) == INV  # outputs overlap
     assert quant(L, H=0) == INV and quant(L, d=200) == UNS and quant(L, dt=ba.BA_F32) == UNS
     assert quant(L, vq=ctypes.c_void_p(P + 1 * (1 << 32) + 8)) == INV
     assert quant(L, vq=A(0)) == INV  # output aliases the input
 
 
 def attn(L, bias=None, B=2, H=2, N=16, d=64, out=A(9), out_dt=ba.BA_BF16, **kw):
-    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6))
+    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6), vsum=A(7))
     args.update(kw)
     pb = ctypes.byref(bias) if bias is not None else None
     return L.ba_attention_fwd(args["qb"], args["qm"], args["kb"], args["km"], args["vq"], args["vs"],
-                              pb, B, H, N, d, out, out_dt, None)
+                              args["vsum"], pb, B, H, N, d, out, out_dt, None)
 
 
 def test_attention_rejections(L):
-    assert attn(L, qb=None) == INV and attn(L, out=None) == INV
+    assert attn(L, qb=None) == INV and attn(L, out=None) == INV and attn(L, vsum=None) == INV
+    assert attn(L, out=A(7)) == INV  # output aliases vsum
     assert attn(L, d=0) == INV and attn(L, d=129) == UNS
     assert attn(L, N=ba.BA_MAX_TOKENS + 1) == UNS
     assert attn(L, out_dt=ba.BA_F32) == UNS and attn(L, out_dt=5) == UNS

@@ -63,6 +63,7 @@ def test_prepass_bit_exact(name):
     vq, vs = oracle.quant_v(inp.v, s.dtype)
     assert np.array_equal(run.vq.cpu().numpy(), vq)
     assert np.array_equal(run.vscale.cpu().numpy(), vs)
+    assert np.array_equal(run.vsum.cpu().numpy(), oracle.channel_sums(vq))
 
 
 @pytest.mark.parametrize("name", sorted(REDUCED))

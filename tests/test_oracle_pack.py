@@ -137,6 +137,25 @@ def test_quant_v_invariants(oracle_lib):
     assert vq.min() >= -127
 
 
+def test_channel_sums_closed_forms(oracle_lib):
+    # a constant channel quantises to +-127 in every token; a channel with one
+    # non-zero token sums to +-127; all-zero channels sum to 0
+    v = np.zeros((1, 2, 30, 16), np.float32)
+    v[0, 0, :, 3] = 2.5
+    v[0, 1, :, 5] = -0.75
+    v[0, 0, 7, 9] = 1.0
+    vq, _ = oracle.quant_v(to_bits(v, F16), F16)
+    cs = oracle.channel_sums(vq)
+    assert cs.shape == (1, 2, 16) and cs.dtype == np.int32
+    assert cs[0, 0, 3] == 127 * 30 and cs[0, 1, 5] == -127 * 30 and cs[0, 0, 9] == 127
+    assert np.count_nonzero(cs) == 3
+    # quantisation is odd-symmetric, so negating V negates every channel sum
+    rv = np.random.default_rng(12).standard_normal((2, 2, 40, 24)).astype(np.float32)
+    pos = oracle.channel_sums(oracle.quant_v(to_bits(rv, BF16), BF16)[0])
+    neg = oracle.channel_sums(oracle.quant_v(to_bits(-rv, BF16), BF16)[0])
+    assert np.array_equal(neg, -pos) and np.any(pos != 0)
+
+
 def test_hand_example_pack_and_quant(oracle_lib):
     g = json.load(open(os.path.join(GOLDEN, "hand_d4.json")))
     q = np.array(g["q"], np.float32)[None, None]
