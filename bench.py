@@ -94,10 +94,19 @@ def cpu_baseline(inp, target_s: float = 12.0):
     t0 = time.perf_counter()
     oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=ob, bh0=0, nbh=nbh, row0=0, nrows=nrows)
     dt = time.perf_counter() - t0
-    ops = 4.0 * nbh * nrows * s.N * s.d
+    reps = 1
+    if nbh == s.B * s.H and nrows == s.N and dt < target_s / 2:
+        # the whole workload is a short sample: repeat it to about target_s
+        reps = max(1, int(target_s / max(dt, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=ob, bh0=0, nbh=nbh, row0=0, nrows=nrows)
+        dt = time.perf_counter() - t0
+    ops = 4.0 * nbh * nrows * s.N * s.d * reps
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS (effective)",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{nbh} head(s) x {nrows} query rows x all {s.N} keys of {s.name} "
+            "sample": f"{nbh} head(s) x {nrows} query rows x all {s.N} keys of {s.name}"
+                      f"{f' (whole workload, {reps} times)' if reps > 1 else ''} "
                       f"(pack + quantise + attention), {dt:.1f} s"}
 
 
@@ -165,8 +174,27 @@ class Workload:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters
 
+    def time_cold(self, fn, calls: int = 12) -> float:
+        """Median ms of single calls of fn, each after a 512 MB device write
+        that evicts L2 and the 256 MB MALL (inputs come from HBM)."""
+        torch = self.torch
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        times = []
+        for i in range(calls):
+            scratch.fill_(i & 0xFF)
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        times = sorted(times[2:])
+        return times[len(times) // 2]
 
-def measure(name: str, steps: int, warmup: int) -> dict:
+
+def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
     import workloads
     torch = __import__("torch")
     w = Workload(name)
@@ -186,12 +214,16 @@ def measure(name: str, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     step_ms = e0.elapsed_time(e1) / steps
-    # the dominant kernel alone
-    attn_ms = w.time(w.attn, iters=max(steps, 20), warmup=3)
+    # the dominant kernel alone: median (and min) of five runs of back-to-back
+    # launches, and the median of single launches with cold caches
+    runs = sorted(w.time(w.attn, iters=max(steps, 20), warmup=3 if i == 0 else 0) for i in range(5))
+    attn_ms = runs[2]
+    attn_cold_ms = w.time_cold(w.attn) if cold else None
     nbytes = algorithmic_bytes(s)
     return {
         "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
-        "attn_ms": attn_ms, "tops": ops / (step_ms * 1e-3) / 1e12,
+        "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms,
+        "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
         "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
     }
@@ -239,7 +271,7 @@ def main() -> int:
     import workloads
     names = list(workloads.WORKLOADS) if args.all else [args.workload]
     for name in names:
-        r = measure(name, args.steps, args.warmup)
+        r = measure(name, args.steps, args.warmup, cold=not args.all)
         s = r["spec"]
         line = {
             "metric": "effective attention TOPS (4*B*H*N^2*d / t_step), step = pack Q/K + quantise V + fused attention",
@@ -250,17 +282,24 @@ def main() -> int:
             "dtype_detail": "Q.K: +-1 signs on fp4 MFMA (exact integer sums); softmax fp32; P.V u8 x int8 -> int32 MFMA",
             "data": "synthetic (seeded N(0,1) activations of the workload's shape)",
             "config": config_of(s),
-            "attn_ms": round(r["attn_ms"], 5), "attn_tops": round(r["attn_tops"], 3),
+            "attn_ms": round(r["attn_ms"], 5), "attn_min_ms": round(r["attn_min_ms"], 5),
+            "attn_tops": round(r["attn_tops"], 3),
             "roofline": {
                 "bound": "mfma", "achieved": round(r["attn_tops"], 3), "peak": INT8_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": round(r["attn_tops"] / INT8_PEAK_TOPS, 4),
                 "traffic": traffic_for(name),
                 "kernel": "attn_fwd_kernel", "ops_per_launch": r["ops"],
-                "note": "int8 tera-ops/s: effective ops 4*B*H*N^2*d per launch / mean launch time (HIP events)",
+                "note": "int8 tera-ops/s: effective ops 4*B*H*N^2*d per launch / launch time (HIP events; "
+                        "median of 5 runs of back-to-back launches)",
             },
             "hbm": {"alg_bytes_per_launch": r["alg_bytes"], "achieved_GBs": round(r["attn_gbs"], 1),
                     "peak_GBs": HBM_PEAK_GBS, "frac": round(r["attn_gbs"] / HBM_PEAK_GBS, 4)},
         }
+        if r["attn_cold_ms"] is not None:
+            c = r["attn_cold_ms"]
+            line["attn_cold"] = {"ms": round(c, 5), "tops": round(r["ops"] / (c * 1e-3) / 1e12, 3),
+                                 "hbm_GBs": round(r["alg_bytes"] / (c * 1e-3) / 1e9, 1),
+                                 "note": "single launches after a 512 MB write that evicts L2 and the MALL"}
         if not args.all and args.secondary:
             r2 = measure(args.secondary, args.steps, args.warmup)
             line["secondary"] = {"config": config_of(r2["spec"]), "value": round(r2["tops"], 3),
