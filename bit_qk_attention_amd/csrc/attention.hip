@@ -157,7 +157,9 @@ struct KeyStage {
   static constexpr int KROW = 32 * NKB;
   static constexpr int NT = BIAS == BIAS_RELPOS ? kTblMax : 4;
   static constexpr int NB = BIAS == BIAS_DENSE_F16 ? kQB * kBC : 8;
+  static constexpr int NKO = BIAS == BIAS_RELPOS ? kBC : 4;
   uint8_t kx[kBC * KROW];  // fp4 K operand
+  int koff[NKO];           // relative position: key part of the table-window index
   uint32_t kraw[256];      // K sign words as loaded, one per thread
   uint16_t bt[NB];         // fp16 dense bias tile: 128 query rows x 64 keys
   float mk[kBC];
@@ -304,6 +306,22 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     dr_lo = wq_lo - rk_hi + gh - 1;
     count = ((wq_hi - rk_lo + gh - 1) - dr_lo + 1) * T2;
   };
+  // Window index of (query, key) = qwin - koff[key]: qwin = (r_i + gh - 1) * T2
+  // + c_i + gw - 1 depends on the query only, koff = (r_j + dr_lo) * T2 + c_j
+  // on the key and the tile's window start dr_lo; -1 marks keys with no grid
+  // position or past N. Written by wave 2 while the tile is staged (plain LDS
+  // stores, visible after the step's barrier).
+  const int qwin = (q_rr + gh - 1) * T2 + q_cc + gw - 1;
+  auto stage_koff = [&](int t, auto bufc) {
+    if (BIAS == BIAS_RELPOS && wave == 2) {
+      int dr_lo, count;
+      tbl_window(t, dr_lo, count);
+      const int j = t * kBC + lane;
+      int ko = -1;
+      if (j >= npre && j < N) ko = ((j - npre) / gw + dr_lo) * T2 + (j - npre) % gw;
+      pick(bufc).koff[lane] = ko;
+    }
+  };
 
   // ---- staging ----
   // Full tiles go global -> LDS with global_load_lds (no registers): V, the
@@ -404,6 +422,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     if (wave == 1)
       __builtin_amdgcn_global_load_lds((gptr_t*)(p.kmu + bh * N + j0 + lane), (lptr_t*)(sb.mk), 4, 0, 0);
     dma_tbl(t, bufc);
+    stage_koff(t, bufc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_global_load_lds((gptr_t*)(p.kbits + (bh * N + j0) * W + kw_src),
                                      (lptr_t*)(sb.kraw + 64 * wave), 4, 0, 0);
@@ -449,6 +468,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     }
     if (with_v) copy_v_checked(t, bufc);
     dma_tbl(t, bufc);
+    stage_koff(t, bufc);
   };
   // s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt not waited for)
   auto wait_vm0 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
@@ -538,28 +558,23 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c0, bv[i]);
     } else if (BIAS == BIAS_RELPOS) {
-      int dr_lo, count;
-      tbl_window(t, dr_lo, count);
-      // local window index = aq - (r_j*T2 + c_j)
-      const int aq = (q_rr + gh - 1 - dr_lo) * T2 + q_cc + gw - 1;
       const float* tb = sb.tbl;
       float bv[16];
       const bool wave_grid = qb * kQB + wave * kQW >= npre;  // no prefix query in this wave
       if (!TAIL && p.relpos_fast && wave_grid && t * kBC >= npre) {
         // 16 keys on one grid row: a contiguous, reversed window
-        const int g0 = jb - npre;
-        const int base = aq - ((g0 / gw) * T2 + g0 % gw);
+        const int base = qwin - sb.koff[jl];
 #pragma unroll
         for (int i = 0; i < 16; ++i) bv[i] = tb[base - i];
       } else {
-        int rj = 0, cj = 0;
-        if (jb >= npre) { rj = (jb - npre) / gw; cj = (jb - npre) % gw; }
+        const int4* kop = reinterpret_cast<const int4*>(sb.koff + jl);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = jb + i;
-          const bool on = q_grid && j >= npre && j < N;
-          bv[i] = on ? tb[aq - (rj * T2 + cj)] : 0.0f;
-          if (j >= npre) { if (++cj == gw) { cj = 0; ++rj; } }
+        for (int r = 0; r < 4; ++r) {
+          const int4 ko = kop[r];
+          const int k4[4] = {ko.x, ko.y, ko.z, ko.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bv[4 * r + e] = (q_grid && k4[e] >= 0) ? tb[qwin - k4[e]] : 0.0f;
         }
       }
 #pragma unroll
