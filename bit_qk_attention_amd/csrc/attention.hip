@@ -65,7 +65,12 @@ constexpr float kLog2_255 = 7.9943534368588578f;
 // Bias variants. Dense rows that allow 16-byte vector access take the
 // specialised paths (fp32: vector loads; fp16: tiles staged in LDS by DMA);
 // any other dense bias takes per-element bounds-checked loads.
-enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3, BIAS_DENSE_ANY = 4 };
+// Relative-position bias: BIAS_RELPOS_ROW when no tokens precede the grid
+// and its width is a multiple of 16 (every run of 16 keys of a full tile
+// lies on one grid row: a contiguous window of the table), else BIAS_RELPOS.
+enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3, BIAS_DENSE_ANY = 4,
+       BIAS_RELPOS_ROW = 5 };
+constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_RELPOS_ROW; }
 
 struct Params {
   const uint32_t* qbits;
@@ -85,7 +90,6 @@ struct Params {
   int out_f16;      // output type: fp16, else bf16
   int v_dma;        // V tiles go global -> LDS directly (16-byte pieces)
   int v_swz_shift;  // 16-byte chunk swizzle of V rows: -1 none, else shift
-  int relpos_fast;  // relative-position rows never wrap inside 16 keys
   int mk_vec;       // key scales of a head start 16-byte aligned (N % 4 == 0)
   void* out;
 };
@@ -155,9 +159,9 @@ struct IntC {
 template <int NKB, int BIAS>
 struct KeyStage {
   static constexpr int KROW = 32 * NKB;
-  static constexpr int NT = BIAS == BIAS_RELPOS ? kTblMax : 4;
+  static constexpr int NT = is_relpos(BIAS) ? kTblMax + 4 : 4;  // [kTblMax]: a 0.0 slot
   static constexpr int NB = BIAS == BIAS_DENSE_F16 ? kQB * kBC : 8;
-  static constexpr int NKO = BIAS == BIAS_RELPOS ? kBC : 4;
+  static constexpr int NKO = is_relpos(BIAS) ? kBC : 4;
   uint8_t kx[kBC * KROW];  // fp4 K operand
   int koff[NKO];           // relative position: key part of the table-window index
   uint32_t kraw[256];      // K sign words as loaded, one per thread
@@ -282,14 +286,14 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const int T2 = 2 * gw - 1;
   int q_rr = 0, q_cc = 0;  // grid row/column of this lane's query
   bool q_grid = false;     // query has a grid position
-  if (BIAS == BIAS_RELPOS && qc >= npre) {
+  if (is_relpos(BIAS) && qc >= npre) {
     q_grid = true;
     q_rr = (qc - npre) / gw;
     q_cc = (qc - npre) % gw;
   }
   // grid rows spanned by this workgroup's queries
   int wq_lo = 0, wq_hi = -1;
-  if (BIAS == BIAS_RELPOS) {
+  if (is_relpos(BIAS)) {
     const int q0 = qb * kQB, q1 = min(qb * kQB + kQB - 1, N - 1);
     if (q1 >= npre) {
       wq_lo = (max(q0, npre) - npre) / gw;
@@ -312,8 +316,13 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   // position or past N. Written by wave 2 while the tile is staged (plain LDS
   // stores, visible after the step's barrier).
   const int qwin = (q_rr + gh - 1) * T2 + q_cc + gw - 1;
+  if (is_relpos(BIAS) && tid == 0) {  // the 0.0 slot of each stage's table window
+    ks0.tbl[kTblMax] = 0.0f;
+    ks1.tbl[kTblMax] = 0.0f;
+    if constexpr (NS1 == 3 || NS2 == 3) ks2.tbl[kTblMax] = 0.0f;
+  }
   auto stage_koff = [&](int t, auto bufc) {
-    if (BIAS == BIAS_RELPOS && wave == 2) {
+    if (is_relpos(BIAS) && wave == 2) {
       int dr_lo, count;
       tbl_window(t, dr_lo, count);
       const int j = t * kBC + lane;
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   // relative-position window rows of tile t (always in bounds of the table)
   auto dma_tbl = [&](int t, auto bufc) {
     KS& sb = pick(bufc);
-    if (BIAS == BIAS_RELPOS) {
+    if (is_relpos(BIAS)) {
       int dr_lo, count;
       tbl_window(t, dr_lo, count);
       const float* src = static_cast<const float*>(p.bias) + (int64_t)h * T2 * (2 * gh - 1) + (int64_t)dr_lo * T2;
@@ -557,11 +566,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c0, bv[i]);
-    } else if (BIAS == BIAS_RELPOS) {
+    } else if (is_relpos(BIAS)) {
       const float* tb = sb.tbl;
       float bv[16];
-      const bool wave_grid = qb * kQB + wave * kQW >= npre;  // no prefix query in this wave
-      if (!TAIL && p.relpos_fast && wave_grid && t * kBC >= npre) {
+      if constexpr (BIAS == BIAS_RELPOS_ROW && !TAIL) {
         // 16 keys on one grid row: a contiguous, reversed window
         const int base = qwin - sb.koff[jl];
 #pragma unroll
@@ -573,8 +581,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
           const int4 ko = kop[r];
           const int k4[4] = {ko.x, ko.y, ko.z, ko.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            bv[4 * r + e] = (q_grid && k4[e] >= 0) ? tb[qwin - k4[e]] : 0.0f;
+          for (int e = 0; e < 4; ++e) bv[4 * r + e] = tb[(q_grid && k4[e] >= 0) ? qwin - k4[e] : kTblMax];
         }
       }
 #pragma unroll
@@ -1019,6 +1026,7 @@ hipError_t launch_bias(const Params& p, int bias, int nblocks, hipStream_t s) {
     case BIAS_DENSE_F32: return launch_t<NKB, NCB, BIAS_DENSE_F32>(p, nblocks, s);
     case BIAS_DENSE_F16: return launch_t<NKB, NCB, BIAS_DENSE_F16>(p, nblocks, s);
     case BIAS_DENSE_ANY: return launch_t<NKB, NCB, BIAS_DENSE_ANY>(p, nblocks, s);
+    case BIAS_RELPOS_ROW: return launch_t<NKB, NCB, BIAS_RELPOS_ROW>(p, nblocks, s);
     default: return launch_t<NKB, NCB, BIAS_RELPOS>(p, nblocks, s);
   }
 }
@@ -1045,7 +1053,6 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 
   int bias = BIAS_NONE;
   p.bias_f16 = 0;
-  p.relpos_fast = 0;
   if (a.bias_kind == BA_BIAS_DENSE) {
     const int per16 = a.bias_dtype == BA_F32 ? 4 : 8;  // elements per 16 bytes
     const bool vec = (a.N % per16 == 0) && (a.bias_bstride % per16 == 0) &&
@@ -1053,8 +1060,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     p.bias_f16 = a.bias_dtype == BA_F16;
     bias = !vec ? BIAS_DENSE_ANY : (a.bias_dtype == BA_F32 ? BIAS_DENSE_F32 : BIAS_DENSE_F16);
   } else if (a.bias_kind == BA_BIAS_RELPOS) {
-    bias = BIAS_RELPOS;
-    p.relpos_fast = (a.grid_w % 16 == 0) && (a.n_prefix % 16 == 0);
+    bias = (a.grid_w % 16 == 0 && a.n_prefix == 0) ? BIAS_RELPOS_ROW : BIAS_RELPOS;
   }
   const int64_t nblocks = (int64_t)p.nqb * a.B * a.H;
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
