@@ -11,9 +11,9 @@
 // tensor-core MMAs that gfx950 does not have):
 //
 //  * One workgroup = 4 waves = 128 queries of one (batch, head); each wave
-//    owns 32 queries. Keys stream through LDS in tiles of 64, double
-//    buffered: the next tile's global loads are in flight while the current
-//    tile is computed, and there is one barrier per tile.
+//    owns 32 queries. Keys stream through LDS in tiles of 64 over two or
+//    three stages: later tiles' global loads are in flight while the
+//    current tile is computed, and there is one barrier per tile.
 //  * Q.K similarity on the matrix cores: the +-1 sign vectors are encoded as
 //    fp4 (e2m1: +1 = 0x2, -1 = 0xA, 0 = 0x0) and multiplied with
 //    v_mfma_f32_32x32x64_f8f6f4 (fp4 runs at twice the int8 rate). The sums
@@ -50,18 +50,6 @@ constexpr int kQB = kWaves * kQW;  // queries per workgroup
 constexpr int kBC = 64;            // keys per LDS tile (two 32-key MFMA blocks)
 constexpr int kTblMax = 2048;      // floats of relative-position window per tile
 
-// Workgroups per CU the register allocation must allow (4 waves each; 2 ->
-// up to 256 VGPRs per wave, 3 -> 168, 4 -> 128), per instantiation, from
-// measurements on MI355X: without a bias and d <= 64 the extra occupancy
-// wins even though a few values spill outside the key loops; the relative-
-// position gather prefers 3; the dense-bias loads need the registers.
-template <int NCB, int BIAS>
-constexpr int min_blocks() {
-  return BIAS == 0 && NCB <= 2 ? 3 : 2;
-}
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLog2_255 = 7.9943534368588578f;
-
 // Bias variants. Dense rows that allow 16-byte vector access take the
 // specialised paths (fp32: vector loads; fp16: tiles staged in LDS by DMA);
 // any other dense bias takes per-element bounds-checked loads.
@@ -71,6 +59,18 @@ constexpr float kLog2_255 = 7.9943534368588578f;
 enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3, BIAS_DENSE_ANY = 4,
        BIAS_RELPOS_ROW = 5 };
 constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_RELPOS_ROW; }
+
+// Workgroups per CU the register allocation must allow (4 waves each; 2 ->
+// up to 256 VGPRs per wave, 3 -> 168), per instantiation, from measurements
+// on MI355X: without a bias or with a relative-position bias, at d <= 64,
+// the third workgroup wins even where values of the ragged-tile code spill
+// (the key loops stay spill-free); the dense-bias tiles need the LDS.
+template <int NCB, int BIAS>
+constexpr int min_blocks() {
+  return (BIAS == BIAS_NONE || is_relpos(BIAS)) && NCB <= 2 ? 3 : 2;
+}
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2_255 = 7.9943534368588578f;
 
 struct Params {
   const uint32_t* qbits;
