@@ -12,7 +12,7 @@ import torch
 import bit_qk_attention_amd as ba
 import oracle
 from gpu_helpers import GpuRun, to_dev, vmax
-from workloads import BF16, F16, from_bits, make
+from workloads import BF16, F16, from_bits, make, to_bits
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -177,3 +177,27 @@ def test_key_permutation():
     run1 = GpuRun(inp)
     d = (run0.out.float() - run1.out.float()).abs().max().item()
     assert d <= 2e-3 * vmax(inp)
+
+
+# V quantisation over the launch shapes the library chooses between: whole
+# rows per block, channel groups of several or one 16-byte piece (with a
+# shorter last group), heads at the register-resident row limit, and the
+# two-pass column-group kernel beyond it or for d % 8 != 0
+@pytest.mark.parametrize("B,H,N,d", [
+    (1, 1, 1, 8), (2, 3, 5, 72), (1, 2, 1024, 72), (8, 16, 300, 72), (1, 3, 777, 24),
+    (1, 1, 16384, 64), (1, 1, 16385, 64), (2, 1, 4096, 128), (1, 2, 50, 20), (3, 1, 2049, 40)])
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_quant_v_launch_shapes(B, H, N, d, dt):
+    rng = np.random.default_rng(B * 1000003 + H * 1009 + N * 13 + d + dt)
+    v = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    v[..., 0] *= 30.0          # one wide channel
+    if d > 3:
+        v[..., 3] = 0.0        # an all-zero channel
+    bits = to_bits(v, dt)
+    vd = to_dev(bits, dt)
+    vq, vs, vsum = ba.quant_v(vd)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_v(bits, dt)
+    assert np.array_equal(vq.cpu().numpy(), rq)
+    assert np.array_equal(vs.cpu().numpy(), rs)
+    assert np.array_equal(vsum.cpu().numpy(), oracle.channel_sums(rq))
