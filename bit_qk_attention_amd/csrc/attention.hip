@@ -62,12 +62,14 @@ constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_
 
 // Workgroups per CU the register allocation must allow (4 waves each; 2 ->
 // up to 256 VGPRs per wave, 3 -> 168), per instantiation, from measurements
-// on MI355X: without a bias or with a relative-position bias, at d <= 64,
-// the third workgroup wins even where values of the ragged-tile code spill
-// (the key loops stay spill-free); the dense-bias tiles need the LDS.
+// on MI355X: at d <= 64 without a bias, with a relative-position bias or
+// with an fp16 dense bias (staged in LDS), the third workgroup wins even
+// where values of the ragged-tile code spill (the key loops stay spill-
+// free); the fp32 and unaligned dense-bias loads go through registers and
+// keep two.
 template <int NCB, int BIAS>
 constexpr int min_blocks() {
-  return (BIAS == BIAS_NONE || is_relpos(BIAS)) && NCB <= 2 ? 3 : 2;
+  return (BIAS == BIAS_NONE || is_relpos(BIAS) || BIAS == BIAS_DENSE_F16) && NCB <= 2 ? 3 : 2;
 }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.9943534368588578f;

@@ -201,3 +201,15 @@ def test_quant_v_launch_shapes(B, H, N, d, dt):
     assert np.array_equal(vq.cpu().numpy(), rq)
     assert np.array_equal(vs.cpu().numpy(), rs)
     assert np.array_equal(vsum.cpu().numpy(), oracle.channel_sums(rq))
+
+
+# every bias kind at head dims that select the smaller kernel instantiations
+# (one or two 32-channel blocks, one fp4 k-step)
+@pytest.mark.parametrize("name,d", [
+    ("dit_512", 16), ("dit_512", 48), ("dit_512", 64),
+    ("long_4k_rp", 32), ("long_16k_rp", 24), ("deit_tiny", 40), ("deit_small", 32)])
+def test_bias_kinds_small_head_dims(name, d):
+    kw = dict(REDUCED[name])
+    kw["d"] = d
+    run = GpuRun(make(name, **kw))
+    check_out(run, label=f"{name} d={d}")
