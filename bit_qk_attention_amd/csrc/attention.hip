@@ -63,13 +63,17 @@ constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_
 // Workgroups per CU the register allocation must allow (4 waves each; 2 ->
 // up to 256 VGPRs per wave, 3 -> 168), per instantiation, from measurements
 // on MI355X: at d <= 64 without a bias, with a relative-position bias or
-// with an fp16 dense bias (staged in LDS), the third workgroup wins even
-// where values of the ragged-tile code spill (the key loops stay spill-
-// free); the fp32 and unaligned dense-bias loads go through registers and
-// keep two.
+// with an fp16 dense bias (staged in LDS), and at d <= 96 without a bias
+// (with the lean pass-2 tile), the third workgroup wins even where values
+// of the ragged-tile code spill (the key loops stay spill-free); the fp32
+// and unaligned dense-bias loads go through registers, and the fp16 bias
+// tiles of d > 64 do not fit the LDS of three, so those keep two.
 template <int NCB, int BIAS>
 constexpr int min_blocks() {
-  return (BIAS == BIAS_NONE || is_relpos(BIAS) || BIAS == BIAS_DENSE_F16) && NCB <= 2 ? 3 : 2;
+  return ((BIAS == BIAS_NONE || is_relpos(BIAS) || BIAS == BIAS_DENSE_F16) && NCB <= 2) ||
+                 (BIAS == BIAS_NONE && NCB == 3)
+             ? 3
+             : 2;
 }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.9943534368588578f;
@@ -978,9 +982,32 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Lean tile: the two key blocks one after the other, nothing carried
+  // across the barrier. Fewer live registers: with three channel blocks it
+  // lets three workgroups share a CU (with one or two it measures the same
+  // as the interleaved tile, which is kept there).
+  auto pass2_tile_lean = [&](auto tail, int t, auto bufc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u4v a[NKB];
+      k_operand(bufc, kb, a);
+      const v16f sig = qk_mfma(a);
+      float sc[16];
+      scores(tail, BoolC<false>(), t, bufc, kb, sig, sc);
+      const v4i pk = probs(tail, t, kb, sc);
+      v4i vt[NCB];
+      read_vt(bufc, kb, vt);
+      pv_regs(vt, pk);
+    }
+  };
+  constexpr bool LEAN = NCB == 3 && min_blocks<NCB, BIAS>() == 3;
   __syncthreads();  // pass 1 is done with both buffers
-  run_pass(IntC<NS2>(), true, pass2_tile);
-  pv_regs(vt_held, p_held);
+  if constexpr (LEAN) {
+    run_pass(IntC<NS2>(), true, pass2_tile_lean);
+  } else {
+    run_pass(IntC<NS2>(), true, pass2_tile);
+    pv_regs(vt_held, p_held);
+  }
 
   // ================= epilogue =================
   float lrun = (l0 + l1) + (l2 + l3);
