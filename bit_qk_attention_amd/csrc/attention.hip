@@ -71,7 +71,7 @@ constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_
 template <int NCB, int BIAS>
 constexpr int min_blocks() {
   return ((BIAS == BIAS_NONE || is_relpos(BIAS) || BIAS == BIAS_DENSE_F16) && NCB <= 2) ||
-                 (BIAS == BIAS_NONE && NCB == 3)
+                 ((BIAS == BIAS_NONE || BIAS == BIAS_DENSE_F16) && NCB == 3)
              ? 3
              : 2;
 }
@@ -104,7 +104,9 @@ struct Params {
 // 32w + m + 4p at nibble p (0..7); the same channel order is used for the
 // query and the key operand, so the dot product is unchanged.
 __device__ __forceinline__ uint32_t fp4_signs(uint32_t bits, int m) {
-  return ((bits << (3 - m)) & 0x88888888u) | 0x22222222u;
+  // ((bits << (3 - m)) & 0x88888888) | 0x22222222 as one three-input
+  // bitwise op (truth table 0xEA = (a & b) | c) after the shift
+  return __builtin_amdgcn_bitop3_b32(bits << (3 - m), 0x88888888u, 0x22222222u, 0xEA);
 }
 
 // LDS swizzle of the 16-byte fp4 slots of one key row (spreads the lanes
@@ -162,13 +164,13 @@ struct IntC {
 // separate __shared__ objects, one per stage, selected at compile time: the
 // compiler then tells a DMA into one stage from reads of another and does
 // not wait for the prefetch before reading.
-template <int NKB, int BIAS>
+template <int NKB, int BIAS, bool RAWK>
 struct KeyStage {
   static constexpr int KROW = 32 * NKB;
   static constexpr int NT = is_relpos(BIAS) ? kTblMax + 4 : 4;  // [kTblMax]: a 0.0 slot
   static constexpr int NB = BIAS == BIAS_DENSE_F16 ? kQB * kBC : 8;
   static constexpr int NKO = is_relpos(BIAS) ? kBC : 4;
-  uint8_t kx[kBC * KROW];  // fp4 K operand
+  uint8_t kx[RAWK ? 16 : kBC * KROW];  // fp4 K operand (unused when the waves expand raw words)
   int koff[NKO];           // relative position: key part of the table-window index
   uint32_t kraw[256];      // K sign words as loaded, one per thread
   uint16_t bt[NB];         // fp16 dense bias tile: 128 query rows x 64 keys
@@ -184,9 +186,15 @@ struct VStage {
 // Stages per pass: pass 1 cycles through three (loads two tiles ahead);
 // pass 2, which also stages V, through three where the LDS budget of the
 // target occupancy allows, else two (one tile ahead).
+// fp16 dense bias with three channel blocks: the waves expand the raw K
+// words themselves (no fp4 copy in LDS), so that three workgroups fit a CU
+template <int NCB, int BIAS>
+constexpr bool raw_k() {
+  return BIAS == BIAS_DENSE_F16 && NCB == 3;
+}
 template <int NKB, int NCB, int BIAS>
 struct StageCfg {
-  static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS>);
+  static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS>()>);
   static constexpr int VSZ = (int)sizeof(VStage<NCB>);
   static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS>() - 2048;  // less the pass-1 reduction buffer
   static constexpr int NS2 = 3 * KS + 3 * VSZ <= BUDGET ? 3 : 2;
@@ -200,7 +208,9 @@ __device__ __forceinline__ int bswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 template <int NKB, int NCB, int BIAS>
 __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kernel(Params p) {
-  using KS = KeyStage<NKB, BIAS>;
+  constexpr bool RAWK = raw_k<NCB, BIAS>();
+  static_assert(!RAWK || NKB == 2, "raw K words: four per key");
+  using KS = KeyStage<NKB, BIAS, RAWK>;
   using VSt = VStage<NCB>;
   using Cfg = StageCfg<NKB, NCB, BIAS>;
   constexpr int KROW = KS::KROW, VS = VSt::VS;
@@ -385,6 +395,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const int kw_src = kw_key * W + min(kw_w, W - 1);  // word offset within a full tile
   auto expand_k = [&](auto bufc, uint32_t bits) {
     KS& sb = pick(bufc);
+    if constexpr (RAWK) {
+      sb.kraw[tid] = bits;
+      return;
+    }
     uint8_t* dst = sb.kx + kw_key * KROW + kslot<NKB>(kw_key, kw_w) * 16;
     if (NKB == 2) {
       u4v o;
@@ -398,7 +412,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   };
   // this thread's K word of a full tile, DMA'd into the stage (needs the
   // thread's own vmcnt wait only)
-  auto finish_k = [&](auto bufc) { expand_k(bufc, pick(bufc).kraw[tid]); };
+  auto finish_k = [&](auto bufc) {
+    if constexpr (!RAWK) expand_k(bufc, pick(bufc).kraw[tid]);
+  };
   // bounds-checked K word of tile t, loaded and expanded synchronously
   auto stage_k_checked = [&](int t, auto bufc) {
     const int j = t * kBC + kw_key;
@@ -494,9 +510,19 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   auto k_operand = [&](auto bufc, int kb, u4v* a) {
     KS& sb = pick(bufc);
     const int key = kb * 32 + key_of_pos(ql);
+    if constexpr (RAWK) {
+      // the key's four words (kraw[4 key + w]), expanded here
+      const u4v wds = *reinterpret_cast<const u4v*>(sb.kraw + 4 * key);
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk)
-      a[kk] = *reinterpret_cast<const u4v*>(sb.kx + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
+      for (int kk = 0; kk < NKB; ++kk) {
+        const uint32_t x = g ? wds[2 * kk + 1] : wds[2 * kk];
+        a[kk] = (u4v){fp4_signs(x, 0), fp4_signs(x, 1), fp4_signs(x, 2), fp4_signs(x, 3)};
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk)
+        a[kk] = *reinterpret_cast<const u4v*>(sb.kx + key * KROW + kslot<NKB>(key, 2 * kk + g) * 16);
+    }
   };
   auto qk_mfma = [&](const u4v* a) -> v16f {
     v16f s = {};

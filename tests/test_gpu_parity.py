@@ -206,10 +206,26 @@ def test_quant_v_launch_shapes(B, H, N, d, dt):
 # every bias kind at head dims that select the smaller kernel instantiations
 # (one or two 32-channel blocks, one fp4 k-step)
 @pytest.mark.parametrize("name,d", [
-    ("dit_512", 16), ("dit_512", 48), ("dit_512", 64),
+    ("dit_512", 16), ("dit_512", 48), ("dit_512", 64),  # N = 333: unaligned rows
     ("long_4k_rp", 32), ("long_16k_rp", 24), ("deit_tiny", 40), ("deit_small", 32)])
 def test_bias_kinds_small_head_dims(name, d):
     kw = dict(REDUCED[name])
     kw["d"] = d
     run = GpuRun(make(name, **kw))
     check_out(run, label=f"{name} d={d}")
+
+
+# the fp16 dense bias with 16-byte aligned rows (N % 8 == 0), the path the
+# DiT layers take: whole 64-key tiles, a ragged last tile of 8 keys, every
+# instantiation of the channel blocks, a shared and a per-batch bias
+@pytest.mark.parametrize("N,d", [(64, 72), (320, 72), (328, 72), (136, 96), (328, 80), (392, 64),
+                                 (200, 48), (256, 16), (8, 72)])
+def test_dense_f16_aligned_rows(N, d):
+    run = GpuRun(make("dit_512", B=2, H=2, N=N, d=d))
+    check_out(run, label=f"fp16 bias N={N} d={d}")
+
+
+def test_dense_f16_aligned_rows_per_batch():
+    run = GpuRun(make("dit_512", B=3, H=2, N=264, bias_shared=False))
+    assert run.inp.bias_batch_stride == 2 * 264 * 264
+    check_out(run, label="per-batch fp16 bias, aligned rows")
