@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
 
 One step = the whole hot path over one batch of synthetic input already
-resident in HBM: ba_pack_qk (sign bits + scales of Q and K), ba_quant_v
-(channel-wise int8 V) and ba_attention_fwd (fused attention), on one stream.
+resident in HBM: ba_pack_qk_quant_v (sign bits + scales of Q and K and
+channel-wise int8 V, one call: the outputs of ba_pack_qk and ba_quant_v) and
+ba_attention_fwd (fused attention), on one stream.
 The headline value is effective attention throughput 4*B*H*N^2*d / t_step
 (d the real head dim), for the DiT-XL/2 512px layer (B=8, H=16, N=1024,
 d=72, dense fp16 bias shared over the batch); the same figures for the
@@ -151,8 +152,8 @@ class Workload:
 
     def step(self):
         ba = self.ba
-        ba.ba_pack_qk(self.q, self.k, self.qbits, self.qmu, self.kbits, self.kmu, self.stream)
-        ba.ba_quant_v(self.v, self.vq, self.vscale, self.vsum, self.stream)
+        ba.ba_pack_qk_quant_v(self.q, self.k, self.v, self.qbits, self.qmu, self.kbits, self.kmu,
+                              self.vq, self.vscale, self.vsum, self.stream)
         self.attn()
 
     def attn(self):

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.ba_pack_qk.restype = I
         L.ba_quant_v.argtypes = [P, I, I, I, I, I, P, P, P, P]
         L.ba_quant_v.restype = I
+        L.ba_pack_qk_quant_v.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.ba_pack_qk_quant_v.restype = I
         L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
         L.ba_attention_fwd.restype = I
         L.ba_debug_hamming_scores.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
@@ -160,6 +162,15 @@ def ba_quant_v(v, vq, vscale, vsum, stream=None) -> None:
                                           _ptr(vsum), _stream(stream)))
 
 
+def ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream=None) -> None:
+    """ba_pack_qk and ba_quant_v in one call (same outputs, bit for bit)."""
+    _require_gpu(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum)
+    B, H, N, d = q.shape
+    _check("ba_pack_qk_quant_v", lib().ba_pack_qk_quant_v(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu),
+        _ptr(vq), _ptr(vscale), _ptr(vsum), _stream(stream)))
+
+
 def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream=None) -> None:
     """Fused forward; out [B,H,N,d] fp16/bf16 defines the shape and output dtype."""
     _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum, out)
@@ -204,11 +215,26 @@ def quant_v(v, stream=None):
     return vq, vscale, vsum
 
 
-def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
-    """Whole forward pass: pack Q/K, quantise V, fused attention."""
+def prepare(q, k, v, stream=None):
+    """Packed Q/K and quantised V of one forward pass, from one call."""
     torch = _torch()
-    qbits, qmu, kbits, kmu = pack_qk(q, k, stream)
-    vq, vscale, vsum = quant_v(v, stream)
+    B, H, N, d = q.shape
+    W = ba_packed_words(d)
+    qbits = torch.empty((B, H, N, W), dtype=torch.int32, device=q.device)
+    kbits = torch.empty_like(qbits)
+    qmu = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    kmu = torch.empty_like(qmu)
+    vq = torch.empty((B, H, N, d), dtype=torch.int8, device=v.device)
+    vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
+    vsum = torch.empty((B, H, d), dtype=torch.int32, device=v.device)
+    ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream)
+    return qbits, qmu, kbits, kmu, vq, vscale, vsum
+
+
+def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
+    """Whole forward pass: pack Q/K and quantise V (one call), fused attention."""
+    torch = _torch()
+    qbits, qmu, kbits, kmu, vq, vscale, vsum = prepare(q, k, v, stream)
     if out is None:
         out = torch.empty_like(q)
     ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream)

@@ -89,6 +89,32 @@ ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d, int
   return from_hip(launch_quant_v(v, dt, B * H, N, d, vq, vscale, vsum, static_cast<hipStream_t>(stream)));
 }
 
+ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dtype dt, int B, int H,
+                             int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu,
+                             int8_t* vq, float* vscale, int32_t* vsum, void* stream) {
+  if (!q || !k || !v || !qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum) return BA_ERR_INVALID_ARG;
+  ba_status st = check_shape(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qbits, 16) || !aligned(kbits, 16) ||
+      !aligned(vq, 16) || !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(vsum, 4))
+    return BA_ERR_INVALID_ARG;
+  const int64_t ntok = (int64_t)B * H * N;
+  const int64_t W = (d + 31) / 32;
+  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale, of vsum
+  const void* outs[7] = {qbits, qmu, kbits, kmu, vq, vscale, vsum};
+  const int64_t osz[7] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d, nc, nc};
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(outs[i], osz[i], q, ntok * d * 2) || overlap(outs[i], osz[i], k, ntok * d * 2) ||
+        overlap(outs[i], osz[i], v, ntok * d * 2))
+      return BA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
+  }
+  return from_hip(launch_prepass(q, k, v, dt, B * H, N, d, qbits, qmu, kbits, kmu, vq, vscale, vsum,
+                                 static_cast<hipStream_t>(stream)));
+}
+
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,
                            const float* kmu, const int8_t* vq, const float* vscale,
                            const int32_t* vsum, const ba_bias* bias, int B, int H, int N,

@@ -58,6 +58,9 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t nto
                           float* kmu, hipStream_t s);
 hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
                           int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s);
+hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, int nbh, int N, int d,
+                          uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
+                          float* vscale, int32_t* vsum, hipStream_t s);
 hipError_t launch_hamming(const uint32_t* qbits, const uint32_t* kbits, int N,
                           int d, int bh_begin, int bh_count, int row_begin,
                           int row_count, int32_t* sigma, hipStream_t s);

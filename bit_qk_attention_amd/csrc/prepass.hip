@@ -54,26 +54,22 @@ __global__ __launch_bounds__(256) void pack_qk_kernel(
 // |x|. The pieces are combined through LDS: each 32-bit word from its 4
 // chunks, mu from the P partial sums in channel order.
 constexpr int kPackU = 4;
-template <int DT>
-__global__ __launch_bounds__(256) void pack_qk_coop_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
-    int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
-    uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
-  __shared__ uint32_t bits_s[256 * kPackU];
-  __shared__ double sum_s[256 * kPackU];
-  const uint16_t* x = blockIdx.y == 0 ? q : k;
-  uint32_t* bits = blockIdx.y == 0 ? qbits : kbits;
-  float* mu = blockIdx.y == 0 ? qmu : kmu;
+// One block of NT threads packs tokens [blk * TB, blk * TB + TB) of x.
+// bits_s and sum_s hold NT * kPackU entries.
+template <int DT, int NT>
+__device__ __forceinline__ void pack_block(const uint16_t* __restrict__ x, int64_t ntok, int d, int64_t blk,
+                                           uint32_t* __restrict__ bits, float* __restrict__ mu,
+                                           uint32_t* bits_s, double* sum_s) {
   const int P = d >> 3;                  // chunks per token (1..16)
-  const int TB = 256 * kPackU / P;       // whole tokens per block
+  const int TB = NT * kPackU / P;        // whole tokens per block
   const int W = (d + 31) >> 5;
-  const int64_t tok0 = (int64_t)blockIdx.x * TB;
+  const int64_t tok0 = blk * TB;
   const int nchunk = (int)min((int64_t)TB, ntok - tok0) * P;  // valid chunks of this block
   const int i = threadIdx.x;
   u4v raw[kPackU];
 #pragma unroll
   for (int u = 0; u < kPackU; ++u) {
-    const int c = i + 256 * u;
+    const int c = i + NT * u;
     raw[u] = c < nchunk ? *reinterpret_cast<const u4v*>(x + tok0 * d + 8 * c) : (u4v){0u, 0u, 0u, 0u};
   }
 #pragma unroll
@@ -87,12 +83,12 @@ __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
       b8 |= xf < 0.0f ? (1u << e) : 0u;
       s += (double)fabsf(xf);
     }
-    bits_s[i + 256 * u] = b8;
-    sum_s[i + 256 * u] = s;
+    bits_s[i + NT * u] = b8;
+    sum_s[i + NT * u] = s;
   }
   __syncthreads();
   const int ntb = nchunk / P;  // valid tokens of this block
-  for (int j = i; j < ntb * W; j += 256) {
+  for (int j = i; j < ntb * W; j += NT) {
     const int tl = j / W, w = j % W;
     uint32_t word = 0;
 #pragma unroll
@@ -102,11 +98,24 @@ __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
     }
     bits[(tok0 + tl) * W + w] = word;
   }
-  for (int tl = i; tl < ntb; tl += 256) {
+  for (int tl = i; tl < ntb; tl += NT) {
     double acc = 0.0;
     for (int pc = 0; pc < P; ++pc) acc += sum_s[tl * P + pc];
     mu[tok0 + tl] = (float)(acc / (double)d);
   }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void pack_qk_coop_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
+    int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
+    uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
+  __shared__ uint32_t bits_s[256 * kPackU];
+  __shared__ double sum_s[256 * kPackU];
+  if (blockIdx.y == 0)
+    pack_block<DT, 256>(q, ntok, d, blockIdx.x, qbits, qmu, bits_s, sum_s);
+  else
+    pack_block<DT, 256>(k, ntok, d, blockIdx.x, kbits, kmu, bits_s, sum_s);
 }
 
 hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t ntok,
@@ -271,14 +280,15 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
 // the held values are quantised and written as int8, and their channel sums
 // gathered with LDS atomic adds.
 constexpr int kQvRows = 12;  // rows per thread held in registers
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+// head bh by one block of 1024 threads; smem holds 3 * 128 words
 template <int DT>
-__global__ __launch_bounds__(1024) void quant_v_head_kernel(
-    const uint16_t* __restrict__ v, int N, int d, int8_t* __restrict__ vq, float* __restrict__ vscale,
-    int32_t* __restrict__ vsum) {
-  __shared__ uint32_t amax_bits[128];
-  __shared__ float inv_s[128];
-  __shared__ int32_t sum_s[128];
-  const int bh = blockIdx.x;
+__device__ __forceinline__ void quant_head_block(const uint16_t* __restrict__ v, int N, int d, int64_t bh,
+                                                 int8_t* __restrict__ vq, float* __restrict__ vscale,
+                                                 int32_t* __restrict__ vsum, uint32_t* smem) {
+  uint32_t* amax_bits = smem;
+  float* inv_s = reinterpret_cast<float*>(smem + 128);
+  int32_t* sum_s = reinterpret_cast<int32_t*>(smem + 256);
   const int P = d >> 3, R = 1024 / P;
   const int t = threadIdx.x;
   const int piece = t % P, r0 = t / P;
@@ -291,17 +301,23 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
   const uint16_t* vh = v + (int64_t)bh * N * d + 8 * piece;
   int8_t* qh = vq + (int64_t)bh * N * d + 8 * piece;
   u4v x[kQvRows];
-  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k) {
     const int r = r0 + k * R;
     x[k] = (active && r < N) ? *reinterpret_cast<const u4v*>(vh + (int64_t)r * d) : (u4v){0u, 0u, 0u, 0u};
   }
+  // max |v| per channel on the 16-bit patterns: for finite fp16 / bf16
+  // values the magnitude bits (sign cleared) order like |v|, so a packed
+  // 16-bit integer max over the rows gives the pattern of the maximum
+  us2 mb[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16)))));
+    for (int w = 0; w < 4; ++w)
+      mb[w] = __builtin_elementwise_max(mb[w], __builtin_bit_cast(us2, x[k][w] & 0x7FFF7FFFu));
+  float m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = to_f32<DT>(mb[e >> 1][e & 1]);
   if (active) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) atomicMax(&amax_bits[8 * piece + e], __float_as_uint(m[e]));
@@ -341,6 +357,37 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
   if (t < d) vsum[(int64_t)bh * d + t] = sum_s[t];
 }
 
+template <int DT>
+__global__ __launch_bounds__(1024) void quant_v_head_kernel(
+    const uint16_t* __restrict__ v, int N, int d, int8_t* __restrict__ vq, float* __restrict__ vscale,
+    int32_t* __restrict__ vsum) {
+  __shared__ uint32_t smem[3 * 128];
+  quant_head_block<DT>(v, N, d, blockIdx.x, vq, vscale, vsum, smem);
+}
+
+// Pack Q and K and quantise V in one launch (d % 8 == 0, heads that fit the
+// register-resident quantiser): blocks 0 .. nbh-1 quantise one head each
+// (the long-running ones, dispatched first), the rest pack npb blocks of
+// tokens of Q, then npb of K, all with 1024 threads.
+template <int DT>
+__global__ __launch_bounds__(1024) void prepass_fused_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int nbh, int N, int d, int64_t npb, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
+    uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
+    float* __restrict__ vscale, int32_t* __restrict__ vsum) {
+  __shared__ uint32_t bits_s[1024 * kPackU];
+  __shared__ double sum_s[1024 * kPackU];
+  const int64_t ntok = (int64_t)nbh * N;
+  const int64_t b = blockIdx.x;
+  if (b < nbh) {
+    quant_head_block<DT>(v, N, d, b, vq, vscale, vsum, bits_s);
+  } else if (b - nbh < npb) {
+    pack_block<DT, 1024>(q, ntok, d, b - nbh, qbits, qmu, bits_s, sum_s);
+  } else {
+    pack_block<DT, 1024>(k, ntok, d, b - nbh - npb, kbits, kmu, bits_s, sum_s);
+  }
+}
+
 hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
                           int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s) {
   if (d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
@@ -369,6 +416,35 @@ hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
     hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale, vsum);
   else
     hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale, vsum);
+  return hipGetLastError();
+}
+
+bool prepass_fusable(int N, int d) {
+  return d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8));
+}
+
+hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, int nbh, int N, int d,
+                          uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
+                          float* vscale, int32_t* vsum, hipStream_t s) {
+  const int64_t ntok = (int64_t)nbh * N;
+  if (!prepass_fusable(N, d)) {
+    hipError_t e = launch_pack_qk(q, k, dt, ntok, d, qbits, qmu, kbits, kmu, s);
+    if (e != hipSuccess) return e;
+    return launch_quant_v(v, dt, nbh, N, d, vq, vscale, vsum, s);
+  }
+  const int TB = 1024 * kPackU / (d / 8);
+  const int64_t npb = (ntok + TB - 1) / TB;
+  const int64_t nblk = nbh + 2 * npb;
+  if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  if (dt == BA_F16)
+    hipLaunchKernelGGL(prepass_fused_kernel<BA_F16>, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, nbh, N,
+                       d, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
+  else
+    hipLaunchKernelGGL(prepass_fused_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, nbh, N,
+                       d, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
   return hipGetLastError();
 }
 

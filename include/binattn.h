@@ -108,6 +108,18 @@ ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H,
 ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
                      int8_t* vq, float* vscale, int32_t* vsum, void* stream);
 
+/* ba_pack_qk and ba_quant_v in one call, for callers that run both before
+ * ba_attention_fwd (as every forward pass does): the same outputs, bit for
+ * bit, with the same layouts, alignment and error rules as the two calls
+ * (q, k, v all [B,H,N,d] of dt). Where d % 8 == 0 and a head fits the
+ * register-resident V quantiser (N <= 12 * 1024 / (d / 8)) it is a single
+ * launch in which the V heads and the Q/K token blocks run side by side;
+ * otherwise it enqueues the two calls' kernels in turn. No output may
+ * overlap another output or an input. */
+ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dtype dt, int B, int H,
+                             int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu,
+                             int8_t* vq, float* vscale, int32_t* vsum, void* stream);
+
 /* Fused BinaryAttention forward (zh sections 2.1-2.3; nl Methodologie 1-3;
  * it section 2; fr section 2B; pt section 2B-2C), non-causal, self-attention
  * (N queries and N keys per head). For each head and query i:

@@ -23,8 +23,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = ba.header_symbols()
-    assert set(names) == {"ba_packed_words", "ba_pack_qk", "ba_quant_v", "ba_attention_fwd",
-                          "ba_debug_hamming_scores", "ba_status_string"}
+    assert set(names) == {"ba_packed_words", "ba_pack_qk", "ba_quant_v", "ba_pack_qk_quant_v",
+                          "ba_attention_fwd", "ba_debug_hamming_scores", "ba_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -63,6 +63,24 @@ def test_quant_rejections(L):
     assert quant(L, H=0) == INV and quant(L, d=200) == UNS and quant(L, dt=ba.BA_F32) == UNS
     assert quant(L, vq=ctypes.c_void_p(P + 1 * (1 << 32) + 8)) == INV
     assert quant(L, vq=A(0)) == INV  # output aliases the input
+
+
+def prep(L, q=A(0), k=A(1), v=A(2), dt=ba.BA_BF16, B=1, H=1, N=8, d=64, **kw):
+    o = dict(qb=A(3), qm=A(4), kb=A(5), km=A(6), vq=A(7), vs=A(8), vsum=A(9))
+    o.update(kw)
+    return L.ba_pack_qk_quant_v(q, k, v, dt, B, H, N, d, o["qb"], o["qm"], o["kb"], o["km"], o["vq"], o["vs"],
+                                o["vsum"], None)
+
+
+def test_pack_qk_quant_v_rejections(L):
+    assert prep(L, v=None) == INV and prep(L, km=None) == INV and prep(L, vsum=None) == INV
+    assert prep(L, N=0) == INV and prep(L, d=129) == UNS and prep(L, dt=ba.BA_F32) == UNS
+    assert prep(L, N=ba.BA_MAX_TOKENS + 1) == UNS
+    assert prep(L, v=ctypes.c_void_p(P + 2 * (1 << 32) + 8)) == INV   # not 16-byte aligned
+    assert prep(L, vs=ctypes.c_void_p(P + 8 * (1 << 32) + 2)) == INV  # not 4-byte aligned
+    assert prep(L, vq=A(3)) == INV    # outputs overlap (vq on qbits)
+    assert prep(L, vsum=A(2)) == INV  # output aliases the V input
+    assert prep(L, qb=A(1)) == INV    # output aliases the K input
 
 
 def attn(L, bias=None, B=2, H=2, N=16, d=64, out=A(9), out_dt=ba.BA_BF16, **kw):

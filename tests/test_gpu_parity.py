@@ -229,3 +229,28 @@ def test_dense_f16_aligned_rows_per_batch():
     run = GpuRun(make("dit_512", B=3, H=2, N=264, bias_shared=False))
     assert run.inp.bias_batch_stride == 2 * 264 * 264
     check_out(run, label="per-batch fp16 bias, aligned rows")
+
+
+# the one-call pre-pass: bit-identical to ba_pack_qk + ba_quant_v, on the
+# fused single launch (d % 8 == 0, heads within the register-resident
+# quantiser) and on its two-launch fallback (long heads, d % 8 != 0)
+@pytest.mark.parametrize("B,H,N,d,dt", [
+    (8, 16, 1024, 72, BF16), (2, 3, 333, 72, BF16), (1, 1, 1, 8, F16), (3, 2, 197, 64, F16),
+    (1, 2, 2000, 64, BF16), (2, 2, 150, 36, F16), (1, 3, 50, 128, BF16)])
+def test_pack_qk_quant_v_one_call(B, H, N, d, dt):
+    rng = np.random.default_rng(B * 7919 + H * 104729 + N * 31 + d)
+    x = rng.standard_normal((3, B, H, N, d)).astype(np.float32)
+    x[2, ..., 1] = 0.0
+    q, k, v = (to_dev(to_bits(x[i], dt), dt) for i in range(3))
+    got = ba.prepare(q, k, v)
+    ref = ba.pack_qk(q, k) + ba.quant_v(v)
+    torch.cuda.synchronize()
+    for g, r in zip(got, ref):
+        assert torch.equal(g, r)
+    qb, qm = oracle.pack(to_bits(x[0], dt), dt)
+    vq, vs = oracle.quant_v(to_bits(x[2], dt), dt)
+    assert np.array_equal(got[0].cpu().numpy().view(np.uint32), qb)
+    assert np.array_equal(got[1].cpu().numpy(), qm)
+    assert np.array_equal(got[4].cpu().numpy(), vq)
+    assert np.array_equal(got[5].cpu().numpy(), vs)
+    assert np.array_equal(got[6].cpu().numpy(), oracle.channel_sums(vq))
