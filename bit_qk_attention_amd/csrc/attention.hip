@@ -89,6 +89,7 @@ struct Params {
   const void* bias;
   int64_t bias_bstride;
   int grid_h, grid_w, n_prefix;
+  uint32_t gw_magic;  // ceil(2^32 / grid_w) for grid_w >= 2, else 0
   int B, H, N, d, W;
   int nqb;          // query blocks per head
   float inv_sqrt_d;
@@ -121,6 +122,15 @@ __device__ __forceinline__ int kslot(int key, int slot) {
 // that lane group g ends up with the 16 consecutive keys 16g..16g+15.
 __device__ __forceinline__ int key_of_pos(int p) {
   return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3);
+}
+
+// x / gw for 0 <= x < 65536 (every token offset), gw the grid width, by one
+// high multiply with m = ceil(2^32 / gw): x * m / 2^32 = x / gw +
+// x * e / (gw * 2^32) with e = m * gw - 2^32 < gw <= 256, and x * e < 2^24, so
+// the floor is the exact quotient (checked for all x and gw in that range).
+// m == 0 stands for gw == 1.
+__device__ __forceinline__ int div_gw(int x, uint32_t m) {
+  return m ? (int)__umulhi((uint32_t)x, m) : x;
 }
 
 // Value held by the partner lane (lane ^ 32). v_permlane32_swap exchanges
@@ -302,18 +312,19 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const int T2 = 2 * gw - 1;
   int q_rr = 0, q_cc = 0;  // grid row/column of this lane's query
   bool q_grid = false;     // query has a grid position
+  const uint32_t gwm = p.gw_magic;
   if (is_relpos(BIAS) && qc >= npre) {
     q_grid = true;
-    q_rr = (qc - npre) / gw;
-    q_cc = (qc - npre) % gw;
+    q_rr = div_gw(qc - npre, gwm);
+    q_cc = qc - npre - q_rr * gw;
   }
   // grid rows spanned by this workgroup's queries
   int wq_lo = 0, wq_hi = -1;
   if (is_relpos(BIAS)) {
     const int q0 = qb * kQB, q1 = min(qb * kQB + kQB - 1, N - 1);
     if (q1 >= npre) {
-      wq_lo = (max(q0, npre) - npre) / gw;
-      wq_hi = (q1 - npre) / gw;
+      wq_lo = div_gw(max(q0, npre) - npre, gwm);
+      wq_hi = div_gw(q1 - npre, gwm);
     }
   }
   // table rows dr_lo.. of the window tile t needs, and its size in floats
@@ -322,7 +333,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     dr_lo = 0;
     count = 0;
     if (wq_hi < wq_lo || j1 < npre) return;
-    const int rk_lo = (max(j0, npre) - npre) / gw, rk_hi = (j1 - npre) / gw;
+    const int rk_lo = div_gw(max(j0, npre) - npre, gwm), rk_hi = div_gw(j1 - npre, gwm);
     dr_lo = wq_lo - rk_hi + gh - 1;
     count = ((wq_hi - rk_lo + gh - 1) - dr_lo + 1) * T2;
   };
@@ -343,7 +354,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       tbl_window(t, dr_lo, count);
       const int j = t * kBC + lane;
       int ko = -1;
-      if (j >= npre && j < N) ko = ((j - npre) / gw + dr_lo) * T2 + (j - npre) % gw;
+      if (j >= npre && j < N) {
+        const int r = div_gw(j - npre, gwm);
+        ko = (r + dr_lo) * T2 + (j - npre - r * gw);
+      }
       pick(bufc).koff[lane] = ko;
     }
   };
@@ -430,8 +444,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 #pragma unroll
       for (int i = 0; i < kTblMax / 256; ++i) {
         const int x0 = 64 * (wave + 4 * i);
-        if (x0 + lane < count)
-          __builtin_amdgcn_global_load_lds((gptr_t*)(src + x0 + lane), (lptr_t*)(sb.tbl + x0), 4, 0, 0);
+        if (x0 >= count) break;  // uniform: the wave's later rows are past the window
+        // lanes past the window reload its last entry into slots past it
+        // (inside tbl, never read), so no lane is masked off
+        __builtin_amdgcn_global_load_lds((gptr_t*)(src + min(x0 + lane, count - 1)), (lptr_t*)(sb.tbl + x0), 4, 0, 0);
       }
     }
   };
@@ -1094,6 +1110,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.vq = a.vq; p.vscale = a.vscale; p.vsum = a.vsum;
   p.bias = a.bias; p.bias_bstride = a.bias_bstride;
   p.grid_h = a.grid_h; p.grid_w = a.grid_w; p.n_prefix = a.n_prefix;
+  p.gw_magic = a.grid_w >= 2 ? (uint32_t)(((1ull << 32) + (uint64_t)a.grid_w - 1) / (uint64_t)a.grid_w) : 0u;
   p.B = a.B; p.H = a.H; p.N = a.N; p.d = a.d; p.W = (a.d + 31) / 32;
   p.nqb = (a.N + kQB - 1) / kQB;
   p.inv_sqrt_d = (float)(1.0 / sqrt((double)a.d));
