@@ -61,15 +61,18 @@ enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3, B
 constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_RELPOS_ROW; }
 
 // Workgroups per CU the register allocation must allow (4 waves each; 2 ->
-// up to 256 VGPRs per wave, 3 -> 168), per instantiation, from measurements
-// on MI355X: at d <= 64 without a bias, with a relative-position bias or
-// with an fp16 dense bias (staged in LDS), and at d <= 96 without a bias
-// (with the lean pass-2 tile), the third workgroup wins even where values
-// of the ragged-tile code spill (the key loops stay spill-free); the fp32
-// and unaligned dense-bias loads go through registers, and the fp16 bias
-// tiles of d > 64 do not fit the LDS of three, so those keep two.
+// up to 256 VGPRs per wave, 3 -> 168, 4 -> 128), per instantiation, from
+// measurements on MI355X. At d <= 64 without a bias or with the row-run
+// relative-position bias, four (with the lean pass-2 tile) beat three even
+// though some values spill. Three: the general relative-position bias and
+// the fp16 dense bias (staged in LDS) at d <= 64, and d <= 96 without a bias
+// or with the fp16 dense bias (lean tile; with the bias the waves expand raw
+// K words to make room in LDS); the third workgroup wins even where values
+// of the ragged-tile code spill. Two: the fp32 and unaligned dense-bias
+// loads go through registers, and d > 96.
 template <int NCB, int BIAS>
 constexpr int min_blocks() {
+  if ((BIAS == BIAS_NONE || BIAS == BIAS_RELPOS_ROW) && NCB <= 2) return 4;
   return ((BIAS == BIAS_NONE || is_relpos(BIAS) || BIAS == BIAS_DENSE_F16) && NCB <= 2) ||
                  ((BIAS == BIAS_NONE || BIAS == BIAS_DENSE_F16) && NCB == 3)
              ? 3
@@ -1025,9 +1028,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   };
 
   // Lean tile: the two key blocks one after the other, nothing carried
-  // across the barrier. Fewer live registers: with three channel blocks it
-  // lets three workgroups share a CU (with one or two it measures the same
-  // as the interleaved tile, which is kept there).
+  // across the barrier. Fewer live registers: it lets three workgroups share
+  // a CU at three channel blocks and four at one or two (at three
+  // workgroups and one or two blocks it measures the same as the
+  // interleaved tile, which is kept there).
   auto pass2_tile_lean = [&](auto tail, int t, auto bufc) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -1042,7 +1046,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       pv_regs(vt, pk);
     }
   };
-  constexpr bool LEAN = NCB == 3 && min_blocks<NCB, BIAS>() == 3;
+  constexpr bool LEAN = (NCB == 3 && min_blocks<NCB, BIAS>() == 3) || min_blocks<NCB, BIAS>() == 4;
   __syncthreads();  // pass 1 is done with both buffers
   if constexpr (LEAN) {
     run_pass(IntC<NS2>(), true, pass2_tile_lean);
