@@ -136,6 +136,13 @@ __device__ __forceinline__ int div_gw(int x, uint32_t m) {
   return m ? (int)__umulhi((uint32_t)x, m) : x;
 }
 
+// Raw buffer descriptor over [base, base + bytes): stride 0, so an access's
+// offset is a byte offset, and one at or past `bytes` reads zero. Word 3 is
+// the untyped 32-bit data format the gfx9 buffer unit expects.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Value held by the partner lane (lane ^ 32). v_permlane32_swap exchanges
 // the upper half of its first operand with the lower half of its second;
 // with both operands = x, lanes 0-31 find the partner value in the second
@@ -388,8 +395,12 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     return p.v_swz_shift >= 0 ? row * vstride + 16 * ((col >> 4) ^ vswz(row)) + (col & 15)
                               : row * vstride + col;
   };
-  // DMA sources: wave w fills the 1 KB LDS chunks w and w + 4 of the tile
-  int v_src[2];
+  // DMA sources: wave w fills the 1 KB LDS chunks w and w + 4 of the tile.
+  // Every per-tile DMA is a buffer load: a descriptor for this (batch, head)
+  // slice in scalar registers, a per-lane 32-bit byte offset that does not
+  // change from tile to tile, and the tile's offset as a scalar, so the loop
+  // carries no 64-bit address arithmetic.
+  uint32_t v_src[2];
   bool v_on[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -400,6 +411,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   }
   typedef __attribute__((address_space(1))) const void gptr_t;
   typedef __attribute__((address_space(3))) void lptr_t;
+  const auto rs_v = make_rsrc(p.vq + bh * N * d, (uint32_t)N * d);
+  const auto rs_kmu = make_rsrc(p.kmu + bh * N, 4u * N);
+  const auto rs_kbits = make_rsrc(p.kbits + bh * N * W, 4u * N * W);
 
   // K sign words of a tile, spread over all 256 threads: thread tid expands
   // word kw_w of key kw_key (NKB == 2: all four 16-byte fp4 slots of the
@@ -409,7 +423,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const int kw_key = tid >> 2;
   const int kw_w = NKB == 2 ? (tid & 3) : ((tid >> 1) & 1);
   const int kw_half = NKB == 2 ? 0 : (tid & 1);
-  const int kw_src = kw_key * W + min(kw_w, W - 1);  // word offset within a full tile
+  const int kw_src = 4 * (kw_key * W + min(kw_w, W - 1));  // byte offset within a full tile
   auto expand_k = [&](auto bufc, uint32_t bits) {
     KS& sb = pick(bufc);
     if constexpr (RAWK) {
@@ -443,14 +457,16 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     if (is_relpos(BIAS)) {
       int dr_lo, count;
       tbl_window(t, dr_lo, count);
-      const float* src = static_cast<const float*>(p.bias) + (int64_t)h * T2 * (2 * gh - 1) + (int64_t)dr_lo * T2;
+      const auto rs = make_rsrc(static_cast<const float*>(p.bias) + (int64_t)h * T2 * (2 * gh - 1),
+                                4u * T2 * (2 * gh - 1));
 #pragma unroll
       for (int i = 0; i < kTblMax / 256; ++i) {
         const int x0 = 64 * (wave + 4 * i);
         if (x0 >= count) break;  // uniform: the wave's later rows are past the window
         // lanes past the window reload its last entry into slots past it
         // (inside tbl, never read), so no lane is masked off
-        __builtin_amdgcn_global_load_lds((gptr_t*)(src + min(x0 + lane, count - 1)), (lptr_t*)(sb.tbl + x0), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t*)(sb.tbl + x0), 4, 4 * min(x0 + lane, count - 1),
+                                                 4 * dr_lo * T2, 0, 0);
       }
     }
   };
@@ -463,29 +479,30 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     const int j0 = t * kBC;
     if (with_v && p.v_dma) {
       VSt& vb = pick_v(bufc);
-      const int8_t* src = p.vq + (bh * N + j0) * d;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         if (v_on[i])
-          __builtin_amdgcn_global_load_lds((gptr_t*)(src + v_src[i]), (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16, v_src[i],
+                                                   j0 * d, 0, 0);
     }
-    if (wave == 1)
-      __builtin_amdgcn_global_load_lds((gptr_t*)(p.kmu + bh * N + j0 + lane), (lptr_t*)(sb.mk), 4, 0, 0);
+    if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * lane, 4 * j0, 0, 0);
     dma_tbl(t, bufc);
     stage_koff(t, bufc);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_global_load_lds((gptr_t*)(p.kbits + (bh * N + j0) * W + kw_src),
-                                     (lptr_t*)(sb.kraw + 64 * wave), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kbits, (lptr_t*)(sb.kraw + 64 * wave), 4, kw_src, 4 * j0 * W, 0, 0);
     if (BIAS == BIAS_DENSE_F16) {
-      // wave w fills its own 32 query rows, 8 rows (1 KB) per instruction
+      // wave w fills its own 32 query rows, 8 rows (1 KB) per instruction;
+      // the descriptor covers this block's query rows
+      const auto rs = make_rsrc(static_cast<const uint16_t*>(p.bias) + (int64_t)b * p.bias_bstride +
+                                    ((int64_t)h * N + qb * kQB) * N,
+                                2u * N * min(kQB, N - qb * kQB));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wave * kQW + 8 * i + (lane >> 3);
         const int chunk = (lane & 7) ^ bswz(row);
-        const int q = min(qb * kQB + row, N - 1);
-        const uint16_t* src = static_cast<const uint16_t*>(p.bias) + (int64_t)b * p.bias_bstride +
-                              ((int64_t)h * N + q) * N + j0 + 8 * chunk;
-        __builtin_amdgcn_global_load_lds((gptr_t*)src, (lptr_t*)(sb.bt + (wave * kQW + 8 * i) * kBC), 16, 0, 0);
+        const int qr = min(qb * kQB + row, N - 1) - qb * kQB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t*)(sb.bt + (wave * kQW + 8 * i) * kBC), 16,
+                                                 2 * (qr * N + 8 * chunk), 2 * j0, 0, 0);
       }
     }
   };
