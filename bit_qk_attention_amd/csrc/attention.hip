@@ -547,11 +547,11 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     KS& sb = pick(bufc);
     const int key = kb * 32 + key_of_pos(ql);
     if constexpr (RAWK) {
-      // the key's four words (kraw[4 key + w]), expanded here
-      const u4v wds = *reinterpret_cast<const u4v*>(sb.kraw + 4 * key);
+      // the key's words g and g + 2 (kraw[4 key + w]), expanded here
+      const uint32_t* wp = sb.kraw + 4 * key + g;
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) {
-        const uint32_t x = g ? wds[2 * kk + 1] : wds[2 * kk];
+        const uint32_t x = wp[2 * kk];
         a[kk] = (u4v){fp4_signs(x, 0), fp4_signs(x, 1), fp4_signs(x, 2), fp4_signs(x, 3)};
       }
     } else {
@@ -992,6 +992,12 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       vt[cb] = (v4i){lo[0], lo[1], hi[0], hi[1]};
     }
   };
+  // pass-2 u8 probabilities of key block kb
+  auto probs2 = [&](auto tail, int t, auto bufc, int kb, const v16f& sig) -> v4i {
+    float sc[16];
+    scores(tail, BoolC<false>(), t, bufc, kb, sig, sc);
+    return probs(tail, t, kb, sc);
+  };
   // P.V of one key block: acc += V^T (127 - p8)
   auto pv_regs = [&](const v4i* vt, const v4i& bop) {
 #pragma unroll
@@ -1019,9 +1025,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     pv_regs(vt_held, p_held);
     v4i vt0[NCB];
     read_vt(bufc, 0, vt0);
-    float sc[16];
-    scores(tail, BoolC<false>(), t, bufc, 0, sig0, sc);
-    const v4i p0 = probs(tail, t, 0, sc);
+    const v4i p0 = probs2(tail, t, bufc, 0, sig0);
 #pragma unroll
     for (int i = 0; i < NKB + NCB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
@@ -1029,8 +1033,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     }
     __builtin_amdgcn_sched_barrier(0);
     pv_regs(vt0, p0);
-    scores(tail, BoolC<false>(), t, bufc, 1, sig1, sc);
-    p_held = probs(tail, t, 1, sc);
+    p_held = probs2(tail, t, bufc, 1, sig1);
     read_vt(bufc, 1, vt_held);
 #pragma unroll
     for (int i = 0; i < NCB; ++i) {
@@ -1055,9 +1058,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       u4v a[NKB];
       k_operand(bufc, kb, a);
       const v16f sig = qk_mfma(a);
-      float sc[16];
-      scores(tail, BoolC<false>(), t, bufc, kb, sig, sc);
-      const v4i pk = probs(tail, t, kb, sc);
+      const v4i pk = probs2(tail, t, bufc, kb, sig);
       v4i vt[NCB];
       read_vt(bufc, kb, vt);
       pv_regs(vt, pk);
