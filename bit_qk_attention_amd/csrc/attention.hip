@@ -420,8 +420,11 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   // key, one per thread; NKB == 1: two threads share a word, 8 bytes each).
   // Padding words (kw_w >= W) expand whatever was loaded: the query operand
   // is zero in those channels.
+  // With raw words kept (RAWK) slot s of key j holds word s ^ ((j >> 3) & 3),
+  // so that the lanes reading one word of 32 keys hit 32 distinct banks; the
+  // words a wave loads stay those of 16 consecutive keys.
   const int kw_key = tid >> 2;
-  const int kw_w = NKB == 2 ? (tid & 3) : ((tid >> 1) & 1);
+  const int kw_w = RAWK ? ((tid & 3) ^ ((kw_key >> 3) & 3)) : NKB == 2 ? (tid & 3) : ((tid >> 1) & 1);
   const int kw_half = NKB == 2 ? 0 : (tid & 1);
   const int kw_src = 4 * (kw_key * W + min(kw_w, W - 1));  // byte offset within a full tile
   auto expand_k = [&](auto bufc, uint32_t bits) {
@@ -543,15 +546,21 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 
   // fp4 K operand (NKB x 16 bytes per lane) of key block kb of the selected
   // buffer, and the S^T block (32 keys x 32 queries) it gives
+  // stage slots of this lane's words g and g + 2 in key block 0
+  int kraw_at[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int kp = key_of_pos(ql);
+    kraw_at[kk] = 4 * kp + ((2 * kk + g) ^ ((kp >> 3) & 3));
+  }
   auto k_operand = [&](auto bufc, int kb, u4v* a) {
     KS& sb = pick(bufc);
     const int key = kb * 32 + key_of_pos(ql);
     if constexpr (RAWK) {
-      // the key's words g and g + 2 (kraw[4 key + w]), expanded here
-      const uint32_t* wp = sb.kraw + 4 * key + g;
+      // the key's words g and g + 2, expanded here
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) {
-        const uint32_t x = wp[2 * kk];
+        const uint32_t x = sb.kraw[kb * 128 + kraw_at[kk]];
         a[kk] = (u4v){fp4_signs(x, 0), fp4_signs(x, 1), fp4_signs(x, 2), fp4_signs(x, 3)};
       }
     } else {
