@@ -173,6 +173,9 @@ struct BoolC {
 };
 
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 template <int V>
@@ -1090,6 +1093,34 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   uint16_t* outp = static_cast<uint16_t*>(p.out) + (bh * N + qi) * d;
   const float* vs = p.vscale + bh * d;
   const int32_t* vsm = p.vsum + bh * d;
+  if ((d & 3) == 0) {
+    // whole groups of 4 channels: channel parameters at fixed offsets from
+    // this lane's base, two elements per packed 16-bit conversion (rounding
+    // to nearest even, as the scalar conversions); |vsum| <= 127 N < 2^23,
+    // so 127 vsum is a 24-bit multiply
+    const float* vsl = vs + 4 * g;
+    const int32_t* vsml = vsm + 4 * g;
+    uint16_t* outl = outp + 4 * g;
+    auto pack2 = [&](float x0, float x1) -> uint32_t {
+      return p.out_f16 ? __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2h))
+                       : __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2bf));
+    };
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c0l = cb * 32 + 8 * r;  // channels c0l + 4g .. + 3
+        if (c0l + 4 * g < d) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = (float)(__mul24(vsml[c0l + e], 127) - acc[cb][4 * r + e]) * (vsl[c0l + e] * inv_l);
+          *reinterpret_cast<uint2*>(outl + c0l) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -1103,14 +1134,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         const float x = (float)a * vs[ce] * inv_l;
         o[e] = (c + e < d) ? (p.out_f16 ? f32_to_f16(x) : f32_to_bf16(x)) : (uint16_t)0;
       }
-      if (c + 3 < d && (d & 3) == 0) {
-        *reinterpret_cast<uint2*>(outp + c) =
-            make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c + e < d) outp[c + e] = o[e];
-      }
+      for (int e = 0; e < 4; ++e)
+        if (c + e < d) outp[c + e] = o[e];
     }
   }
 }
