@@ -271,35 +271,42 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
   for (int i = threadIdx.x; i < cg; i += blockDim.x) vsum[(int64_t)bh * d + c0 + i] = sum_s[i];
 }
 
-// quant_v for heads that fit in the registers of one 1024-thread block
-// (d % 8 == 0, N <= kQvRows * R): one block per head reads the head once.
-// The head is row-major N x d, so thread t < R*P (P = d/8 16-byte pieces
-// per row, R = 1024/P rows per sweep) owns piece t % P of rows t / P + k*R:
-// every load of the block is one contiguous run of 16*R*P bytes. Channel
-// maxima go through an LDS atomic max on the float bits (non-negative), then
-// the held values are quantised and written as int8, and their channel sums
-// gathered with LDS atomic adds.
+// quant_v for heads that fit in registers (d % 8 == 0): a block of 1024
+// threads quantises HB heads (HB = 1024 / T, T threads per head, a power of
+// two chosen so that no thread holds more than kQvRows rows), reading each
+// head once. A head is row-major N x d, so thread t < R*P of its group
+// (P = d/8 16-byte pieces per row, R = T/P rows per sweep) owns piece t % P
+// of rows t / P + k*R: every load of the group is one contiguous run of
+// 16*R*P bytes. Channel maxima go through an LDS atomic max on the float
+// bits (non-negative), then the held values are quantised and written as
+// int8, and their channel sums gathered with LDS atomic adds.
 constexpr int kQvRows = 12;  // rows per thread held in registers
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-// head bh by one block of 1024 threads; smem holds 3 * 128 words
+// heads bh0 .. bh0 + HB - 1 (those below nbh) by one block of 1024
+// threads; smem holds 3 * 128 words per head
 template <int DT>
-__device__ __forceinline__ void quant_head_block(const uint16_t* __restrict__ v, int N, int d, int64_t bh,
-                                                 int8_t* __restrict__ vq, float* __restrict__ vscale,
-                                                 int32_t* __restrict__ vsum, uint32_t* smem) {
-  uint32_t* amax_bits = smem;
-  float* inv_s = reinterpret_cast<float*>(smem + 128);
-  int32_t* sum_s = reinterpret_cast<int32_t*>(smem + 256);
-  const int P = d >> 3, R = 1024 / P;
-  const int t = threadIdx.x;
+__device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v, int N, int d, int64_t bh0,
+                                                  int64_t nbh, int HB, int8_t* __restrict__ vq,
+                                                  float* __restrict__ vscale, int32_t* __restrict__ vsum,
+                                                  uint32_t* smem) {
+  const int T = 1024 / HB;
+  const int hs = threadIdx.x / T, t = threadIdx.x % T;
+  const int64_t bh = bh0 + hs;
+  const bool hvalid = bh < nbh;
+  uint32_t* amax_bits = smem + 384 * hs;
+  float* inv_s = reinterpret_cast<float*>(amax_bits + 128);
+  int32_t* sum_s = reinterpret_cast<int32_t*>(amax_bits + 256);
+  const int P = d >> 3, R = T / P;
   const int piece = t % P, r0 = t / P;
-  const bool active = r0 < R;
+  const bool active = hvalid && r0 < R;
   if (t < d) {
     amax_bits[t] = 0u;
     sum_s[t] = 0;
   }
   __syncthreads();
-  const uint16_t* vh = v + (int64_t)bh * N * d + 8 * piece;
-  int8_t* qh = vq + (int64_t)bh * N * d + 8 * piece;
+  const int64_t hoff = hvalid ? bh * N * d : 0;
+  const uint16_t* vh = v + hoff + 8 * piece;
+  int8_t* qh = vq + hoff + 8 * piece;
   u4v x[kQvRows];
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k) {
@@ -323,10 +330,10 @@ __device__ __forceinline__ void quant_head_block(const uint16_t* __restrict__ v,
     for (int e = 0; e < 8; ++e) atomicMax(&amax_bits[8 * piece + e], __float_as_uint(m[e]));
   }
   __syncthreads();
-  if (t < d) {
+  if (hvalid && t < d) {
     const float a = __uint_as_float(amax_bits[t]);
     inv_s[t] = a > 0.0f ? 127.0f / a : 0.0f;
-    vscale[(int64_t)bh * d + t] = a / 127.0f;
+    vscale[bh * d + t] = a / 127.0f;
   }
   __syncthreads();
   float inv[8];
@@ -354,37 +361,51 @@ __device__ __forceinline__ void quant_head_block(const uint16_t* __restrict__ v,
     for (int e = 0; e < 8; ++e) atomicAdd(&sum_s[8 * piece + e], csum[e]);
   }
   __syncthreads();
-  if (t < d) vsum[(int64_t)bh * d + t] = sum_s[t];
+  if (hvalid && t < d) vsum[bh * d + t] = sum_s[t];
+}
+
+// Heads per 1024-thread block for the register-resident quantiser: the most
+// (a power of two, at most 8) whose T = 1024 / HB threads per head still
+// hold at most 8 rows each (kQvRows when one head takes the whole block),
+// while leaving at least 64 blocks; with fewer heads than that, one head
+// per block keeps each head's rows spread over all 1024 threads.
+int quant_heads_per_block(int nbh, int N, int d) {
+  const int P = d / 8;
+  for (int hb = 8; hb > 1; hb >>= 1) {
+    const int T = 1024 / hb;
+    if (T >= P && (int64_t)N <= 8 * (int64_t)(T / P) && nbh >= 64 * hb) return hb;
+  }
+  return 1;
 }
 
 template <int DT>
 __global__ __launch_bounds__(1024) void quant_v_head_kernel(
-    const uint16_t* __restrict__ v, int N, int d, int8_t* __restrict__ vq, float* __restrict__ vscale,
-    int32_t* __restrict__ vsum) {
-  __shared__ uint32_t smem[3 * 128];
-  quant_head_block<DT>(v, N, d, blockIdx.x, vq, vscale, vsum, smem);
+    const uint16_t* __restrict__ v, int nbh, int N, int d, int HB, int8_t* __restrict__ vq,
+    float* __restrict__ vscale, int32_t* __restrict__ vsum) {
+  __shared__ uint32_t smem[8 * 3 * 128];
+  quant_heads_block<DT>(v, N, d, (int64_t)blockIdx.x * HB, nbh, HB, vq, vscale, vsum, smem);
 }
 
 // Pack Q and K and quantise V in one launch (d % 8 == 0, heads that fit the
-// register-resident quantiser): blocks 0 .. nbh-1 quantise one head each
+// register-resident quantiser): blocks 0 .. nvb-1 quantise HB heads each
 // (the long-running ones, dispatched first), the rest pack npb blocks of
 // tokens of Q, then npb of K, all with 1024 threads.
 template <int DT>
 __global__ __launch_bounds__(1024) void prepass_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int nbh, int N, int d, int64_t npb, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
-    uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
+    int nbh, int N, int d, int HB, int64_t nvb, int64_t npb, uint32_t* __restrict__ qbits,
+    float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
     float* __restrict__ vscale, int32_t* __restrict__ vsum) {
   __shared__ uint32_t bits_s[1024 * kPackU];
   __shared__ double sum_s[1024 * kPackU];
   const int64_t ntok = (int64_t)nbh * N;
   const int64_t b = blockIdx.x;
-  if (b < nbh) {
-    quant_head_block<DT>(v, N, d, b, vq, vscale, vsum, bits_s);
-  } else if (b - nbh < npb) {
-    pack_block<DT, 1024>(q, ntok, d, b - nbh, qbits, qmu, bits_s, sum_s);
+  if (b < nvb) {
+    quant_heads_block<DT>(v, N, d, b * HB, nbh, HB, vq, vscale, vsum, bits_s);
+  } else if (b - nvb < npb) {
+    pack_block<DT, 1024>(q, ntok, d, b - nvb, qbits, qmu, bits_s, sum_s);
   } else {
-    pack_block<DT, 1024>(k, ntok, d, b - nbh - npb, kbits, kmu, bits_s, sum_s);
+    pack_block<DT, 1024>(k, ntok, d, b - nvb - npb, kbits, kmu, bits_s, sum_s);
   }
 }
 
@@ -392,10 +413,12 @@ hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
                           int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s) {
   if (d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
+    const int HB = quant_heads_per_block(nbh, N, d);
+    const unsigned nvb = (unsigned)((nbh + HB - 1) / HB);
     if (dt == BA_F16)
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale, vsum);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3(nvb), dim3(1024), 0, s, v16, nbh, N, d, HB, vq, vscale, vsum);
     else
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3((unsigned)nbh), dim3(1024), 0, s, v16, N, d, vq, vscale, vsum);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3(nvb), dim3(1024), 0, s, v16, nbh, N, d, HB, vq, vscale, vsum);
     return hipGetLastError();
   }
   // widest channel group (whole rows when possible) that still gives
@@ -434,17 +457,19 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
   }
   const int TB = 1024 * kPackU / (d / 8);
   const int64_t npb = (ntok + TB - 1) / TB;
-  const int64_t nblk = nbh + 2 * npb;
+  const int HB = quant_heads_per_block(nbh, N, d);
+  const int64_t nvb = (nbh + HB - 1) / HB;
+  const int64_t nblk = nvb + 2 * npb;
   if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   if (dt == BA_F16)
     hipLaunchKernelGGL(prepass_fused_kernel<BA_F16>, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, nbh, N,
-                       d, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
+                       d, HB, nvb, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
   else
     hipLaunchKernelGGL(prepass_fused_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, nbh, N,
-                       d, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
+                       d, HB, nvb, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
   return hipGetLastError();
 }
 

@@ -182,10 +182,12 @@ def test_key_permutation():
 # V quantisation over the launch shapes the library chooses between: whole
 # rows per block, channel groups of several or one 16-byte piece (with a
 # shorter last group), heads at the register-resident row limit, and the
-# two-pass column-group kernel beyond it or for d % 8 != 0
+# two-pass column-group kernel beyond it or for d % 8 != 0; many short heads
+# share a block (8, 4 and 2 heads per block, the last block part empty)
 @pytest.mark.parametrize("B,H,N,d", [
     (1, 1, 1, 8), (2, 3, 5, 72), (1, 2, 1024, 72), (8, 16, 300, 72), (1, 3, 777, 24),
-    (1, 1, 16384, 64), (1, 1, 16385, 64), (2, 1, 4096, 128), (1, 2, 50, 20), (3, 1, 2049, 40)])
+    (1, 1, 16384, 64), (1, 1, 16385, 64), (2, 1, 4096, 128), (1, 2, 50, 20), (3, 1, 2049, 40),
+    (5, 103, 77, 64), (3, 97, 200, 72), (1, 131, 250, 128)])
 @pytest.mark.parametrize("dt", [F16, BF16])
 def test_quant_v_launch_shapes(B, H, N, d, dt):
     rng = np.random.default_rng(B * 1000003 + H * 1009 + N * 13 + d + dt)
@@ -236,7 +238,8 @@ def test_dense_f16_aligned_rows_per_batch():
 # quantiser) and on its two-launch fallback (long heads, d % 8 != 0)
 @pytest.mark.parametrize("B,H,N,d,dt", [
     (8, 16, 1024, 72, BF16), (2, 3, 333, 72, BF16), (1, 1, 1, 8, F16), (3, 2, 197, 64, F16),
-    (1, 2, 2000, 64, BF16), (2, 2, 150, 36, F16), (1, 3, 50, 128, BF16)])
+    (1, 2, 2000, 64, BF16), (2, 2, 150, 36, F16), (1, 3, 50, 128, BF16),
+    (5, 103, 77, 64, F16), (3, 97, 200, 72, BF16)])
 def test_pack_qk_quant_v_one_call(B, H, N, d, dt):
     rng = np.random.default_rng(B * 7919 + H * 104729 + N * 31 + d)
     x = rng.standard_normal((3, B, H, N, d)).astype(np.float32)
