@@ -257,3 +257,40 @@ def test_pack_qk_quant_v_one_call(B, H, N, d, dt):
     assert np.array_equal(got[4].cpu().numpy(), vq)
     assert np.array_equal(got[5].cpu().numpy(), vs)
     assert np.array_equal(got[6].cpu().numpy(), oracle.channel_sums(vq))
+
+
+# sign bits and scales of the special 16-bit values, on the cooperative
+# packer (d % 8 == 0: alone and inside the one-call pre-pass) and the
+# per-token one: -0 and +0 give bit 0, -inf bit 1, subnormals and the
+# largest finite values of either sign; an infinite input gives mu = inf
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("d", [64, 72, 20])
+def test_pack_special_values(dt, d):
+    inf, big = (0x7C00, 0x7BFF) if dt == F16 else (0x7F80, 0x7F7F)
+    special = np.array([0x0000, 0x8000, 0x0001, 0x8001, big, 0x8000 | big, 0x3C00, 0xBC00], np.uint16)
+    rng = np.random.default_rng(d * 7 + dt)
+    x = to_bits(rng.standard_normal((2, 3, 50, d)).astype(np.float32), dt)
+    flat = x.reshape(-1)
+    pos = rng.choice(flat.size, size=flat.size // 4, replace=False)
+    flat[pos] = special[rng.integers(0, special.size, pos.size)]
+    x[0, 0, 7, :] = 0x8000                       # a token of -0 only: all bits 0, mu 0
+    x[0, 1, 9, 3] = inf | 0x8000                 # -inf: bit 1, mu inf
+    x[1, 2, 11, d - 1] = inf                     # +inf: bit 0, mu inf
+    q = to_dev(x, dt)
+    k = to_dev(x[:, ::-1].copy(), dt)
+    qb, qm = oracle.pack(x, dt)
+    kb, km = oracle.pack(x[:, ::-1].copy(), dt)
+    got = ba.pack_qk(q, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(got[0].cpu().numpy().view(np.uint32), qb)
+    assert np.array_equal(got[1].cpu().numpy(), qm)
+    assert np.array_equal(got[2].cpu().numpy().view(np.uint32), kb)
+    assert np.array_equal(got[3].cpu().numpy(), km)
+    assert np.isinf(qm[0, 1, 9]) and qm[0, 0, 7] == 0.0
+    if d % 8 == 0:
+        both = ba.prepare(q, k, q)
+        torch.cuda.synchronize()
+        assert np.array_equal(both[0].cpu().numpy().view(np.uint32), qb)
+        assert np.array_equal(both[1].cpu().numpy(), qm)
+        assert np.array_equal(both[2].cpu().numpy().view(np.uint32), kb)
+        assert np.array_equal(both[3].cpu().numpy(), km)
