@@ -85,10 +85,10 @@ def lib():
         L.bao_pack.argtypes = [P, I, I64, I, P, P]
         L.bao_quant_v.argtypes = [P, I, I64, I, I, P, P]
         L.bao_hamming.argtypes = [P, P, I, I, I, I, I, I, P]
-        L.bao_attention.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias),
-                                    I, I, I, I, I, P, P, P, P, P, P]
-        L.bao_attention_fp.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias),
-                                       I, I, I, I, P, P]
+        L.bao_attention_mu.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias), P, P,
+                                       I, I, I, I, I, P, P, P, P, P, P]
+        L.bao_attention_fp_mu.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias), P, P,
+                                          I, I, I, I, P, P]
         L.bao_num_threads.restype = I
         _lib = L
     return _lib
@@ -189,11 +189,24 @@ class AttnResult:
     p8: np.ndarray | None  # uint8 [nbh, nrows, N] quantised probabilities
 
 
+def _mu_arg(mu, shape):
+    """A given scale array float32 [B,H,N] (or None: computed per token)."""
+    if mu is None:
+        return None
+    mu = np.ascontiguousarray(mu, dtype=np.float32)
+    assert mu.shape == shape[:3], (mu.shape, shape)
+    return mu
+
+
 def attention(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
-              nrows=None, out_dtype=None, want_p8=False) -> AttnResult:
-    """Quantised BinaryAttention forward from raw uint16 Q, K, V [B,H,N,d]."""
+              nrows=None, out_dtype=None, want_p8=False, qmu=None, kmu=None) -> AttnResult:
+    """Quantised BinaryAttention forward from raw uint16 Q, K, V [B,H,N,d].
+
+    qmu, kmu: optional given scales float32 [B,H,N] in place of the per-token
+    mean |x| (mu is an input of the attention step, e.g. a per-head scalar)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, H, N, d = q.shape
+    qmu, kmu = _mu_arg(qmu, q.shape), _mu_arg(kmu, q.shape)
     assert k.shape == q.shape and v.shape == q.shape
     nbh = B * H - bh0 if nbh is None else nbh
     nrows = N - row0 if nrows is None else nrows
@@ -205,9 +218,9 @@ def attention(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
     acc = np.empty((nbh, nrows, d), np.int64)
     p8 = np.empty((nbh, nrows, N), np.uint8) if want_p8 else None
     cb, keep = _cbias(bias)
-    rc = lib().bao_attention(_ptr(q), _ptr(k), _ptr(v), dtype, B, H, N, d, ctypes.byref(cb),
-                             bh0, nbh, row0, nrows, out_dtype, _ptr(out), _ptr(bits),
-                             _ptr(m), _ptr(l), _ptr(p8), _ptr(acc))
+    rc = lib().bao_attention_mu(_ptr(q), _ptr(k), _ptr(v), dtype, B, H, N, d, ctypes.byref(cb),
+                                _ptr(qmu), _ptr(kmu), bh0, nbh, row0, nrows, out_dtype, _ptr(out),
+                                _ptr(bits), _ptr(m), _ptr(l), _ptr(p8), _ptr(acc))
     del keep
     if rc == -2:
         raise OverflowError("integer P.V accumulator left int32 range")
@@ -217,17 +230,18 @@ def attention(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
 
 
 def attention_fp(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
-                 nrows=None, want_prob=False):
+                 nrows=None, want_prob=False, qmu=None, kmu=None):
     """Unquantised reference: (out float64 [nbh,nrows,d], prob or None)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, H, N, d = q.shape
+    qmu, kmu = _mu_arg(qmu, q.shape), _mu_arg(kmu, q.shape)
     nbh = B * H - bh0 if nbh is None else nbh
     nrows = N - row0 if nrows is None else nrows
     out = np.empty((nbh, nrows, d), np.float64)
     prob = np.empty((nbh, nrows, N), np.float64) if want_prob else None
     cb, keep = _cbias(bias)
-    rc = lib().bao_attention_fp(_ptr(q), _ptr(k), _ptr(v), dtype, B, H, N, d, ctypes.byref(cb),
-                                bh0, nbh, row0, nrows, _ptr(out), _ptr(prob))
+    rc = lib().bao_attention_fp_mu(_ptr(q), _ptr(k), _ptr(v), dtype, B, H, N, d, ctypes.byref(cb),
+                                   _ptr(qmu), _ptr(kmu), bh0, nbh, row0, nrows, _ptr(out), _ptr(prob))
     del keep
     if rc != 0:
         raise ValueError(f"bao_attention_fp rejected its arguments (rc={rc})")

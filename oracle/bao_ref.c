@@ -258,7 +258,8 @@ typedef struct {
 } head_ws;
 
 static int head_prepare(const uint16_t* k, const uint16_t* v, int dtype,
-                        int64_t bh, int N, int d, int want_v, head_ws* ws) {
+                        int64_t bh, int N, int d, int want_v,
+                        const float* kmu_in, head_ws* ws) {
   const int W = bao_words(d);
   ws->kbits = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)N * W);
   ws->kmu = (float*)malloc(sizeof(float) * (size_t)N);
@@ -266,9 +267,11 @@ static int head_prepare(const uint16_t* k, const uint16_t* v, int dtype,
   ws->vscale = want_v ? (float*)malloc(sizeof(float) * (size_t)d) : NULL;
   if (!ws->kbits || !ws->kmu || (want_v && (!ws->vq || !ws->vscale))) return -1;
   const int64_t base = bh * (int64_t)N * d;
-  for (int j = 0; j < N; ++j)
+  for (int j = 0; j < N; ++j) {
     pack_one(k, dtype, base + (int64_t)j * d, d, ws->kbits + (int64_t)j * W,
              ws->kmu + j);
+    if (kmu_in) ws->kmu[j] = kmu_in[bh * N + j];  /* a given key scale */
+  }
   if (want_v) quant_head(v, dtype, base, N, d, ws->vq, ws->vscale);
   return 0;
 }
@@ -283,11 +286,12 @@ static void head_release(head_ws* ws) {
  * (p8 = rne(255 p~)), V is the channel-wise int8 above, P.V is summed in
  * integers and dequantised: O_ic = A_ic * scale_c / (255 * l_i).
  * Reading: l is the float sum of the unquantised p~. */
-int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  int dtype, int B, int H, int N, int d, const bao_bias* bias,
-                  int bh0, int nbh, int row0, int nrows, int out_dtype,
-                  double* out_f64, uint16_t* out_bits, double* row_m,
-                  double* row_l, uint8_t* p8, int64_t* acc) {
+int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int dtype, int B, int H, int N, int d, const bao_bias* bias,
+                     const float* qmu_in, const float* kmu_in,
+                     int bh0, int nbh, int row0, int nrows, int out_dtype,
+                     double* out_f64, uint16_t* out_bits, double* row_m,
+                     double* row_l, uint8_t* p8, int64_t* acc) {
   if (check_args(dtype, B, H, N, d, bias, bh0, nbh, row0, nrows)) return -1;
   if (out_dtype != BAO_F16 && out_dtype != BAO_BF16) return -1;
   const int W = bao_words(d);
@@ -296,7 +300,7 @@ int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     const int64_t bh = bh0 + hh;
     const int b = (int)(bh / H), h = (int)(bh % H);
     head_ws ws;
-    if (head_prepare(k, v, dtype, bh, N, d, 1, &ws)) { head_release(&ws); return -1; }
+    if (head_prepare(k, v, dtype, bh, N, d, 1, kmu_in, &ws)) { head_release(&ws); return -1; }
 #pragma omp parallel
     {
       double* s = (double*)malloc(sizeof(double) * (size_t)N);
@@ -309,6 +313,7 @@ int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       for (int r = 0; r < nrows; ++r) {
         const int i = row0 + r;
         pack_one(q, dtype, (bh * N + i) * (int64_t)d, d, qb, &qmu);
+        if (qmu_in) qmu = qmu_in[bh * N + i];  /* a given query scale */
         score_row(qb, qmu, ws.kbits, ws.kmu, W, N, d, bias, b, h, i, s);
         double m, l;
         softmax_row(s, N, pt, &m, &l);
@@ -349,17 +354,18 @@ int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /* Unquantised reference (no P or V quantisation): O_ic = sum_j p~_ij v_jc / l_i
  * with the same binary scores and bias. */
-int bao_attention_fp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                     int dtype, int B, int H, int N, int d,
-                     const bao_bias* bias, int bh0, int nbh, int row0,
-                     int nrows, double* out_f64, double* prob) {
+int bao_attention_fp_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        int dtype, int B, int H, int N, int d,
+                        const bao_bias* bias, const float* qmu_in,
+                        const float* kmu_in, int bh0, int nbh, int row0,
+                        int nrows, double* out_f64, double* prob) {
   if (check_args(dtype, B, H, N, d, bias, bh0, nbh, row0, nrows)) return -1;
   const int W = bao_words(d);
   for (int hh = 0; hh < nbh; ++hh) {
     const int64_t bh = bh0 + hh;
     const int b = (int)(bh / H), h = (int)(bh % H);
     head_ws ws;
-    if (head_prepare(k, v, dtype, bh, N, d, 0, &ws)) { head_release(&ws); return -1; }
+    if (head_prepare(k, v, dtype, bh, N, d, 0, kmu_in, &ws)) { head_release(&ws); return -1; }
     const int64_t base = bh * (int64_t)N * d;
 #pragma omp parallel
     {
@@ -371,6 +377,7 @@ int bao_attention_fp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       for (int r = 0; r < nrows; ++r) {
         const int i = row0 + r;
         pack_one(q, dtype, (bh * N + i) * (int64_t)d, d, qb, &qmu);
+        if (qmu_in) qmu = qmu_in[bh * N + i];  /* a given query scale */
         score_row(qb, qmu, ws.kbits, ws.kmu, W, N, d, bias, b, h, i, s);
         double m, l;
         softmax_row(s, N, pt, &m, &l);
@@ -389,4 +396,26 @@ int bao_attention_fp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     head_release(&ws);
   }
   return 0;
+}
+
+/* The scales mu are an input of the attention step (zh section 2.2 item 1
+ * calls them learnable; reading R1 computes them per token). These two
+ * forms take them as given arrays [B,H,N] (either may be NULL: then the
+ * per-token mean |x| as in bao_pack), e.g. a per-head scalar. */
+int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  int dtype, int B, int H, int N, int d, const bao_bias* bias,
+                  int bh0, int nbh, int row0, int nrows, int out_dtype,
+                  double* out_f64, uint16_t* out_bits, double* row_m,
+                  double* row_l, uint8_t* p8, int64_t* acc) {
+  return bao_attention_mu(q, k, v, dtype, B, H, N, d, bias, NULL, NULL, bh0, nbh,
+                          row0, nrows, out_dtype, out_f64, out_bits, row_m, row_l,
+                          p8, acc);
+}
+
+int bao_attention_fp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int dtype, int B, int H, int N, int d,
+                     const bao_bias* bias, int bh0, int nbh, int row0,
+                     int nrows, double* out_f64, double* prob) {
+  return bao_attention_fp_mu(q, k, v, dtype, B, H, N, d, bias, NULL, NULL, bh0,
+                             nbh, row0, nrows, out_f64, prob);
 }

@@ -78,6 +78,22 @@ int bao_attention_fp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const bao_bias* bias, int bh0, int nbh, int row0,
                      int nrows, double* out_f64, double* prob);
 
+/* The same two computations with the scales mu given instead of computed:
+ * qmu_in, kmu_in float [B,H,N] (either may be NULL: computed as in
+ * bao_pack). mu is an input of the attention step (a learnable scale in
+ * zh section 2.2 item 1), so e.g. a per-head scalar passes through here. */
+int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int dtype, int B, int H, int N, int d, const bao_bias* bias,
+                     const float* qmu_in, const float* kmu_in,
+                     int bh0, int nbh, int row0, int nrows, int out_dtype,
+                     double* out_f64, uint16_t* out_bits, double* row_m,
+                     double* row_l, uint8_t* p8, int64_t* acc);
+int bao_attention_fp_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        int dtype, int B, int H, int N, int d,
+                        const bao_bias* bias, const float* qmu_in,
+                        const float* kmu_in, int bh0, int nbh, int row0,
+                        int nrows, double* out_f64, double* prob);
+
 /* Number of OpenMP threads the oracle will use. */
 int bao_num_threads(void);
 

@@ -294,3 +294,43 @@ def test_pack_special_values(dt, d):
         assert np.array_equal(both[1].cpu().numpy(), qm)
         assert np.array_equal(both[2].cpu().numpy().view(np.uint32), kb)
         assert np.array_equal(both[3].cpu().numpy(), km)
+
+
+# scales given as inputs (mu is an input of ba_attention_fwd): one scalar per
+# head on each side, the per-token values' head mean, against the oracle
+# with the same scales; and mu = 0, where every score is the bias alone or 0
+@pytest.mark.parametrize("name", ["dit_512", "long_4k", "deit_small"])
+def test_given_mu_per_head(name):
+    inp = make(name, **REDUCED[name])
+    s = inp.spec
+    run = GpuRun(inp)
+    qm = run.qmu.mean(dim=2, keepdim=True).expand_as(run.qmu).contiguous()
+    km = (0.5 * run.kmu.mean(dim=2, keepdim=True)).expand_as(run.kmu).contiguous()
+    out = torch.empty_like(run.out)
+    ba.ba_attention_fwd(run.qbits, qm, run.kbits, km, run.vq, run.vscale, run.vsum, run.lib_bias, out)
+    torch.cuda.synchronize()
+    qm_h, km_h = qm.cpu().numpy(), km.cpu().numpy()
+    ref = oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias, qmu=qm_h, kmu=km_h)
+    fp, _ = oracle.attention_fp(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias, qmu=qm_h, kmu=km_h)
+    got = out.float().cpu().numpy().reshape(s.B * s.H, s.N, s.d)
+    vm = vmax(inp)
+    e_q = np.abs(got - ref.out).max() / vm
+    e_fp = np.abs(got - fp).max() / vm
+    print(f"{name} per-head mu: max|gpu-oracle|/max|V| = {e_q:.2e}, max|gpu-fp|/max|V| = {e_fp:.2e}")
+    assert e_q <= TOL and e_fp <= TOL
+
+
+def test_given_mu_zero_no_bias():
+    inp = make("dit_256", B=2, H=3, N=200)
+    s = inp.spec
+    run = GpuRun(inp)
+    z = torch.zeros_like(run.qmu)
+    out = torch.empty_like(run.out)
+    ba.ba_attention_fwd(run.qbits, z, run.kbits, z, run.vq, run.vscale, run.vsum, None, out)
+    torch.cuda.synchronize()
+    vq, vs = oracle.quant_v(inp.v, s.dtype)
+    mean = vq.astype(np.float64).sum(axis=2) * vs.astype(np.float64) / s.N  # [B,H,d]
+    got = out.float().cpu().numpy()
+    err = np.abs(got - mean[:, :, None, :]).max() / vmax(inp)
+    print(f"mu = 0: max|gpu - mean of dequantised V| / max|V| = {err:.2e}")
+    assert err <= 4e-3  # one 16-bit rounding of the output

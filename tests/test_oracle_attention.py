@@ -349,3 +349,66 @@ def test_rejects_bad_arguments(oracle_lib):
     with pytest.raises(ValueError):
         oracle.attention(x, x, x, F16, bias=Bias(oracle.BIAS_RELPOS, np.zeros((1, 9), np.float32),
                                                  oracle.F32, 0, 2, 3, 0))
+
+
+# ---------------------------------------------------- given scales (mu in) --
+# mu is an input of the attention step (zh §2.2(1): a learnable scale), so the
+# oracle also takes it as given arrays, e.g. one scalar per head.
+
+def test_given_mu_zero_is_uniform_average(oracle_lib):
+    """mu = 0 and no bias: every score is 0, every p~ = 1 and p8 = 255, l = N,
+    so the output is the plain average of the dequantised V rows."""
+    rng = np.random.default_rng(31)
+    B, H, N, d = 2, 3, 45, 40
+    x = rng.standard_normal((3, B, H, N, d)).astype(np.float32)
+    q16, k16, v16 = (to_bits(t, BF16) for t in x)
+    z = np.zeros((B, H, N), np.float32)
+    r = oracle.attention(q16, k16, v16, BF16, qmu=z, kmu=z, want_p8=True)
+    assert (r.p8 == 255).all()
+    assert np.array_equal(r.l, np.full((B * H, N), float(N)))
+    vq, vs = oracle.quant_v(v16, BF16)
+    mean = (vq.astype(np.float64).sum(axis=2) * vs.astype(np.float64) / N).reshape(B * H, 1, d)
+    assert np.allclose(r.out, np.broadcast_to(mean, r.out.shape), rtol=1e-14, atol=0)
+    out_fp, _ = oracle.attention_fp(q16, k16, v16, BF16, qmu=z, kmu=z)
+    want_fp = from_bits(v16, BF16).astype(np.float64).mean(axis=2).reshape(B * H, 1, d)
+    assert np.allclose(out_fp, np.broadcast_to(want_fp, out_fp.shape), rtol=1e-12, atol=1e-15)
+
+
+def test_given_mu_matches_scores_from_numpy(oracle_lib):
+    """One scalar scale per head (query side c_q, key side c_k): the
+    unquantised path is softmax(c_q c_k sign(Q) sign(K)^T / sqrt(d)) V."""
+    rng = np.random.default_rng(32)
+    B, H, N, d = 1, 3, 37, 72
+    x = rng.standard_normal((3, B, H, N, d)).astype(np.float32)
+    q16, k16, v16 = (to_bits(t, F16) for t in x)
+    cq = np.array([0.5, 1.25, 2.0], np.float32)
+    ck = np.array([0.75, 1.5, 0.3], np.float32)
+    qmu = np.broadcast_to(cq[None, :, None], (B, H, N)).copy()
+    kmu = np.broadcast_to(ck[None, :, None], (B, H, N)).copy()
+    out, prob = oracle.attention_fp(q16, k16, v16, F16, qmu=qmu, kmu=kmu, want_prob=True)
+    qs = signs(from_bits(q16, F16).astype(np.float64))
+    ks = signs(from_bits(k16, F16).astype(np.float64))
+    S = (cq.astype(np.float64) * ck.astype(np.float64))[None, :, None, None] * (qs @ np.swapaxes(ks, -1, -2)) / np.sqrt(d)
+    P = softmax(S, axis=-1)
+    O = P @ from_bits(v16, F16).astype(np.float64)
+    assert np.allclose(prob.reshape(P.shape), P, rtol=1e-12, atol=1e-15)
+    assert np.allclose(out.reshape(O.shape), O, rtol=1e-11, atol=1e-12)
+
+
+def test_given_mu_invariances(oracle_lib):
+    """Passing the per-token scales the oracle computes changes nothing, and
+    moving a factor 4 from the key scales to the query scales changes
+    nothing either (the products are exact)."""
+    rng = np.random.default_rng(33)
+    B, H, N, d = 2, 2, 50, 64
+    x = rng.standard_normal((3, B, H, N, d)).astype(np.float32)
+    q16, k16, v16 = (to_bits(t, BF16) for t in x)
+    _, qm = oracle.pack(q16, BF16)
+    _, km = oracle.pack(k16, BF16)
+    r0 = oracle.attention(q16, k16, v16, BF16, want_p8=True)
+    r1 = oracle.attention(q16, k16, v16, BF16, qmu=qm, kmu=km, want_p8=True)
+    r2 = oracle.attention(q16, k16, v16, BF16, qmu=qm * np.float32(4), kmu=km / np.float32(4), want_p8=True)
+    for r in (r1, r2):
+        assert np.array_equal(r.p8, r0.p8)
+        assert np.array_equal(r.acc, r0.acc)
+        assert np.array_equal(r.out_bits, r0.out_bits)
