@@ -376,13 +376,15 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   };
 
   // ---- staging ----
-  // Full tiles go global -> LDS with global_load_lds (no registers): V, the
-  // key scales and the relative-position window rows first, then the K sign
-  // words and the fp16 bias tile, a fixed number of instructions per wave,
-  // so that a wait for all but that last group leaves only the newest tile
-  // in flight. Each thread DMAs one K word and, once its own load has
-  // landed, expands it to the fp4 operand (no barrier between the two). The
-  // ragged last tile is staged synchronously with bounds checks.
+  // Full tiles go global -> LDS by buffer loads with the LDS destination (no
+  // registers): V, the key scales and the relative-position window rows
+  // first, then the K sign words and the fp16 bias tile, a fixed number of
+  // instructions per wave, so that a wait for all but that last group leaves
+  // only the newest tile in flight. Each thread DMAs one K word and, once
+  // its own load has landed, expands it to the fp4 operand (no barrier
+  // between the two); where the raw words are kept, the waves expand them
+  // where they use them. The ragged last tile is staged synchronously with
+  // bounds checks.
   //
   // V layout in LDS (v_dma): row stride d; with v_swz_shift >= 0 the 16-byte
   // chunks of row r are permuted, chunk c stored at c ^ vswz(r), so that the
