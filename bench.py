@@ -1,6 +1,6 @@
 """Benchmark of the BinaryAttention forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all | --block]
 
 One step = the whole hot path over one batch of synthetic input already
 resident in HBM: ba_pack_qk_quant_v (sign bits + scales of Q and K and
@@ -10,7 +10,9 @@ The headline value is effective attention throughput 4*B*H*N^2*d / t_step
 (d the real head dim), for the DiT-XL/2 512px layer (B=8, H=16, N=1024,
 d=72, dense fp16 bias shared over the batch); the same figures for the
 64x64-token long sequence (B=2, H=16, N=4096, d=64) ride along under
-"secondary". Prints one JSON line (rank 0).
+"secondary". Prints one JSON line (rank 0). --block instead times the
+attention block around the kernels (QKV projection on the ROCm BLAS,
+BinaryAttention, output projection) at the 64x64-token shape.
 
 roofline: the fused attention kernel, timed alone with HIP events on the
 stream it runs on: achieved = effective ops per launch / mean launch time,
@@ -230,6 +232,47 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
     }
 
 
+def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64) -> dict:
+    """The attention block (QKV projection -> BinaryAttention -> output
+    projection) at the 64x64-token shape with synthetic bf16 weights: time per
+    block (HIP events, back-to-back blocks) and the attention call alone."""
+    import torch
+    from bit_qk_attention_amd.block import attention_block, split_heads
+    import bit_qk_attention_amd as ba
+    C = H * d
+    g = torch.Generator().manual_seed(1234)
+    bf = torch.bfloat16
+    x = torch.randn(B, N, C, generator=g).to(bf).cuda()
+    w_qkv = (torch.randn(C, 3 * C, generator=g) / C ** 0.5).to(bf).cuda()
+    b_qkv = (0.1 * torch.randn(3 * C, generator=g)).to(bf).cuda()
+    w_out = (torch.randn(C, C, generator=g) / C ** 0.5).to(bf).cuda()
+    b_out = (0.1 * torch.randn(C, generator=g)).to(bf).cuda()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    block_ms = timed(lambda: attention_block(x, w_qkv, b_qkv, w_out, b_out, H))
+    qkv = torch.addmm(b_qkv, x.view(B * N, C), w_qkv).view(B, N, 3 * C)
+    q, k, v = split_heads(qkv, H)
+    attn_ms = timed(lambda: ba.attention(q, k, v))
+    gemm_ms = timed(lambda: torch.addmm(b_qkv, x.view(B * N, C), w_qkv)) + \
+        timed(lambda: torch.addmm(b_out, x.view(B * N, C), w_out))
+    return {"B": B, "N": N, "H": H, "d": d, "C": C, "block_ms": block_ms, "attn_ms": attn_ms,
+            "gemm_ms": gemm_ms, "tokens_per_s": B * N / (block_ms * 1e-3),
+            "attn_ops": 4.0 * B * H * N * N * d, "gemm_flops": 2.0 * B * N * C * 4 * C}
+
+
 def config_of(s) -> dict:
     bias = {"none": "none", "dense_f32": "dense fp32 [H,N,N]", "dense_f16": "dense fp16 [H,N,N]",
             "relpos": f"relative-position table fp32 [H,{(2 * s.grid[0] - 1) * (2 * s.grid[1] - 1)}]"}[s.bias]
@@ -248,6 +291,9 @@ def main() -> int:
     ap.add_argument("--secondary", default="long_4k")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block", action="store_true",
+                    help="only the attention block (QKV projection, BinaryAttention, output "
+                         "projection) at B=2, N=4096, 16 heads of 64, synthetic bf16 weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (read BYTES, write BYTES) five "
                          "times: the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -268,6 +314,20 @@ def main() -> int:
             torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes 4n bytes
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 4 * n}))
+        return 0
+    if args.block:
+        r = measure_block(args.steps, args.warmup)
+        print(json.dumps({
+            "metric": "attention block tokens/s (QKV projection + BinaryAttention + output projection)",
+            "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(r["block_ms"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 GEMMs, int8 attention",
+            "data": "synthetic (seeded N(0,1) activations, N(0,1/C) weights)",
+            "config": {"workload": "attention_block_64x64_tokens", "B": r["B"], "N": r["N"], "H": r["H"],
+                       "d": r["d"], "C": r["C"]},
+            "attn_ms": round(r["attn_ms"], 5), "gemm_ms": round(r["gemm_ms"], 5),
+            "attn_share": round(r["attn_ms"] / r["block_ms"], 3),
+            "gemm_tflops": round(r["gemm_flops"] / (r["gemm_ms"] * 1e-3) / 1e12, 1)}), flush=True)
         return 0
     import workloads
     names = list(workloads.WORKLOADS) if args.all else [args.workload]
