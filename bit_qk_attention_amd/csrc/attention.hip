@@ -652,10 +652,16 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       const float* tb = sb.tbl;
       float bv[16];
       if constexpr (BIAS == BIAS_RELPOS_ROW && !TAIL) {
-        // 16 keys on one grid row: a contiguous, reversed window
-        const int base = qwin - sb.koff[jl];
+        // 16 keys on one grid row: a contiguous, reversed window. Its lowest
+        // entry's address is formed once and kept opaque, so that the 16
+        // reads take small immediate offsets from it (the window's offset
+        // inside the stage would not fit the paired read's offset fields,
+        // and the compiler would add it per pair).
+        typedef __attribute__((address_space(3))) const float lds_f32;
+        lds_f32* lo = (lds_f32*)(tb + (qwin - sb.koff[jl] - 15));
+        asm volatile("" : "+v"(lo));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) bv[i] = tb[base - i];
+        for (int i = 0; i < 16; ++i) bv[i] = lo[15 - i];
       } else {
         const int4* kop = reinterpret_cast<const int4*>(sb.koff + jl);
 #pragma unroll
