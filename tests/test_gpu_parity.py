@@ -334,3 +334,32 @@ def test_given_mu_zero_no_bias():
     err = np.abs(got - mean[:, :, None, :]).max() / vmax(inp)
     print(f"mu = 0: max|gpu - mean of dequantised V| / max|V| = {err:.2e}")
     assert err <= 4e-3  # one 16-bit rounding of the output
+
+
+# a seeded sweep over random shapes, dtypes and bias kinds (every kernel
+# instantiation family: 1-4 channel blocks, one or two fp4 k-steps, dense
+# fp32 / fp16 / per-batch, relative position with and without prefix tokens,
+# grid rows that are and are not multiples of 16)
+def _random_case(i):
+    rng = np.random.default_rng(4242 + i)
+    d = int(rng.integers(1, 129))
+    bias = ["none", "dense_f32", "dense_f16", "relpos"][i % 4]
+    kw = dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), d=d,
+              dtype=[F16, BF16][int(rng.integers(0, 2))], seed=9000 + i, bias=bias)
+    if bias == "relpos":
+        gh = int(rng.integers(2, 12))
+        gw = [16, 32][i % 2] if i % 8 < 4 else int(rng.integers(2, 20))
+        pre = int(rng.integers(0, 2))
+        kw.update(grid=(gh, gw), n_prefix=pre, N=pre + gh * gw)
+    else:
+        kw["N"] = int(rng.integers(1, 300))
+        if bias.startswith("dense"):
+            kw["bias_shared"] = bool(rng.integers(0, 2))
+    return kw
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    kw = _random_case(i)
+    run = GpuRun(make("dit_512", **kw))
+    check_out(run, label=f"random case {i}: {kw}")
