@@ -235,7 +235,8 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
 def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64) -> dict:
     """The attention block (QKV projection -> BinaryAttention -> output
     projection) at the 64x64-token shape with synthetic bf16 weights: time per
-    block (HIP events, back-to-back blocks) and the attention call alone."""
+    block (HIP events, back-to-back blocks), the attention call alone on the
+    block's strided views, and on dense copies of them."""
     import torch
     from bit_qk_attention_amd.block import attention_block, split_heads
     import bit_qk_attention_amd as ba
@@ -264,11 +265,15 @@ def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64) -> dict:
 
     block_ms = timed(lambda: attention_block(x, w_qkv, b_qkv, w_out, b_out, H))
     qkv = torch.addmm(b_qkv, x.view(B * N, C), w_qkv).view(B, N, 3 * C)
-    q, k, v = split_heads(qkv, H)
-    attn_ms = timed(lambda: ba.attention(q, k, v))
+    q, k, v = split_heads(qkv, H)  # strided head views of the projection output
+    o = torch.empty(B, N, H, d, dtype=bf, device=x.device)
+    attn_ms = timed(lambda: ba.attention(q, k, v, out=o.transpose(1, 2)))
+    qc, kc, vc = q.contiguous(), k.contiguous(), v.contiguous()
+    attn_dense_ms = timed(lambda: ba.attention(qc, kc, vc))
     gemm_ms = timed(lambda: torch.addmm(b_qkv, x.view(B * N, C), w_qkv)) + \
         timed(lambda: torch.addmm(b_out, x.view(B * N, C), w_out))
     return {"B": B, "N": N, "H": H, "d": d, "C": C, "block_ms": block_ms, "attn_ms": attn_ms,
+            "attn_dense_inputs_ms": attn_dense_ms,
             "gemm_ms": gemm_ms, "tokens_per_s": B * N / (block_ms * 1e-3),
             "attn_ops": 4.0 * B * H * N * N * d, "gemm_flops": 2.0 * B * N * C * 4 * C}
 
@@ -325,8 +330,8 @@ def main() -> int:
             "data": "synthetic (seeded N(0,1) activations, N(0,1/C) weights)",
             "config": {"workload": "attention_block_64x64_tokens", "B": r["B"], "N": r["N"], "H": r["H"],
                        "d": r["d"], "C": r["C"]},
-            "attn_ms": round(r["attn_ms"], 5), "gemm_ms": round(r["gemm_ms"], 5),
-            "attn_share": round(r["attn_ms"] / r["block_ms"], 3),
+            "attn_ms": round(r["attn_ms"], 5), "attn_dense_inputs_ms": round(r["attn_dense_inputs_ms"], 5),
+            "gemm_ms": round(r["gemm_ms"], 5), "attn_share": round(r["attn_ms"] / r["block_ms"], 3),
             "gemm_tflops": round(r["gemm_flops"] / (r["gemm_ms"] * 1e-3) / 1e12, 1)}), flush=True)
         return 0
     import workloads

@@ -38,6 +38,11 @@ class ba_bias(ctypes.Structure):
                 ("grid_w", ctypes.c_int32), ("n_prefix", ctypes.c_int32)]
 
 
+class ba_strides(ctypes.Structure):
+    """Mirror of the C struct ba_strides (element strides of a [B,H,N,d] view)."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -57,8 +62,14 @@ def lib() -> ctypes.CDLL:
         L.ba_quant_v.restype = I
         L.ba_pack_qk_quant_v.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P]
         L.ba_pack_qk_quant_v.restype = I
+        L.ba_pack_qk_quant_v_strided.argtypes = [P, P, P, ctypes.POINTER(ba_strides), I, I, I, I, I,
+                                                 P, P, P, P, P, P, P, P]
+        L.ba_pack_qk_quant_v_strided.restype = I
         L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
         L.ba_attention_fwd.restype = I
+        L.ba_attention_fwd_strided.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P,
+                                               ctypes.POINTER(ba_strides), I, P]
+        L.ba_attention_fwd_strided.restype = I
         L.ba_debug_hamming_scores.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
         L.ba_debug_hamming_scores.restype = I
         L.ba_status_string.argtypes = [I]
@@ -108,12 +119,20 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _require_gpu(*ts):
+def _require_gpu(*ts, contiguous=True):
     for t in ts:
         if t is not None and not t.is_cuda:
             raise ValueError("libbinattn takes device tensors only (no CPU path)")
-        if t is not None and not t.is_contiguous():
+        if contiguous and t is not None and not t.is_contiguous():
             raise ValueError("libbinattn takes contiguous tensors only")
+
+
+def view_strides(t) -> ba_strides:
+    """(batch, head, token) element strides of a [B,H,N,d] view whose channels
+    are contiguous."""
+    if t.dim() != 4 or (t.shape[-1] > 1 and t.stride(-1) != 1):
+        raise ValueError("a [B,H,N,d] view with contiguous channels is required")
+    return ba_strides(t.stride(0), t.stride(1), t.stride(2))
 
 
 @dataclass
@@ -171,6 +190,20 @@ def ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream
         _ptr(vq), _ptr(vscale), _ptr(vsum), _stream(stream)))
 
 
+def ba_pack_qk_quant_v_strided(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream=None) -> None:
+    """ba_pack_qk_quant_v reading q, k, v through [B,H,N,d] views with one
+    set of strides (e.g. the head slices of a [B,N,3,H,d] projection)."""
+    _require_gpu(q, k, v, contiguous=False)
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum)
+    if not (q.shape == k.shape == v.shape and q.stride() == k.stride() == v.stride()):
+        raise ValueError("q, k and v must be views of one shape and one set of strides")
+    st = view_strides(q)
+    B, H, N, d = q.shape
+    _check("ba_pack_qk_quant_v_strided", lib().ba_pack_qk_quant_v_strided(
+        _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st), _dt(q), B, H, N, d, _ptr(qbits), _ptr(qmu), _ptr(kbits),
+        _ptr(kmu), _ptr(vq), _ptr(vscale), _ptr(vsum), _stream(stream)))
+
+
 def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream=None) -> None:
     """Fused forward; out [B,H,N,d] fp16/bf16 defines the shape and output dtype."""
     _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum, out)
@@ -179,6 +212,19 @@ def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream
     _check("ba_attention_fwd", lib().ba_attention_fwd(
         _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), _ptr(vsum),
         ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
+
+
+def ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream=None) -> None:
+    """ba_attention_fwd writing through ``out``, any [B,H,N,d] view with
+    contiguous channels (e.g. ``o.transpose(1, 2)`` of an o [B,N,H,d])."""
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum)
+    _require_gpu(out, contiguous=False)
+    st = view_strides(out)
+    B, H, N, d = out.shape
+    cb = (bias or Bias()).to_c()
+    _check("ba_attention_fwd_strided", lib().ba_attention_fwd_strided(
+        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), _ptr(vsum),
+        ctypes.byref(cb), B, H, N, d, _ptr(out), ctypes.byref(st), _dt(out), _stream(stream)))
 
 
 def ba_debug_hamming_scores(qbits, kbits, d, bh_begin, bh_count, row_begin, row_count, sigma,
@@ -216,7 +262,8 @@ def quant_v(v, stream=None):
 
 
 def prepare(q, k, v, stream=None):
-    """Packed Q/K and quantised V of one forward pass, from one call."""
+    """Packed Q/K and quantised V of one forward pass, from one call. q, k, v
+    are contiguous [B,H,N,d], or views sharing one set of strides."""
     torch = _torch()
     B, H, N, d = q.shape
     W = ba_packed_words(d)
@@ -227,15 +274,23 @@ def prepare(q, k, v, stream=None):
     vq = torch.empty((B, H, N, d), dtype=torch.int8, device=v.device)
     vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
     vsum = torch.empty((B, H, d), dtype=torch.int32, device=v.device)
-    ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream)
+    if q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
+        ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream)
+    else:
+        ba_pack_qk_quant_v_strided(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream)
     return qbits, qmu, kbits, kmu, vq, vscale, vsum
 
 
 def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
-    """Whole forward pass: pack Q/K and quantise V (one call), fused attention."""
+    """Whole forward pass: pack Q/K and quantise V (one call), fused attention.
+    q, k, v and out may be strided [B,H,N,d] views (see prepare and
+    ba_attention_fwd_strided)."""
     torch = _torch()
     qbits, qmu, kbits, kmu, vq, vscale, vsum = prepare(q, k, v, stream)
     if out is None:
-        out = torch.empty_like(q)
-    ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if out.is_contiguous():
+        ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream)
+    else:
+        ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream)
     return out

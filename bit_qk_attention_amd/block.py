@@ -5,10 +5,12 @@ end-to-end throughput at 1024x1024 input; nl Resultaten, speed and
 efficiency); this block is the part of a transformer layer that the method
 changes, at synthetic weights.
 
-The two projections are plain GEMMs on the ROCm BLAS (``torch.matmul``); the
-head split and merge are layout copies. Everything between them — packing Q
-and K, quantising V, the fused attention — runs in this library's kernels
-through the C ABI.
+The two projections are plain GEMMs on the ROCm BLAS (``torch.addmm``).
+Between them there is no layout copy: the pre-pass reads Q, K and V as
+strided head views of the [B, N, 3, H, d] projection output, and the
+attention writes [B, N, H, d], which the output projection reads as
+[B*N, C]. Packing Q and K, quantising V and the fused attention run in this
+library's kernels through the C ABI.
 """
 from __future__ import annotations
 
@@ -16,17 +18,10 @@ from . import Bias, attention
 
 
 def split_heads(qkv, H: int):
-    """[B, N, 3*H*d] -> three contiguous [B, H, N, d] tensors (q, k, v)."""
+    """[B, N, 3*H*d] -> three [B, H, N, d] views (q, k, v), no copy."""
     B, N, C3 = qkv.shape
-    d = C3 // (3 * H)
-    t = qkv.view(B, N, 3, H, d).permute(2, 0, 3, 1, 4).contiguous()
-    return t[0], t[1], t[2]
-
-
-def merge_heads(o):
-    """[B, H, N, d] -> [B, N, H*d]."""
-    B, H, N, d = o.shape
-    return o.permute(0, 2, 1, 3).reshape(B, N, H * d)
+    t = qkv.view(B, N, 3, H, C3 // (3 * H))
+    return t[:, :, 0].transpose(1, 2), t[:, :, 1].transpose(1, 2), t[:, :, 2].transpose(1, 2)
 
 
 def attention_block(x, w_qkv, b_qkv, w_out, b_out, H: int, bias: Bias | None = None,
@@ -40,7 +35,8 @@ def attention_block(x, w_qkv, b_qkv, w_out, b_out, H: int, bias: Bias | None = N
     B, N, C = x.shape
     qkv = torch.addmm(b_qkv, x.view(B * N, C), w_qkv).view(B, N, 3 * C)
     q, k, v = split_heads(qkv, H)
-    o = attention(q, k, v, bias=bias, stream=stream)
+    o = torch.empty(B, N, H, C // H, dtype=x.dtype, device=x.device)
+    attention(q, k, v, bias=bias, out=o.transpose(1, 2), stream=stream)
     if keep is not None:
-        keep.update(q=q, k=k, v=v, o=o)
-    return torch.addmm(b_out, merge_heads(o).reshape(B * N, C), w_out).view(B, N, C)
+        keep.update(q=q, k=k, v=v, o=o.transpose(1, 2))
+    return torch.addmm(b_out, o.view(B * N, C), w_out).view(B, N, C)

@@ -30,6 +30,122 @@ bool overlap(const void* p, int64_t bytes, const void* q, int64_t qbytes) {
 
 ba_status from_hip(hipError_t e) { return e == hipSuccess ? BA_OK : BA_ERR_HIP; }
 
+// Elements spanned by a [B, H, N, d] view with these strides (first to last
+// element, plus one).
+int64_t view_extent(const ba_strides& st, int B, int H, int N, int d) {
+  return (int64_t)(B - 1) * st.batch + (int64_t)(H - 1) * st.head + (int64_t)(N - 1) * st.token + d;
+}
+
+// Non-negative strides whose view spans at most 2^40 elements (so no
+// offset computed from them overflows).
+bool strides_valid(const ba_strides* st, int B, int H, int N) {
+  if (!st || st->batch < 0 || st->head < 0 || st->token < 0) return false;
+  const int64_t lim = (int64_t)1 << 38;  // per dimension: 4 x 2^38 <= 2^40
+  return st->batch <= lim / (B > 1 ? B - 1 : 1) && st->head <= lim / (H > 1 ? H - 1 : 1) &&
+         st->token <= lim / (N > 1 ? N - 1 : 1);
+}
+
+// No two elements of the view share an address: with the dimensions of size
+// > 1 in increasing stride order (channels first, stride 1), each stride
+// exceeds the span of the dimensions inside it.
+bool view_disjoint(const ba_strides& st, int B, int H, int N, int d) {
+  int64_t dim[4][2] = {{1, d}, {st.token, N}, {st.head, H}, {st.batch, B}};
+  for (int i = 1; i < 4; ++i)  // insertion sort of the outer three by stride
+    for (int j = i; j > 1 && dim[j][0] < dim[j - 1][0]; --j)
+      for (int e = 0; e < 2; ++e) { const int64_t t = dim[j][e]; dim[j][e] = dim[j - 1][e]; dim[j - 1][e] = t; }
+  int64_t span = d;  // elements spanned by the dimensions so far
+  for (int i = 1; i < 4; ++i) {
+    if (dim[i][1] == 1) continue;
+    if (dim[i][0] < span) return false;
+    span += (dim[i][1] - 1) * dim[i][0];
+  }
+  return true;
+}
+
+// ba_pack_qk_quant_v on the view `in` (validated here); in_elems = the
+// elements each of q, k, v spans.
+ba_status prepass_checked(const void* q, const void* k, const void* v, const InView& in, int64_t in_elems,
+                          int in_align, ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
+                          uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, int32_t* vsum, void* stream) {
+  if (!q || !k || !v || !qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum) return BA_ERR_INVALID_ARG;
+  ba_status st = check_shape(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
+  if (!aligned(q, in_align) || !aligned(k, in_align) || !aligned(v, in_align) || !aligned(qbits, 16) ||
+      !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) ||
+      !aligned(vsum, 4))
+    return BA_ERR_INVALID_ARG;
+  const int64_t ntok = (int64_t)B * H * N;
+  const int64_t W = (d + 31) / 32;
+  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale, of vsum
+  const void* outs[7] = {qbits, qmu, kbits, kmu, vq, vscale, vsum};
+  const int64_t osz[7] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d, nc, nc};
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(outs[i], osz[i], q, in_elems * 2) || overlap(outs[i], osz[i], k, in_elems * 2) ||
+        overlap(outs[i], osz[i], v, in_elems * 2))
+      return BA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
+  }
+  return from_hip(launch_prepass(q, k, v, dt, in, B * H, N, d, qbits, qmu, kbits, kmu, vq, vscale, vsum,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint32_t* kbits, const float* kmu,
+                            const int8_t* vq, const float* vscale, const int32_t* vsum, const ba_bias* bias, int B,
+                            int H, int N, int d, void* out, const ba_strides& ost, int out_align, ba_dtype out_dt,
+                            void* stream) {
+  if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum || !out) return BA_ERR_INVALID_ARG;
+  ba_status st = check_shape(B, H, N, d);
+  if (st != BA_OK) return st;
+  if (!dtype16(out_dt)) return BA_ERR_UNSUPPORTED;
+  if (!aligned(qbits, 16) || !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(out, out_align) ||
+      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(vsum, 4))
+    return BA_ERR_INVALID_ARG;
+  const int64_t ntok = (int64_t)B * H * N;
+  const int64_t W = (d + 31) / 32;
+  AttnArgs a = {};
+  a.qbits = qbits; a.qmu = qmu; a.kbits = kbits; a.kmu = kmu; a.vq = vq; a.vscale = vscale;
+  a.vsum = vsum;
+  a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt;
+  a.out_sb = ost.batch; a.out_sh = ost.head; a.out_sn = ost.token;
+  a.bias_kind = BA_BIAS_NONE;
+  int64_t bias_bytes = 0;
+  if (bias && bias->kind != BA_BIAS_NONE) {
+    if (!bias->data) return BA_ERR_INVALID_ARG;
+    if (bias->kind == BA_BIAS_DENSE) {
+      if (bias->dtype != BA_F32 && bias->dtype != BA_F16) return BA_ERR_UNSUPPORTED;
+      const int64_t slice = (int64_t)H * N * N;
+      if (bias->batch_stride != 0 && bias->batch_stride < slice) return BA_ERR_INVALID_ARG;
+      const int esz = bias->dtype == BA_F32 ? 4 : 2;
+      if (!aligned(bias->data, esz)) return BA_ERR_INVALID_ARG;
+      bias_bytes = ((int64_t)(B - 1) * bias->batch_stride + slice) * esz;
+      a.bias_kind = BA_BIAS_DENSE;
+      a.bias_dtype = bias->dtype;
+      a.bias_bstride = bias->batch_stride;
+    } else if (bias->kind == BA_BIAS_RELPOS) {
+      if (bias->dtype != BA_F32) return BA_ERR_UNSUPPORTED;
+      if (bias->grid_h < 1 || bias->grid_w < 1 || bias->n_prefix < 0) return BA_ERR_INVALID_ARG;
+      if (bias->grid_w > 256) return BA_ERR_UNSUPPORTED;  // table window must fit LDS
+      if ((int64_t)bias->n_prefix + (int64_t)bias->grid_h * bias->grid_w != N) return BA_ERR_INVALID_ARG;
+      if (!aligned(bias->data, 4)) return BA_ERR_INVALID_ARG;
+      bias_bytes = (int64_t)H * (2 * bias->grid_h - 1) * (2 * bias->grid_w - 1) * 4;
+      a.bias_kind = BA_BIAS_RELPOS;
+      a.grid_h = bias->grid_h; a.grid_w = bias->grid_w; a.n_prefix = bias->n_prefix;
+    } else {
+      return BA_ERR_INVALID_ARG;
+    }
+    a.bias = bias->data;
+  }
+  const int64_t out_bytes = view_extent(ost, B, H, N, d) * 2;
+  const void* ins[8] = {qbits, qmu, kbits, kmu, vq, vscale, vsum, a.bias};
+  const int64_t isz[8] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
+                          (int64_t)B * H * d * 4, (int64_t)B * H * d * 4, bias_bytes};
+  for (int i = 0; i < 8; ++i)
+    if (overlap(out, out_bytes, ins[i], isz[i])) return BA_ERR_INVALID_ARG;
+  return from_hip(launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -65,7 +181,7 @@ ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H, in
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
   }
-  return from_hip(launch_pack_qk(q, k, dt, ntok, d, qbits, qmu, kbits, kmu,
+  return from_hip(launch_pack_qk(q, k, dt, dense_view(H, N, d), B * H, N, d, qbits, qmu, kbits, kmu,
                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -86,87 +202,58 @@ ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d, int
     for (int j = i + 1; j < 3; ++j)
       if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
   }
-  return from_hip(launch_quant_v(v, dt, B * H, N, d, vq, vscale, vsum, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_quant_v(v, dt, dense_view(H, N, d), B * H, N, d, vq, vscale, vsum,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dtype dt, int B, int H,
                              int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu,
                              int8_t* vq, float* vscale, int32_t* vsum, void* stream) {
-  if (!q || !k || !v || !qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum) return BA_ERR_INVALID_ARG;
+  const ba_status st = check_shape(B, H, N, d);
+  if (st != BA_OK) return st;
+  return prepass_checked(q, k, v, dense_view(H, N, d), (int64_t)B * H * N * d, 16, dt, B, H, N, d, qbits, qmu,
+                         kbits, kmu, vq, vscale, vsum, stream);
+}
+
+ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v, const ba_strides* in_strides,
+                                     ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
+                                     uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, int32_t* vsum,
+                                     void* stream) {
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
-  if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qbits, 16) || !aligned(kbits, 16) ||
-      !aligned(vq, 16) || !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(vsum, 4))
-    return BA_ERR_INVALID_ARG;
-  const int64_t ntok = (int64_t)B * H * N;
-  const int64_t W = (d + 31) / 32;
-  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale, of vsum
-  const void* outs[7] = {qbits, qmu, kbits, kmu, vq, vscale, vsum};
-  const int64_t osz[7] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d, nc, nc};
-  for (int i = 0; i < 7; ++i) {
-    if (overlap(outs[i], osz[i], q, ntok * d * 2) || overlap(outs[i], osz[i], k, ntok * d * 2) ||
-        overlap(outs[i], osz[i], v, ntok * d * 2))
-      return BA_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 7; ++j)
-      if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
-  }
-  return from_hip(launch_prepass(q, k, v, dt, B * H, N, d, qbits, qmu, kbits, kmu, vq, vscale, vsum,
-                                 static_cast<hipStream_t>(stream)));
+  if (!strides_valid(in_strides, B, H, N)) return BA_ERR_INVALID_ARG;
+  InView in;
+  in.sb = in_strides->batch;
+  in.sh = in_strides->head;
+  in.sn = in_strides->token;
+  in.H = H;
+  in.vec = d % 8 == 0 && in.sb % 8 == 0 && in.sh % 8 == 0 && in.sn % 8 == 0 && aligned(q, 16) &&
+           aligned(k, 16) && aligned(v, 16);
+  return prepass_checked(q, k, v, in, view_extent(*in_strides, B, H, N, d), 2, dt, B, H, N, d, qbits, qmu, kbits,
+                         kmu, vq, vscale, vsum, stream);
 }
 
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,
                            const float* kmu, const int8_t* vq, const float* vscale,
                            const int32_t* vsum, const ba_bias* bias, int B, int H, int N,
                            int d, void* out, ba_dtype out_dt, void* stream) {
-  if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum || !out) return BA_ERR_INVALID_ARG;
+  // head and token strides of a dense output (N * d <= 2^23) fit 32 bits
+  const ba_strides dense = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, B, H, N, d, out, dense, 16, out_dt,
+                           stream);
+}
+
+ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,
+                                   const float* kmu, const int8_t* vq, const float* vscale,
+                                   const int32_t* vsum, const ba_bias* bias, int B, int H, int N,
+                                   int d, void* out, const ba_strides* out_strides, ba_dtype out_dt,
+                                   void* stream) {
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
-  if (!dtype16(out_dt)) return BA_ERR_UNSUPPORTED;
-  if (!aligned(qbits, 16) || !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(out, 16) ||
-      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(vsum, 4))
-    return BA_ERR_INVALID_ARG;
-  const int64_t ntok = (int64_t)B * H * N;
-  const int64_t W = (d + 31) / 32;
-  AttnArgs a = {};
-  a.qbits = qbits; a.qmu = qmu; a.kbits = kbits; a.kmu = kmu; a.vq = vq; a.vscale = vscale;
-  a.vsum = vsum;
-  a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt;
-  a.bias_kind = BA_BIAS_NONE;
-  int64_t bias_bytes = 0;
-  if (bias && bias->kind != BA_BIAS_NONE) {
-    if (!bias->data) return BA_ERR_INVALID_ARG;
-    if (bias->kind == BA_BIAS_DENSE) {
-      if (bias->dtype != BA_F32 && bias->dtype != BA_F16) return BA_ERR_UNSUPPORTED;
-      const int64_t slice = (int64_t)H * N * N;
-      if (bias->batch_stride != 0 && bias->batch_stride < slice) return BA_ERR_INVALID_ARG;
-      const int esz = bias->dtype == BA_F32 ? 4 : 2;
-      if (!aligned(bias->data, esz)) return BA_ERR_INVALID_ARG;
-      bias_bytes = ((int64_t)(B - 1) * bias->batch_stride + slice) * esz;
-      a.bias_kind = BA_BIAS_DENSE;
-      a.bias_dtype = bias->dtype;
-      a.bias_bstride = bias->batch_stride;
-    } else if (bias->kind == BA_BIAS_RELPOS) {
-      if (bias->dtype != BA_F32) return BA_ERR_UNSUPPORTED;
-      if (bias->grid_h < 1 || bias->grid_w < 1 || bias->n_prefix < 0) return BA_ERR_INVALID_ARG;
-      if (bias->grid_w > 256) return BA_ERR_UNSUPPORTED;  // table window must fit LDS
-      if ((int64_t)bias->n_prefix + (int64_t)bias->grid_h * bias->grid_w != N) return BA_ERR_INVALID_ARG;
-      if (!aligned(bias->data, 4)) return BA_ERR_INVALID_ARG;
-      bias_bytes = (int64_t)H * (2 * bias->grid_h - 1) * (2 * bias->grid_w - 1) * 4;
-      a.bias_kind = BA_BIAS_RELPOS;
-      a.grid_h = bias->grid_h; a.grid_w = bias->grid_w; a.n_prefix = bias->n_prefix;
-    } else {
-      return BA_ERR_INVALID_ARG;
-    }
-    a.bias = bias->data;
-  }
-  const int64_t out_bytes = ntok * d * 2;
-  const void* ins[8] = {qbits, qmu, kbits, kmu, vq, vscale, vsum, a.bias};
-  const int64_t isz[8] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
-                          (int64_t)B * H * d * 4, (int64_t)B * H * d * 4, bias_bytes};
-  for (int i = 0; i < 8; ++i)
-    if (overlap(out, out_bytes, ins[i], isz[i])) return BA_ERR_INVALID_ARG;
-  return from_hip(launch_attention(a, static_cast<hipStream_t>(stream)));
+  if (!strides_valid(out_strides, B, H, N) || !view_disjoint(*out_strides, B, H, N, d)) return BA_ERR_INVALID_ARG;
+  if (out_strides->head > 0x7FFFFFFF || out_strides->token > 0x7FFFFFFF) return BA_ERR_UNSUPPORTED;
+  return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, B, H, N, d, out, *out_strides, 2,
+                           out_dt, stream);
 }
 
 ba_status ba_debug_hamming_scores(const uint32_t* qbits, const uint32_t* kbits, int B, int H,

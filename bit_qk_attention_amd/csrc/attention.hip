@@ -97,10 +97,13 @@ struct Params {
   int nqb;          // query blocks per head
   float inv_sqrt_d;
   int bias_f16;     // dense bias element type (BIAS_DENSE_ANY): fp16, else fp32
-  int out_f16;      // output type: fp16, else bf16
+  int out_mode;     // bit 0: fp16 output (else bf16); bit 1: 8-byte row stores
+                    // (d and the output strides % 4 == 0, 8-byte aligned base)
   int v_dma;        // V tiles go global -> LDS directly (16-byte pieces)
   int v_swz_shift;  // 16-byte chunk swizzle of V rows: -1 none, else shift
   int mk_vec;       // key scales of a head start 16-byte aligned (N % 4 == 0)
+  int64_t out_sb;              // element strides of the output's [B, H, N, d] view
+  int out_sh, out_sn;
   void* out;
 };
 
@@ -414,7 +417,6 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     const int row = dst / max(d, 1), pc = (dst % max(d, 1)) >> 4;
     v_src[i] = p.v_swz_shift >= 0 ? row * d + 16 * (pc ^ vswz(row)) : dst;
   }
-  typedef __attribute__((address_space(1))) const void gptr_t;
   typedef __attribute__((address_space(3))) void lptr_t;
   const auto rs_v = make_rsrc(p.vq + bh * N * d, (uint32_t)N * d);
   const auto rs_kmu = make_rsrc(p.kmu + bh * N, 4u * N);
@@ -1098,10 +1100,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   lrun += partner32(lrun, lane);
   if (!qvalid) return;
   const float inv_l = 1.0f / lrun;
-  uint16_t* outp = static_cast<uint16_t*>(p.out) + (bh * N + qi) * d;
+  uint16_t* outp = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)h * p.out_sh + (int64_t)qi * p.out_sn;
   const float* vs = p.vscale + bh * d;
   const int32_t* vsm = p.vsum + bh * d;
-  if ((d & 3) == 0) {
+  if (p.out_mode & 2) {
     // whole groups of 4 channels: channel parameters at fixed offsets from
     // this lane's base, two elements per packed 16-bit conversion (rounding
     // to nearest even, as the scalar conversions); |vsum| <= 127 N < 2^23,
@@ -1110,7 +1112,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     const int32_t* vsml = vsm + 4 * g;
     uint16_t* outl = outp + 4 * g;
     auto pack2 = [&](float x0, float x1) -> uint32_t {
-      return p.out_f16 ? __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2h))
+      return (p.out_mode & 1) ? __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2h))
                        : __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2bf));
     };
 #pragma unroll
@@ -1139,8 +1141,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       for (int e = 0; e < 4; ++e) {
         const int ce = min(c + e, d - 1);
         const int a = 127 * vsm[ce] - acc[cb][4 * r + e];  // sum_j p8_j v8_j
-        const float x = (float)a * vs[ce] * inv_l;
-        o[e] = (c + e < d) ? (p.out_f16 ? f32_to_f16(x) : f32_to_bf16(x)) : (uint16_t)0;
+        const float x = (float)a * (vs[ce] * inv_l);      // rounded as on the 8-byte path
+        o[e] = (c + e < d) ? ((p.out_mode & 1) ? f32_to_f16(x) : f32_to_bf16(x)) : (uint16_t)0;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -1185,7 +1187,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.v_swz_shift = -1;
   if (p.v_dma && (a.d == 32 || a.d == 64 || a.d == 128)) p.v_swz_shift = a.d == 32 ? 2 : a.d == 64 ? 1 : 0;
   p.out = a.out;
-  p.out_f16 = a.out_dt == BA_F16;
+  if (a.out_sh > 0x7FFFFFFF || a.out_sn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  p.out_sb = a.out_sb; p.out_sh = (int)a.out_sh; p.out_sn = (int)a.out_sn;
+  const bool out_vec = a.d % 4 == 0 && a.out_sb % 4 == 0 && a.out_sh % 4 == 0 && a.out_sn % 4 == 0 &&
+                       reinterpret_cast<uintptr_t>(a.out) % 8 == 0;
+  p.out_mode = (a.out_dt == BA_F16 ? 1 : 0) | (out_vec ? 2 : 0);
   p.mk_vec = (a.N % 4) == 0 && reinterpret_cast<uintptr_t>(a.kmu) % 16 == 0;
 
   int bias = BIAS_NONE;

@@ -53,13 +53,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 
 // ---- launchers (host side; arguments already validated) -------------------
 
-hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t ntok,
+// Element strides of a [B, H, N, d] view of 16-bit Q, K or V with contiguous
+// channels: token (b, h, n) starts at b*sb + h*sh + n*sn. vec: every token
+// row starts 16-byte aligned (d % 8 == 0, strides % 8 == 0, aligned bases),
+// so the kernels may load whole 16-byte pieces.
+struct InView {
+  int64_t sb, sh, sn;
+  int H;
+  bool vec;
+  bool dense(int N, int d) const { return sn == d && sh == (int64_t)N * d && sb == (int64_t)H * sh; }
+};
+InView dense_view(int H, int N, int d);
+
+hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InView& in, int nbh, int N,
                           int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
                           float* kmu, hipStream_t s);
-hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
+hipError_t launch_quant_v(const void* v, ba_dtype dt, const InView& in, int nbh, int N, int d,
                           int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s);
-hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, int nbh, int N, int d,
-                          uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
+hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, const InView& in, int nbh,
+                          int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
                           float* vscale, int32_t* vsum, hipStream_t s);
 hipError_t launch_hamming(const uint32_t* qbits, const uint32_t* kbits, int N,
                           int d, int bh_begin, int bh_count, int row_begin,
@@ -81,6 +93,7 @@ struct AttnArgs {
   int B, H, N, d;
   void* out;
   int out_dt;
+  int64_t out_sb, out_sh, out_sn;  // element strides of out's [B, H, N, d] view
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

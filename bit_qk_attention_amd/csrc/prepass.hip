@@ -18,16 +18,18 @@ namespace binattn {
 // sets bit c iff x_c < 0, and computes mu = sum|x| / d with a float64 sum
 // (exact for fp16/bf16 inputs of ordinary range) and one float64 division
 // rounded once to float.
-// grid.y selects Q (0) or K (1).
+// grid.y selects Q (0) or K (1). Tokens are read through the view `in`
+// (any strides, 2-byte aligned).
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(256) void pack_qk_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, InView in, int N, int64_t ntok,
     int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
     uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= ntok) return;
-  const uint16_t* x = (blockIdx.y == 0 ? q : k) + t * d;
+  const int64_t bh = t / N, n = t - bh * N;
+  const uint16_t* x = (blockIdx.y == 0 ? q : k) + (bh / in.H) * in.sb + (bh % in.H) * in.sh + n * in.sn;
   uint32_t* bits = (blockIdx.y == 0 ? qbits : kbits);
   float* mu = (blockIdx.y == 0 ? qmu : kmu);
   const int W = (d + 31) >> 5;
@@ -55,22 +57,33 @@ __global__ __launch_bounds__(256) void pack_qk_kernel(
 // chunks, mu from the P partial sums in channel order.
 constexpr int kPackU = 4;
 // One block of NT threads packs tokens [blk * TB, blk * TB + TB) of x.
-// bits_s and sum_s hold NT * kPackU entries.
-template <int DT, int NT>
+// bits_s and sum_s hold NT * kPackU entries. STR: token t of x starts at
+// x + t * sx (sx % 8 == 0) instead of x + t * d, so a block's chunks are
+// runs of P pieces, one run per token.
+template <int DT, int NT, bool STR = false>
 __device__ __forceinline__ void pack_block(const uint16_t* __restrict__ x, int64_t ntok, int d, int64_t blk,
                                            uint32_t* __restrict__ bits, float* __restrict__ mu,
-                                           uint32_t* bits_s, double* sum_s) {
+                                           uint32_t* bits_s, double* sum_s, int64_t sx = 0) {
   const int P = d >> 3;                  // chunks per token (1..16)
   const int TB = NT * kPackU / P;        // whole tokens per block
   const int W = (d + 31) >> 5;
   const int64_t tok0 = blk * TB;
   const int nchunk = (int)min((int64_t)TB, ntok - tok0) * P;  // valid chunks of this block
   const int i = threadIdx.x;
+  // c / P for c < 4096 and P <= 16 as (c * ceil(2^16 / P)) >> 16 (exact there)
+  const uint32_t pmag = STR ? (65536u + P - 1) / P : 0u;
   u4v raw[kPackU];
 #pragma unroll
   for (int u = 0; u < kPackU; ++u) {
     const int c = i + NT * u;
-    raw[u] = c < nchunk ? *reinterpret_cast<const u4v*>(x + tok0 * d + 8 * c) : (u4v){0u, 0u, 0u, 0u};
+    const uint16_t* src;
+    if constexpr (STR) {
+      const int tl = (int)(__umul24((uint32_t)c, pmag) >> 16);
+      src = x + (tok0 + tl) * sx + 8 * (c - tl * P);
+    } else {
+      src = x + tok0 * d + 8 * c;
+    }
+    raw[u] = c < nchunk ? *reinterpret_cast<const u4v*>(src) : (u4v){0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int u = 0; u < kPackU; ++u) {
@@ -105,38 +118,63 @@ __device__ __forceinline__ void pack_block(const uint16_t* __restrict__ x, int64
   }
 }
 
-template <int DT>
+// Dense inputs: the blocks take consecutive runs of the B*H*N tokens. A
+// strided view (STR): nbph blocks per head, each within one head.
+template <int DT, bool STR>
 __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t ntok,
-    int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, InView in, int N, int64_t nbph,
+    int64_t ntok, int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
     uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
   __shared__ uint32_t bits_s[256 * kPackU];
   __shared__ double sum_s[256 * kPackU];
-  if (blockIdx.y == 0)
+  if constexpr (STR) {
+    const bool isk = blockIdx.y != 0;
+    const int64_t bh = blockIdx.x / nbph, tb = blockIdx.x - bh * nbph;
+    const int W = (d + 31) >> 5;
+    pack_block<DT, 256, true>((isk ? k : q) + (bh / in.H) * in.sb + (bh % in.H) * in.sh, N, d, tb,
+                              (isk ? kbits : qbits) + bh * N * W, (isk ? kmu : qmu) + bh * N, bits_s, sum_s,
+                              in.sn);
+  } else if (blockIdx.y == 0) {
     pack_block<DT, 256>(q, ntok, d, blockIdx.x, qbits, qmu, bits_s, sum_s);
-  else
+  } else {
     pack_block<DT, 256>(k, ntok, d, blockIdx.x, kbits, kmu, bits_s, sum_s);
+  }
 }
 
-hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t ntok,
+InView dense_view(int H, int N, int d) {
+  InView v;
+  v.sn = d;
+  v.sh = (int64_t)N * d;
+  v.sb = (int64_t)H * v.sh;
+  v.H = H;
+  v.vec = d % 8 == 0;
+  return v;
+}
+
+hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InView& in, int nbh, int N,
                           int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
                           float* kmu, hipStream_t s) {
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
-  if (d % 8 == 0) {
+  const int64_t ntok = (int64_t)nbh * N;
+  if (in.vec) {
     const int TB = 256 * kPackU / (d / 8);
-    const dim3 grid((unsigned)((ntok + TB - 1) / TB), 2);
-    if (dt == BA_F16)
-      hipLaunchKernelGGL(pack_qk_coop_kernel<BA_F16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
-    else
-      hipLaunchKernelGGL(pack_qk_coop_kernel<BA_BF16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+    const bool str = !in.dense(N, d);
+    const int64_t nbph = (N + TB - 1) / TB;
+    const int64_t nblk = str ? nbh * nbph : (ntok + TB - 1) / TB;
+    if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nblk, 2);
+    auto kern = dt == BA_F16 ? (str ? pack_qk_coop_kernel<BA_F16, true> : pack_qk_coop_kernel<BA_F16, false>)
+                             : (str ? pack_qk_coop_kernel<BA_BF16, true> : pack_qk_coop_kernel<BA_BF16, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, q16, k16, in, N, nbph, ntok, d, qbits, qmu, kbits, kmu);
     return hipGetLastError();
   }
+  if ((ntok + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((ntok + 255) / 256), 2);
   if (dt == BA_F16)
-    hipLaunchKernelGGL(pack_qk_kernel<BA_F16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+    hipLaunchKernelGGL(pack_qk_kernel<BA_F16>, grid, dim3(256), 0, s, q16, k16, in, N, ntok, d, qbits, qmu, kbits, kmu);
   else
-    hipLaunchKernelGGL(pack_qk_kernel<BA_BF16>, grid, dim3(256), 0, s, q16, k16, ntok, d, qbits, qmu, kbits, kmu);
+    hipLaunchKernelGGL(pack_qk_kernel<BA_BF16>, grid, dim3(256), 0, s, q16, k16, in, N, ntok, d, qbits, qmu, kbits, kmu);
   return hipGetLastError();
 }
 
@@ -152,7 +190,7 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, int64_t nto
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(256) void quant_v_kernel(
-    const uint16_t* __restrict__ v, int nbh, int N, int d, int CG,
+    const uint16_t* __restrict__ v, InView in, int nbh, int N, int d, int CG,
     int8_t* __restrict__ vq, float* __restrict__ vscale, int32_t* __restrict__ vsum) {
   __shared__ uint32_t amax_bits[128];
   __shared__ float inv_s[128];
@@ -172,9 +210,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
   }
   __syncthreads();
 
-  const uint16_t* vh = v + (int64_t)bh * N * d;
+  const uint16_t* vh = v + (int64_t)(bh / in.H) * in.sb + (int64_t)(bh % in.H) * in.sh;  // row j at j * in.sn
   int8_t* qh = vq + (int64_t)bh * N * d;
-  const bool vec = (d % 8) == 0 && (cg % 8) == 0;
+  const bool vec = in.vec && (cg % 8) == 0;
   if (vec) {
     const int P = cg / 8;                 // 8-channel pieces per row
     const int rows = blockDim.x / P;      // rows per sweep
@@ -189,7 +227,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
         u4v raw[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * d + c0 + piece * 8);
+          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * in.sn + c0 + piece * 8);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -197,7 +235,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
             m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(raw[u][e >> 1] >> ((e & 1) * 16)))));
       }
       for (; j < N; j += rows) {
-        const u4v raw = *reinterpret_cast<const u4v*>(vh + (int64_t)j * d + c0 + piece * 8);
+        const u4v raw = *reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn + c0 + piece * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16)))));
@@ -234,14 +272,14 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
         u4v raw[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * d + c0 + piece * 8);
+          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * in.sn + c0 + piece * 8);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
           *reinterpret_cast<uint2*>(qh + (int64_t)(j + u * rows) * d + c0 + piece * 8) = quant8(raw[u]);
       }
       for (; j < N; j += rows) {
-        const int64_t off = (int64_t)j * d + c0 + piece * 8;
-        *reinterpret_cast<uint2*>(qh + off) = quant8(*reinterpret_cast<const u4v*>(vh + off));
+        *reinterpret_cast<uint2*>(qh + (int64_t)j * d + c0 + piece * 8) =
+            quant8(*reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn + c0 + piece * 8));
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) atomicAdd(&sum_s[piece * 8 + e], csum[e]);
@@ -250,7 +288,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
     // generic d: one thread per (row, channel) element, scalar accesses
     for (int idx = threadIdx.x; idx < N * cg; idx += blockDim.x) {
       const int j = idx / cg, c = idx % cg;
-      atomicMax(&amax_bits[c], __float_as_uint(fabsf(to_f32<DT>(vh[(int64_t)j * d + c0 + c]))));
+      atomicMax(&amax_bits[c], __float_as_uint(fabsf(to_f32<DT>(vh[(int64_t)j * in.sn + c0 + c]))));
     }
     __syncthreads();
     for (int i = threadIdx.x; i < cg; i += blockDim.x) {
@@ -261,7 +299,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
     __syncthreads();
     for (int idx = threadIdx.x; idx < N * cg; idx += blockDim.x) {
       const int j = idx / cg, c = idx % cg;
-      float y = __builtin_rintf(to_f32<DT>(vh[(int64_t)j * d + c0 + c]) * inv_s[c]);
+      float y = __builtin_rintf(to_f32<DT>(vh[(int64_t)j * in.sn + c0 + c]) * inv_s[c]);
       y = fminf(fmaxf(y, -127.0f), 127.0f);
       qh[(int64_t)j * d + c0 + c] = (int8_t)(int)y;
       atomicAdd(&sum_s[c], (int)y);
@@ -285,7 +323,8 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 // heads bh0 .. bh0 + HB - 1 (those below nbh) by one block of 1024
 // threads; smem holds 3 * 128 words per head
 template <int DT>
-__device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v, int N, int d, int64_t bh0,
+__device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v, const InView& in, int N, int d,
+                                                  int64_t bh0,
                                                   int64_t nbh, int HB, int8_t* __restrict__ vq,
                                                   float* __restrict__ vscale, int32_t* __restrict__ vsum,
                                                   uint32_t* smem) {
@@ -304,14 +343,13 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
     sum_s[t] = 0;
   }
   __syncthreads();
-  const int64_t hoff = hvalid ? bh * N * d : 0;
-  const uint16_t* vh = v + hoff + 8 * piece;
-  int8_t* qh = vq + hoff + 8 * piece;
+  const uint16_t* vh = v + (hvalid ? (bh / in.H) * in.sb + (bh % in.H) * in.sh : 0) + 8 * piece;
+  int8_t* qh = vq + (hvalid ? bh * N * d : 0) + 8 * piece;
   u4v x[kQvRows];
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k) {
     const int r = r0 + k * R;
-    x[k] = (active && r < N) ? *reinterpret_cast<const u4v*>(vh + (int64_t)r * d) : (u4v){0u, 0u, 0u, 0u};
+    x[k] = (active && r < N) ? *reinterpret_cast<const u4v*>(vh + (int64_t)r * in.sn) : (u4v){0u, 0u, 0u, 0u};
   }
   // max |v| per channel on the 16-bit patterns: for finite fp16 / bf16
   // values the magnitude bits (sign cleared) order like |v|, so a packed
@@ -380,20 +418,21 @@ int quant_heads_per_block(int nbh, int N, int d) {
 
 template <int DT>
 __global__ __launch_bounds__(1024) void quant_v_head_kernel(
-    const uint16_t* __restrict__ v, int nbh, int N, int d, int HB, int8_t* __restrict__ vq,
+    const uint16_t* __restrict__ v, InView in, int nbh, int N, int d, int HB, int8_t* __restrict__ vq,
     float* __restrict__ vscale, int32_t* __restrict__ vsum) {
   __shared__ uint32_t smem[8 * 3 * 128];
-  quant_heads_block<DT>(v, N, d, (int64_t)blockIdx.x * HB, nbh, HB, vq, vscale, vsum, smem);
+  quant_heads_block<DT>(v, in, N, d, (int64_t)blockIdx.x * HB, nbh, HB, vq, vscale, vsum, smem);
 }
 
 // Pack Q and K and quantise V in one launch (d % 8 == 0, heads that fit the
 // register-resident quantiser): blocks 0 .. nvb-1 quantise HB heads each
 // (the long-running ones, dispatched first), the rest pack npb blocks of
-// tokens of Q, then npb of K, all with 1024 threads.
-template <int DT>
+// tokens of Q, then npb of K, all with 1024 threads. STR (a strided view):
+// the pack blocks are nbph per head, each within one head.
+template <int DT, bool STR>
 __global__ __launch_bounds__(1024) void prepass_fused_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int nbh, int N, int d, int HB, int64_t nvb, int64_t npb, uint32_t* __restrict__ qbits,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, InView in,
+    int nbh, int N, int d, int HB, int64_t nvb, int64_t npb, int64_t nbph, uint32_t* __restrict__ qbits,
     float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
     float* __restrict__ vscale, int32_t* __restrict__ vsum) {
   __shared__ uint32_t bits_s[1024 * kPackU];
@@ -401,7 +440,15 @@ __global__ __launch_bounds__(1024) void prepass_fused_kernel(
   const int64_t ntok = (int64_t)nbh * N;
   const int64_t b = blockIdx.x;
   if (b < nvb) {
-    quant_heads_block<DT>(v, N, d, b * HB, nbh, HB, vq, vscale, vsum, bits_s);
+    quant_heads_block<DT>(v, in, N, d, b * HB, nbh, HB, vq, vscale, vsum, bits_s);
+  } else if constexpr (STR) {
+    const bool isk = b - nvb >= npb;
+    const int64_t pb = b - nvb - (isk ? npb : 0);
+    const int64_t bh = pb / nbph, tb = pb - bh * nbph;
+    const int W = (d + 31) >> 5;
+    pack_block<DT, 1024, true>((isk ? k : q) + (bh / in.H) * in.sb + (bh % in.H) * in.sh, N, d, tb,
+                               (isk ? kbits : qbits) + bh * N * W, (isk ? kmu : qmu) + bh * N, bits_s, sum_s,
+                               in.sn);
   } else if (b - nvb < npb) {
     pack_block<DT, 1024>(q, ntok, d, b - nvb, qbits, qmu, bits_s, sum_s);
   } else {
@@ -409,22 +456,24 @@ __global__ __launch_bounds__(1024) void prepass_fused_kernel(
   }
 }
 
-hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
+hipError_t launch_quant_v(const void* v, ba_dtype dt, const InView& in, int nbh, int N, int d,
                           int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s) {
-  if (d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
+  if (in.vec && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     const int HB = quant_heads_per_block(nbh, N, d);
     const unsigned nvb = (unsigned)((nbh + HB - 1) / HB);
     if (dt == BA_F16)
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3(nvb), dim3(1024), 0, s, v16, nbh, N, d, HB, vq, vscale, vsum);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3(nvb), dim3(1024), 0, s, v16, in, nbh, N, d, HB, vq, vscale,
+                         vsum);
     else
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3(nvb), dim3(1024), 0, s, v16, nbh, N, d, HB, vq, vscale, vsum);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3(nvb), dim3(1024), 0, s, v16, in, nbh, N, d, HB, vq, vscale,
+                         vsum);
     return hipGetLastError();
   }
   // widest channel group (whole rows when possible) that still gives
   // >= 1024 blocks; at least 8 channels per group, at most 128.
   int CG = d;
-  if (d % 8 == 0) {
+  if (in.vec) {
     while (CG > 8 && (int64_t)nbh * ((d + CG - 1) / CG) < 1024) {
       int next = CG / 2;
       if (next % 8) next = (next / 8) * 8;
@@ -436,9 +485,11 @@ hipError_t launch_quant_v(const void* v, ba_dtype dt, int nbh, int N, int d,
   const int64_t nblk = (int64_t)nbh * ngroups;
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   if (dt == BA_F16)
-    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale, vsum);
+    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, in, nbh, N, d, CG, vq, vscale,
+                       vsum);
   else
-    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, nbh, N, d, CG, vq, vscale, vsum);
+    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, in, nbh, N, d, CG, vq,
+                       vscale, vsum);
   return hipGetLastError();
 }
 
@@ -446,17 +497,19 @@ bool prepass_fusable(int N, int d) {
   return d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8));
 }
 
-hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, int nbh, int N, int d,
-                          uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
+hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, const InView& in, int nbh,
+                          int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
                           float* vscale, int32_t* vsum, hipStream_t s) {
   const int64_t ntok = (int64_t)nbh * N;
-  if (!prepass_fusable(N, d)) {
-    hipError_t e = launch_pack_qk(q, k, dt, ntok, d, qbits, qmu, kbits, kmu, s);
+  if (!in.vec || !prepass_fusable(N, d)) {
+    hipError_t e = launch_pack_qk(q, k, dt, in, nbh, N, d, qbits, qmu, kbits, kmu, s);
     if (e != hipSuccess) return e;
-    return launch_quant_v(v, dt, nbh, N, d, vq, vscale, vsum, s);
+    return launch_quant_v(v, dt, in, nbh, N, d, vq, vscale, vsum, s);
   }
   const int TB = 1024 * kPackU / (d / 8);
-  const int64_t npb = (ntok + TB - 1) / TB;
+  const bool str = !in.dense(N, d);
+  const int64_t nbph = (N + TB - 1) / TB;
+  const int64_t npb = str ? nbh * nbph : (ntok + TB - 1) / TB;
   const int HB = quant_heads_per_block(nbh, N, d);
   const int64_t nvb = (nbh + HB - 1) / HB;
   const int64_t nblk = nvb + 2 * npb;
@@ -464,12 +517,10 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
-  if (dt == BA_F16)
-    hipLaunchKernelGGL(prepass_fused_kernel<BA_F16>, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, nbh, N,
-                       d, HB, nvb, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
-  else
-    hipLaunchKernelGGL(prepass_fused_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, nbh, N,
-                       d, HB, nvb, npb, qbits, qmu, kbits, kmu, vq, vscale, vsum);
+  auto kern = dt == BA_F16 ? (str ? prepass_fused_kernel<BA_F16, true> : prepass_fused_kernel<BA_F16, false>)
+                           : (str ? prepass_fused_kernel<BA_BF16, true> : prepass_fused_kernel<BA_BF16, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, nvb, npb, nbph,
+                     qbits, qmu, kbits, kmu, vq, vscale, vsum);
   return hipGetLastError();
 }
 

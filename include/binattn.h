@@ -19,8 +19,11 @@
  *    queued on `stream` has finished.
  *  - Stream: `stream` is a hipStream_t passed as void* (NULL = the default
  *    stream). Every call only enqueues work; none synchronises.
- *  - Layouts: dense, row-major, no strides. Tokens are [B, H, N, d] (head
- *    index bh = b*H + h). W = ba_packed_words(d) = ceil(d/32).
+ *  - Layouts: dense, row-major. Tokens are [B, H, N, d] (head index
+ *    bh = b*H + h). W = ba_packed_words(d) = ceil(d/32). The two *_strided
+ *    calls also read Q/K/V from, and write the output to, strided views
+ *    (ba_strides); every layout the library writes besides that output is
+ *    dense.
  *  - Errors: arguments are validated before any HIP call. A rejected call
  *    returns BA_ERR_INVALID_ARG (null or misaligned pointer, size < 1,
  *    inconsistent bias description) or BA_ERR_UNSUPPORTED (d outside
@@ -58,6 +61,16 @@ typedef enum {
 /* Largest N accepted: the integer P.V sum must stay inside int32
  * (255 * 127 * N < 2^31). */
 #define BA_MAX_TOKENS 65536
+
+/* Element strides of a [B, H, N, d] view of 16-bit values whose d channels
+ * are contiguous: element (b, h, n, c) sits at
+ * base + b*batch + h*head + n*token + c (in elements, not bytes). Strides are
+ * non-negative. The dense layout is {H*N*d, N*d, d}; the per-head slices of
+ * a fused QKV projection output [B, N, 3, H, d] are {3*N*H*d, d, 3*H*d}
+ * (from the q, k and v bases 0, H*d and 2*H*d). */
+typedef struct {
+  int64_t batch, head, token;
+} ba_strides;
 
 /* Additive bias b_ij on the scores (bias enhancement: zh technical summary
  * section 2.2 item 2; nl Methodologie 2; it/fr/pt section 2B). The pages
@@ -120,6 +133,21 @@ ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dty
                              int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu,
                              int8_t* vq, float* vscale, int32_t* vsum, void* stream);
 
+/* ba_pack_qk_quant_v with q, k and v read through strided views that share
+ * in_strides (typically the head slices of one QKV projection output, so no
+ * head-split copy is needed; zh technical summary section 4 measures the
+ * method inside whole transformer layers). The outputs are the dense ones
+ * of ba_pack_qk_quant_v, bit for bit equal to packing a dense copy. q, k, v
+ * need 2-byte alignment only; where d % 8 == 0, every stride is a multiple
+ * of 8 and q, k, v are 16-byte aligned, the 16-byte-load kernels run. The
+ * views may overlap one another (they are only read) but no output may
+ * overlap the span of any view. in_strides NULL or negative, or a view
+ * spanning more than 2^40 elements: BA_ERR_INVALID_ARG. */
+ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v, const ba_strides* in_strides,
+                                     ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
+                                     uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, int32_t* vsum,
+                                     void* stream);
+
 /* Fused BinaryAttention forward (zh sections 2.1-2.3; nl Methodologie 1-3;
  * it section 2; fr section 2B; pt section 2B-2C), non-causal, self-attention
  * (N queries and N keys per head). For each head and query i:
@@ -144,6 +172,23 @@ ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu,
                            const int32_t* vsum, const ba_bias* bias,
                            int B, int H, int N, int d,
                            void* out, ba_dtype out_dt, void* stream);
+
+/* ba_attention_fwd writing the output through a strided view: element
+ * (b, h, i, c) of the result goes to out + b*batch + h*head + i*token + c
+ * (e.g. {N*H*d, d, H*d} writes [B, N, H, d], the input layout of an output
+ * projection, with no head-merge copy). The same values as
+ * ba_attention_fwd, bit for bit; elements outside the view are not
+ * touched. out needs 2-byte alignment (8-byte stores where d and the
+ * strides are multiples of 4 and out is 8-byte aligned). The view must not
+ * map two elements to one address and its span must not overlap an input:
+ * BA_ERR_INVALID_ARG otherwise, as for NULL or negative strides. */
+ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu,
+                                   const uint32_t* kbits, const float* kmu,
+                                   const int8_t* vq, const float* vscale,
+                                   const int32_t* vsum, const ba_bias* bias,
+                                   int B, int H, int N, int d, void* out,
+                                   const ba_strides* out_strides, ba_dtype out_dt,
+                                   void* stream);
 
 /* Integer Hamming similarity for inspection (zh sections 2.1 and 2.2 item 1;
  * it section 2A; fr section 2A): for heads [bh_begin, bh_begin+bh_count) and

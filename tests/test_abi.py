@@ -6,7 +6,7 @@ import ctypes
 import pytest
 
 import bit_qk_attention_amd as ba
-from bit_qk_attention_amd import ba_bias
+from bit_qk_attention_amd import ba_bias, ba_strides
 
 OK, INV, UNS = ba.BA_OK, ba.BA_ERR_INVALID_ARG, ba.BA_ERR_UNSUPPORTED
 P = 0x7F0000000000  # fake, 256-byte aligned device addresses (never dereferenced)
@@ -24,7 +24,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = ba.header_symbols()
     assert set(names) == {"ba_packed_words", "ba_pack_qk", "ba_quant_v", "ba_pack_qk_quant_v",
-                          "ba_attention_fwd", "ba_debug_hamming_scores", "ba_status_string"}
+                          "ba_pack_qk_quant_v_strided", "ba_attention_fwd", "ba_attention_fwd_strided",
+                          "ba_debug_hamming_scores", "ba_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -121,3 +122,49 @@ def test_hamming_rejections(L):
     assert ham(bh0=1, nbh=2) == INV and ham(r0=5, nr=6) == INV and ham(bh0=-1) == INV
     assert ham(d=129) == UNS
     assert ham(sig=A(0)) == INV
+
+
+def prep_s(L, st=ba_strides(3 * 8 * 64, 64, 3 * 64), q=A(0), k=None, v=None, dt=ba.BA_BF16, B=1, H=1, N=8, d=64,
+           **kw):
+    # default: q, k, v are the head slices of one [B, N, 3, H, d] buffer
+    k = k or ctypes.c_void_p(P + 2 * H * d)
+    v = v or ctypes.c_void_p(P + 4 * H * d)
+    o = dict(qb=A(3), qm=A(4), kb=A(5), km=A(6), vq=A(7), vs=A(8), vsum=A(9))
+    o.update(kw)
+    pst = ctypes.byref(st) if st is not None else None
+    return L.ba_pack_qk_quant_v_strided(q, k, v, pst, dt, B, H, N, d, o["qb"], o["qm"], o["kb"], o["km"],
+                                        o["vq"], o["vs"], o["vsum"], None)
+
+
+def test_pack_qk_quant_v_strided_rejections(L):
+    assert prep_s(L, st=None) == INV
+    assert prep_s(L, st=ba_strides(0, 0, -1)) == INV
+    assert prep_s(L, st=ba_strides(1 << 40, 0, 64), B=2) == INV      # span above 2^40 elements
+    assert prep_s(L, q=None) == INV and prep_s(L, vsum=None) == INV
+    assert prep_s(L, q=ctypes.c_void_p(P + 1)) == INV                 # not 2-byte aligned
+    assert prep_s(L, N=0) == INV and prep_s(L, d=129) == UNS and prep_s(L, dt=ba.BA_F32) == UNS
+    # an output inside the span of the V view: V's last token starts at element 2*C + 7*3*C
+    assert prep_s(L, vq=ctypes.c_void_p(P + 2 * (2 * 64 + 7 * 3 * 64) + 16)) == INV
+    assert prep_s(L, qm=A(3)) == INV                                  # outputs overlap
+
+
+def attn_s(L, st=ba_strides(16 * 2 * 64, 64, 2 * 64), B=2, H=2, N=16, d=64, out=A(9), **kw):
+    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6), vsum=A(7))
+    args.update(kw)
+    pst = ctypes.byref(st) if st is not None else None
+    return L.ba_attention_fwd_strided(args["qb"], args["qm"], args["kb"], args["km"], args["vq"], args["vs"],
+                                      args["vsum"], None, B, H, N, d, out, pst, ba.BA_BF16, None)
+
+
+def test_attention_strided_rejections(L):
+    assert attn_s(L, st=None) == INV and attn_s(L, out=None) == INV
+    assert attn_s(L, st=ba_strides(-1, 64, 128)) == INV
+    assert attn_s(L, out=ctypes.c_void_p(P + 9 * (1 << 32) + 1)) == INV  # not 2-byte aligned
+    # views that map two elements to one address
+    assert attn_s(L, st=ba_strides(0, 64, 128)) == INV                     # batches alias
+    assert attn_s(L, st=ba_strides(2048, 32, 128)) == INV                  # heads overlap channels
+    assert attn_s(L, st=ba_strides(2048, 64, 0)) == INV                    # tokens alias
+    assert attn_s(L, st=ba_strides(2048, 64, 64)) == INV                   # tokens land on the next head
+    # the span of the view reaches an input (vsum at A(7))
+    assert attn_s(L, out=ctypes.c_void_p(P + 7 * (1 << 32) - 1024)) == INV
+    assert attn_s(L, d=129) == UNS
