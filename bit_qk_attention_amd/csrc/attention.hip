@@ -456,11 +456,6 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   auto finish_k = [&](auto bufc) {
     if constexpr (!RAWK) expand_k(bufc, pick(bufc).kraw[tid]);
   };
-  // bounds-checked K word of tile t, loaded and expanded synchronously
-  auto stage_k_checked = [&](int t, auto bufc) {
-    const int j = t * kBC + kw_key;
-    expand_k(bufc, (kw_w < W && j < N) ? p.kbits[(bh * N + j) * W + kw_w] : 0u);
-  };
   // relative-position window rows of tile t (always in bounds of the table)
   auto dma_tbl = [&](int t, auto bufc) {
     KS& sb = pick(bufc);
@@ -516,34 +511,41 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       }
     }
   };
-  // V tile t through registers, rows past N zero (ragged tile; any d)
+  // V tile t through registers, rows past N zero (tiles of V without the
+  // DMA layout; any d)
   auto copy_v_checked = [&](int t, auto bufc) {
     VSt& sb = pick_v(bufc);
     const int j0 = t * kBC;
-    if (p.v_dma) {
-      for (int x = tid; x < kBC * d / 8; x += 256) {
-        const int off = 8 * x, row = off / d, col = off % d;
-        uint2 v = make_uint2(0u, 0u);
-        if (j0 + row < N) v = *reinterpret_cast<const uint2*>(p.vq + (bh * N + j0) * d + off);
-        *reinterpret_cast<uint2*>(sb.vr + vaddr(row, col)) = v;
-      }
-    } else {
-      for (int x = tid; x < kBC * d; x += 256) {
-        const int row = x / d, col = x % d;
-        const int j = j0 + row;
-        sb.vr[row * VS + col] = j < N ? (uint8_t)p.vq[(bh * N + j) * d + col] : (uint8_t)0;
-      }
+    for (int x = tid; x < kBC * d; x += 256) {
+      const int row = x / d, col = x % d;
+      const int j = j0 + row;
+      sb.vr[row * VS + col] = j < N ? (uint8_t)p.vq[(bh * N + j) * d + col] : (uint8_t)0;
     }
   };
-  // synchronous staging of tile t with bounds checks (the ragged tile)
+  // The ragged tile, staged after the full ones by the same DMA but with the
+  // tile's offset in the per-lane offset, which each descriptor's range check
+  // covers: every access past the head's keys is dropped. Whatever those
+  // lanes leave in LDS is never used (scores of keys past N are masked, and
+  // their P.V operand bytes zeroed). The caller waits, expands the K words
+  // and synchronises.
   auto stage_checked = [&](int t, auto bufc, bool with_v) {
     KS& sb = pick(bufc);
-    stage_k_checked(t, bufc);
-    if (wave == 1) {
-      const int j = t * kBC + lane;
-      sb.mk[lane] = j < N ? p.kmu[bh * N + j] : 0.0f;
+    const int j0 = t * kBC;
+    if (with_v) {
+      if (p.v_dma) {
+        VSt& vb = pick_v(bufc);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (v_on[i])
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16,
+                                                     v_src[i] + j0 * d, 0, 0, 0);
+      } else {
+        copy_v_checked(t, bufc);
+      }
     }
-    if (with_v) copy_v_checked(t, bufc);
+    if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * (lane + j0), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kbits, (lptr_t*)(sb.kraw + 64 * wave), 4, kw_src + 4 * j0 * W, 0,
+                                             0, 0);
     dma_tbl(t, bufc);
     stage_koff(t, bufc);
   };
@@ -766,6 +768,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     } else {
       stage_checked(0, IntC<0>(), with_v);
       wait_vm0();
+      finish_k(IntC<0>());
     }
     __syncthreads();
     auto step = [&](int t, auto cur) {
@@ -795,6 +798,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         if (nfull > 0) {
           stage_checked(t, cur, with_v);
           wait_vm0();
+          finish_k(cur);
           __syncthreads();
         }
         body(BoolC<true>(), t, cur);
@@ -999,6 +1003,18 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       wd = __builtin_amdgcn_cvt_pk_u8_f32(e2, 2, wd);
       wd = __builtin_amdgcn_cvt_pk_u8_f32(e3, 3, wd);
       pw[r] = wd ^ 0x7F7F7F7Fu;  // u8 p8 -> s8 (127 - p8)
+    }
+    if (TAIL) {
+      // keys past N: operand 0, so the (unused) V rows staged for them add
+      // nothing
+      const int jb = t * kBC + kb * 32 + 16 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t keep = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) keep |= (jb + 4 * r + e < N ? 0xFFu : 0u) << (8 * e);
+        pw[r] &= keep;
+      }
     }
     return (v4i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
   };
