@@ -142,7 +142,7 @@ ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dty
  * of 8 and q, k, v are 16-byte aligned, the 16-byte-load kernels run. The
  * views may overlap one another (they are only read) but no output may
  * overlap the span of any view. in_strides NULL or negative, or a view
- * spanning more than 2^40 elements: BA_ERR_INVALID_ARG. */
+ * spanning more than about 2^40 elements: BA_ERR_INVALID_ARG. */
 ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v, const ba_strides* in_strides,
                                      ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
                                      uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, int32_t* vsum,
@@ -181,7 +181,9 @@ ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu,
  * touched. out needs 2-byte alignment (8-byte stores where d and the
  * strides are multiples of 4 and out is 8-byte aligned). The view must not
  * map two elements to one address and its span must not overlap an input:
- * BA_ERR_INVALID_ARG otherwise, as for NULL or negative strides. */
+ * BA_ERR_INVALID_ARG otherwise, as for NULL or negative strides or a span
+ * above about 2^40 elements; a head or token stride above 2^31 - 1:
+ * BA_ERR_UNSUPPORTED. */
 ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu,
                                    const uint32_t* kbits, const float* kmu,
                                    const int8_t* vq, const float* vscale,

@@ -168,3 +168,4 @@ def test_attention_strided_rejections(L):
     # the span of the view reaches an input (vsum at A(7))
     assert attn_s(L, out=ctypes.c_void_p(P + 7 * (1 << 32) - 1024)) == INV
     assert attn_s(L, d=129) == UNS
+    assert attn_s(L, st=ba_strides(1 << 33, 1 << 32, 64), N=1) == UNS   # head stride above 2^31 - 1
