@@ -9,6 +9,8 @@
 //
 // All three are memory-bound; the kernels aim at coalesced 16-byte accesses
 // and an XCD-aware block order where blocks share cache lines.
+#include <algorithm>
+
 #include "common.h"
 
 namespace binattn {
@@ -179,134 +181,48 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InVie
 }
 
 // ---------------------------------------------------------------------------
-// quant_v: one block per (head, channel group of CG channels). The block
-// reads the group's columns of all N tokens twice: pass 1 takes the per-
-// channel max |v| (an LDS atomic max on the float bits, valid because the
-// values are non-negative), pass 2 quantises with inv = 127/amax, writes
-// int8 and gathers the channel sums of the int8 values (LDS atomic adds). With CG == d a wave reads whole rows (fully coalesced); smaller
-// groups keep enough blocks in flight when there are few heads, and the
-// block order keeps the groups of one head on one XCD so they share L2.
-// VEC: d % 8 == 0, each thread handles 8 consecutive channels.
+// quant_v, element path (d % 8 != 0, or rows of a strided view that are not
+// 16-byte aligned): one block per head, one thread per (row, channel)
+// element with scalar accesses. Pass 1 takes the per-channel max |v| (an
+// LDS atomic max on the float bits, valid because the values are
+// non-negative), pass 2 quantises with inv = 127/amax, writes int8 and
+// gathers the channel sums of the int8 values (LDS atomic adds).
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(256) void quant_v_kernel(
-    const uint16_t* __restrict__ v, InView in, int nbh, int N, int d, int CG,
+    const uint16_t* __restrict__ v, InView in, int N, int d,
     int8_t* __restrict__ vq, float* __restrict__ vscale, int32_t* __restrict__ vsum) {
   __shared__ uint32_t amax_bits[128];
   __shared__ float inv_s[128];
   __shared__ int32_t sum_s[128];
-  const int ngroups = (d + CG - 1) / CG;
-  const int nblk = nbh * ngroups;
-  // XCD-aware order: consecutive block ids go to different XCDs, so hand each
-  // XCD a contiguous range of (head, group) work items.
-  int u = blockIdx.x;
-  if ((nblk & 7) == 0) u = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int bh = u / ngroups;
-  const int c0 = (u % ngroups) * CG;
-  const int cg = min(CG, d - c0);
-  for (int i = threadIdx.x; i < cg; i += blockDim.x) {
+  const int bh = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
     amax_bits[i] = 0u;
     sum_s[i] = 0;
   }
   __syncthreads();
-
   const uint16_t* vh = v + (int64_t)(bh / in.H) * in.sb + (int64_t)(bh % in.H) * in.sh;  // row j at j * in.sn
   int8_t* qh = vq + (int64_t)bh * N * d;
-  const bool vec = in.vec && (cg % 8) == 0;
-  if (vec) {
-    const int P = cg / 8;                 // 8-channel pieces per row
-    const int rows = blockDim.x / P;      // rows per sweep
-    const int piece = threadIdx.x % P;
-    const int r0 = threadIdx.x / P;
-    const bool active = r0 < rows;
-    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (active) {
-      // 8 rows in flight per thread
-      int j = r0;
-      for (; j + 7 * rows < N; j += 8 * rows) {
-        u4v raw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * in.sn + c0 + piece * 8);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(raw[u][e >> 1] >> ((e & 1) * 16)))));
-      }
-      for (; j < N; j += rows) {
-        const u4v raw = *reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn + c0 + piece * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16)))));
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) atomicMax(&amax_bits[piece * 8 + e], __float_as_uint(m[e]));
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < cg; i += blockDim.x) {
-      const float a = __uint_as_float(amax_bits[i]);
-      inv_s[i] = a > 0.0f ? 127.0f / a : 0.0f;
-      vscale[(int64_t)bh * d + c0 + i] = a / 127.0f;
-    }
-    __syncthreads();
-    if (active) {
-      float inv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) inv[e] = inv_s[piece * 8 + e];
-      int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      auto quant8 = [&](const u4v& raw) -> uint2 {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
-          y = fminf(fmaxf(y, -127.0f), 127.0f);
-          csum[e] += (int)y;
-          const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
-          if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
-        }
-        return make_uint2(lo, hi);
-      };
-      int j = r0;
-      for (; j + 7 * rows < N; j += 8 * rows) {
-        u4v raw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * in.sn + c0 + piece * 8);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          *reinterpret_cast<uint2*>(qh + (int64_t)(j + u * rows) * d + c0 + piece * 8) = quant8(raw[u]);
-      }
-      for (; j < N; j += rows) {
-        *reinterpret_cast<uint2*>(qh + (int64_t)j * d + c0 + piece * 8) =
-            quant8(*reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn + c0 + piece * 8));
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) atomicAdd(&sum_s[piece * 8 + e], csum[e]);
-    }
-  } else {
-    // generic d: one thread per (row, channel) element, scalar accesses
-    for (int idx = threadIdx.x; idx < N * cg; idx += blockDim.x) {
-      const int j = idx / cg, c = idx % cg;
-      atomicMax(&amax_bits[c], __float_as_uint(fabsf(to_f32<DT>(vh[(int64_t)j * in.sn + c0 + c]))));
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < cg; i += blockDim.x) {
-      const float a = __uint_as_float(amax_bits[i]);
-      inv_s[i] = a > 0.0f ? 127.0f / a : 0.0f;
-      vscale[(int64_t)bh * d + c0 + i] = a / 127.0f;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < N * cg; idx += blockDim.x) {
-      const int j = idx / cg, c = idx % cg;
-      float y = __builtin_rintf(to_f32<DT>(vh[(int64_t)j * in.sn + c0 + c]) * inv_s[c]);
-      y = fminf(fmaxf(y, -127.0f), 127.0f);
-      qh[(int64_t)j * d + c0 + c] = (int8_t)(int)y;
-      atomicAdd(&sum_s[c], (int)y);
-    }
+  for (int idx = threadIdx.x; idx < N * d; idx += blockDim.x) {
+    const int j = idx / d, c = idx % d;
+    atomicMax(&amax_bits[c], __float_as_uint(fabsf(to_f32<DT>(vh[(int64_t)j * in.sn + c]))));
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < cg; i += blockDim.x) vsum[(int64_t)bh * d + c0 + i] = sum_s[i];
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float a = __uint_as_float(amax_bits[i]);
+    inv_s[i] = a > 0.0f ? 127.0f / a : 0.0f;
+    vscale[(int64_t)bh * d + i] = a / 127.0f;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < N * d; idx += blockDim.x) {
+    const int j = idx / d, c = idx % d;
+    float y = __builtin_rintf(to_f32<DT>(vh[(int64_t)j * in.sn + c]) * inv_s[c]);
+    y = fminf(fmaxf(y, -127.0f), 127.0f);
+    qh[(int64_t)j * d + c] = (int8_t)(int)y;
+    atomicAdd(&sum_s[c], (int)y);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < d; i += blockDim.x) vsum[(int64_t)bh * d + i] = sum_s[i];
 }
 
 // quant_v for heads that fit in registers (d % 8 == 0): a block of 1024
@@ -456,6 +372,133 @@ __global__ __launch_bounds__(1024) void prepass_fused_kernel(
   }
 }
 
+// quant_v for long heads (16-byte rows, heads past the register-resident
+// quantiser): the rows of each head are split over S blocks so that the whole
+// chip streams V. After a zero fill of vscale and vsum, pass A takes each
+// block's channel maxima of |v| and combines them with a global atomic max
+// on the float bits kept in vscale (valid for non-negative values); pass B
+// reads them back, quantises with inv = 127 / amax, writes int8 and combines
+// the channel sums with global atomic adds into vsum; a last pass turns the
+// maxima into vscale = amax / 127. The arithmetic is that of the one-block
+// quantisers, so the outputs are the same bit for bit.
+__global__ __launch_bounds__(256) void zero2_kernel(uint32_t* __restrict__ a, int32_t* __restrict__ b, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    a[i] = 0u;
+    b[i] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void amax_to_scale_kernel(float* __restrict__ vscale, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) vscale[i] = vscale[i] / 127.0f;  // amax, held as its float bits, to the scale
+}
+
+// Block x: head x / S, rows [s * RB, min(N, s * RB + RB)) with s = x % S.
+// QUANT false: pass A (maxima into amax_bits); true: pass B.
+template <int DT, bool QUANT>
+__global__ __launch_bounds__(256) void quant_v_split_kernel(
+    const uint16_t* __restrict__ v, InView in, int N, int d, int S, int RB, int8_t* __restrict__ vq,
+    uint32_t* __restrict__ amax_bits, int32_t* __restrict__ vsum) {
+  __shared__ uint32_t red[128];  // channel maxima (pass A) or sums (pass B)
+  __shared__ float inv_s[128];
+  const int64_t bh = blockIdx.x / S;
+  const int r_begin = (int)(blockIdx.x - bh * S) * RB, r_end = min(N, r_begin + RB);
+  const int P = d >> 3, rows = 256 / P;  // 16-byte pieces per row, rows per sweep
+  const int piece = threadIdx.x % P, r0 = threadIdx.x / P;
+  const bool active = r0 < rows;
+  if (threadIdx.x < d) {
+    red[threadIdx.x] = 0u;
+    if (QUANT) {
+      const float a = __uint_as_float(amax_bits[bh * d + threadIdx.x]);
+      inv_s[threadIdx.x] = a > 0.0f ? 127.0f / a : 0.0f;
+    }
+  }
+  __syncthreads();
+  const uint16_t* vh = v + (bh / in.H) * in.sb + (bh % in.H) * in.sh + 8 * piece;  // row j at j * in.sn
+  if constexpr (!QUANT) {
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto take = [&](const u4v& raw) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        m[e] = fmaxf(m[e], fabsf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16)))));
+    };
+    if (active) {
+      int j = r_begin + r0;
+      for (; j + 7 * rows < r_end; j += 8 * rows) {  // 8 rows in flight per thread
+        u4v raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * in.sn);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) take(raw[u]);
+      }
+      for (; j < r_end; j += rows) take(*reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicMax(&red[8 * piece + e], __float_as_uint(m[e]));
+    }
+    __syncthreads();
+    if (threadIdx.x < d && red[threadIdx.x] != 0u) atomicMax(&amax_bits[bh * d + threadIdx.x], red[threadIdx.x]);
+  } else {
+    float inv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
+    int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto quant8 = [&](const u4v& raw) -> uint2 {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
+        y = fminf(fmaxf(y, -127.0f), 127.0f);
+        csum[e] += (int)y;
+        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
+        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+      }
+      return make_uint2(lo, hi);
+    };
+    int8_t* qh = vq + bh * N * d + 8 * piece;
+    if (active) {
+      int j = r_begin + r0;
+      for (; j + 7 * rows < r_end; j += 8 * rows) {
+        u4v raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * rows) * in.sn);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) *reinterpret_cast<uint2*>(qh + (int64_t)(j + u * rows) * d) = quant8(raw[u]);
+      }
+      for (; j < r_end; j += rows)
+        *reinterpret_cast<uint2*>(qh + (int64_t)j * d) = quant8(*reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicAdd(reinterpret_cast<int32_t*>(&red[8 * piece + e]), csum[e]);
+    }
+    __syncthreads();
+    const int32_t sum = (int32_t)red[threadIdx.x < d ? threadIdx.x : 0];
+    if (threadIdx.x < d && sum != 0) atomicAdd(&vsum[bh * d + threadIdx.x], sum);
+  }
+}
+
+template <int DT>
+hipError_t launch_quant_v_split(const uint16_t* v, const InView& in, int nbh, int N, int d, int8_t* vq,
+                                float* vscale, int32_t* vsum, hipStream_t s) {
+  const int rows = 256 / (d / 8);
+  // about four blocks per CU, each with at least one full sweep of 8 rows per thread
+  const int64_t want = (1024 + (int64_t)nbh - 1) / nbh;
+  const int64_t cap = std::max<int64_t>(1, N / (8 * rows));
+  const int S0 = (int)std::min(want, cap);
+  const int RB = (N + S0 - 1) / S0;
+  const int S = (N + RB - 1) / RB;
+  const int64_t nblk = (int64_t)nbh * S, n = (int64_t)nbh * d;
+  if (nblk > 0x7FFFFFFF || (n + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(vscale);
+  const unsigned nz = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(zero2_kernel, dim3(nz), dim3(256), 0, s, amax_bits, vsum, n);
+  hipLaunchKernelGGL((quant_v_split_kernel<DT, false>), dim3((unsigned)nblk), dim3(256), 0, s, v, in, N, d, S, RB, vq,
+                     amax_bits, vsum);
+  hipLaunchKernelGGL((quant_v_split_kernel<DT, true>), dim3((unsigned)nblk), dim3(256), 0, s, v, in, N, d, S, RB, vq,
+                     amax_bits, vsum);
+  hipLaunchKernelGGL(amax_to_scale_kernel, dim3(nz), dim3(256), 0, s, vscale, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_v(const void* v, ba_dtype dt, const InView& in, int nbh, int N, int d,
                           int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s) {
   if (in.vec && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
@@ -470,26 +513,17 @@ hipError_t launch_quant_v(const void* v, ba_dtype dt, const InView& in, int nbh,
                          vsum);
     return hipGetLastError();
   }
-  // widest channel group (whole rows when possible) that still gives
-  // >= 1024 blocks; at least 8 channels per group, at most 128.
-  int CG = d;
   if (in.vec) {
-    while (CG > 8 && (int64_t)nbh * ((d + CG - 1) / CG) < 1024) {
-      int next = CG / 2;
-      if (next % 8) next = (next / 8) * 8;
-      if (next < 8) next = 8;
-      CG = next;
-    }
+    const uint16_t* v16 = static_cast<const uint16_t*>(v);
+    return dt == BA_F16 ? launch_quant_v_split<BA_F16>(v16, in, nbh, N, d, vq, vscale, vsum, s)
+                        : launch_quant_v_split<BA_BF16>(v16, in, nbh, N, d, vq, vscale, vsum, s);
   }
-  const int ngroups = (d + CG - 1) / CG;
-  const int64_t nblk = (int64_t)nbh * ngroups;
+  // element path (d % 8 != 0 or rows not 16-byte aligned): one block per head
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   if (dt == BA_F16)
-    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, in, nbh, N, d, CG, vq, vscale,
-                       vsum);
+    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nbh), dim3(256), 0, s, v16, in, N, d, vq, vscale, vsum);
   else
-    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nblk), dim3(256), 0, s, v16, in, nbh, N, d, CG, vq,
-                       vscale, vsum);
+    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nbh), dim3(256), 0, s, v16, in, N, d, vq, vscale, vsum);
   return hipGetLastError();
 }
 

@@ -187,7 +187,9 @@ def test_key_permutation():
 @pytest.mark.parametrize("B,H,N,d", [
     (1, 1, 1, 8), (2, 3, 5, 72), (1, 2, 1024, 72), (8, 16, 300, 72), (1, 3, 777, 24),
     (1, 1, 16384, 64), (1, 1, 16385, 64), (2, 1, 4096, 128), (1, 2, 50, 20), (3, 1, 2049, 40),
-    (5, 103, 77, 64), (3, 97, 200, 72), (1, 131, 250, 128)])
+    (5, 103, 77, 64), (3, 97, 200, 72), (1, 131, 250, 128),
+    # heads split over several blocks (maxima and sums combined across blocks)
+    (2, 3, 1600, 72), (1, 1, 20000, 128), (2, 16, 4096, 64), (1, 4, 1537, 64), (1, 1, 7000, 16)])
 @pytest.mark.parametrize("dt", [F16, BF16])
 def test_quant_v_launch_shapes(B, H, N, d, dt):
     rng = np.random.default_rng(B * 1000003 + H * 1009 + N * 13 + d + dt)
