@@ -97,6 +97,7 @@ struct Params {
   int nqb;          // query blocks per head
   float inv_sqrt_d;
   int bias_f16;     // dense bias element type (BIAS_DENSE_ANY): fp16, else fp32
+  int bias_al4;     // BIAS_DENSE_ANY: every bias row starts 4-byte aligned
   int out_mode;     // bit 0: fp16 output (else bf16); bit 1: 8-byte row stores
                     // (d and the output strides % 4 == 0, 8-byte aligned base)
   int v_dma;        // V tiles go global -> LDS directly (16-byte pieces)
@@ -638,6 +639,27 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float4 v = src[r];
+            bv[4 * r] = v.x; bv[4 * r + 1] = v.y; bv[4 * r + 2] = v.z; bv[4 * r + 3] = v.w;
+          }
+        }
+      } else if (BIAS == BIAS_DENSE_ANY && !TAIL && p.bias_al4) {
+        // rows 4-byte but not 16-byte aligned: 16-byte loads at 4-byte
+        // alignment (gfx950 global loads accept them), not one load per value
+        typedef float f4a4 __attribute__((ext_vector_type(4), aligned(4)));
+        typedef unsigned u4a4 __attribute__((ext_vector_type(4), aligned(4)));
+        if (p.bias_f16) {
+          const u4a4* src = reinterpret_cast<const u4a4*>(static_cast<const uint16_t*>(p.bias) + row + jb);
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const u4a4 v = src[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[8 * r + e] = f16_to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+          }
+        } else {
+          const f4a4* src = reinterpret_cast<const f4a4*>(static_cast<const float*>(p.bias) + row + jb);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f4a4 v = src[r];
             bv[4 * r] = v.x; bv[4 * r + 1] = v.y; bv[4 * r + 2] = v.z; bv[4 * r + 3] = v.w;
           }
         }
@@ -1212,11 +1234,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 
   int bias = BIAS_NONE;
   p.bias_f16 = 0;
+  p.bias_al4 = 0;
   if (a.bias_kind == BA_BIAS_DENSE) {
     const int per16 = a.bias_dtype == BA_F32 ? 4 : 8;  // elements per 16 bytes
     const bool vec = (a.N % per16 == 0) && (a.bias_bstride % per16 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.bias) % 16 == 0);
     p.bias_f16 = a.bias_dtype == BA_F16;
+    p.bias_al4 = a.bias_dtype == BA_F32 ||
+                 (a.N % 2 == 0 && a.bias_bstride % 2 == 0 && reinterpret_cast<uintptr_t>(a.bias) % 4 == 0);
     bias = !vec ? BIAS_DENSE_ANY : (a.bias_dtype == BA_F32 ? BIAS_DENSE_F32 : BIAS_DENSE_F16);
   } else if (a.bias_kind == BA_BIAS_RELPOS) {
     bias = (a.grid_w % 16 == 0 && a.n_prefix == 0) ? BIAS_RELPOS_ROW : BIAS_RELPOS;
