@@ -97,7 +97,8 @@ struct Params {
   int nqb;          // query blocks per head
   float inv_sqrt_d;
   int bias_f16;     // dense bias element type (BIAS_DENSE_ANY): fp16, else fp32
-  int bias_al4;     // BIAS_DENSE_ANY: every bias row starts 4-byte aligned
+  int bias_al4;     // BIAS_DENSE_ANY: 1 every bias row starts 4-byte aligned; 2 only the
+                    // base is (fp16 rows at 2-byte alignment); 0 neither
   int out_mode;     // bit 0: fp16 output (else bf16); bit 1: 8-byte row stores
                     // (d and the output strides % 4 == 0, 8-byte aligned base)
   int v_dma;        // V tiles go global -> LDS directly (16-byte pieces)
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
             bv[4 * r] = v.x; bv[4 * r + 1] = v.y; bv[4 * r + 2] = v.z; bv[4 * r + 3] = v.w;
           }
         }
-      } else if (BIAS == BIAS_DENSE_ANY && !TAIL && p.bias_al4) {
+      } else if (BIAS == BIAS_DENSE_ANY && !TAIL && p.bias_al4 == 1) {
         // rows 4-byte but not 16-byte aligned: 16-byte loads at 4-byte
         // alignment (gfx950 global loads accept them), not one load per value
         typedef float f4a4 __attribute__((ext_vector_type(4), aligned(4)));
@@ -662,6 +663,23 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
             const f4a4 v = src[r];
             bv[4 * r] = v.x; bv[4 * r + 1] = v.y; bv[4 * r + 2] = v.z; bv[4 * r + 3] = v.w;
           }
+        }
+      } else if (BIAS == BIAS_DENSE_ANY && !TAIL && p.bias_al4 == 2) {
+        // fp16 rows only 2-byte aligned (a 4-byte aligned base): the 4-byte words around the lane's 16
+        // values (a ninth word only when they start mid-word, so nothing past
+        // the last value's word is read), realigned by a funnel shift
+        typedef unsigned u4a4 __attribute__((ext_vector_type(4), aligned(4)));
+        const int64_t o = row + jb;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.bias) + (o & ~(int64_t)1));
+        const uint32_t sh = 16u * (uint32_t)(o & 1);
+        const u4a4 w0 = reinterpret_cast<const u4a4*>(w)[0], w1 = reinterpret_cast<const u4a4*>(w)[1];
+        const uint32_t w8 = sh ? w[8] : 0u;
+        const uint32_t ws[9] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], w8};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t pr = __builtin_amdgcn_alignbit(ws[k + 1], ws[k], sh);
+          bv[2 * k] = f16_to_f32((uint16_t)pr);
+          bv[2 * k + 1] = f16_to_f32((uint16_t)(pr >> 16));
         }
       } else {
 #pragma unroll
@@ -1240,8 +1258,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const bool vec = (a.N % per16 == 0) && (a.bias_bstride % per16 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.bias) % 16 == 0);
     p.bias_f16 = a.bias_dtype == BA_F16;
-    p.bias_al4 = a.bias_dtype == BA_F32 ||
-                 (a.N % 2 == 0 && a.bias_bstride % 2 == 0 && reinterpret_cast<uintptr_t>(a.bias) % 4 == 0);
+    const bool base4 = reinterpret_cast<uintptr_t>(a.bias) % 4 == 0;
+    p.bias_al4 = (a.bias_dtype == BA_F32 || (a.N % 2 == 0 && a.bias_bstride % 2 == 0 && base4)) ? 1 : base4 ? 2 : 0;
     bias = !vec ? BIAS_DENSE_ANY : (a.bias_dtype == BA_F32 ? BIAS_DENSE_F32 : BIAS_DENSE_F16);
   } else if (a.bias_kind == BA_BIAS_RELPOS) {
     bias = (a.grid_w % 16 == 0 && a.n_prefix == 0) ? BIAS_RELPOS_ROW : BIAS_RELPOS;
