@@ -305,7 +305,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the attention shards by head with no communication; see DESIGN.md)", file=sys.stderr)
+              "(the attention shards by head with no communication)", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():

@@ -36,7 +36,7 @@ def dev_bias(inp):
     return None, None
 
 
-class GpuRun:
+class DeviceRun:
     """All device tensors of one forward pass."""
 
     def __init__(self, inp, out_dt=None):

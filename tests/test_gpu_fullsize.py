@@ -8,7 +8,7 @@ import torch
 
 import bit_qk_attention_amd as ba
 import oracle
-from gpu_helpers import GpuRun, vmax
+from gpu_helpers import DeviceRun, vmax
 from workloads import WORKLOADS, make
 
 pytestmark = pytest.mark.gpu
@@ -20,7 +20,7 @@ def test_full_size_sampled(name):
     inp = make(name)
     s = inp.spec
     print(f"[full-size] {name} B={s.B} H={s.H} N={s.N} d={s.d}", flush=True)
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     out = run.out.float()
     assert torch.isfinite(out).all()
     vq, vs = oracle.quant_v(inp.v, s.dtype)

@@ -11,7 +11,7 @@ import torch
 
 import bit_qk_attention_amd as ba
 import oracle
-from gpu_helpers import GpuRun, to_dev, vmax
+from gpu_helpers import DeviceRun, to_dev, vmax
 from workloads import BF16, F16, from_bits, make, to_bits
 
 pytestmark = pytest.mark.gpu
@@ -53,7 +53,7 @@ def check_out(run, rows=None, label=""):
 def test_prepass_bit_exact(name):
     inp = make(name, **REDUCED[name])
     s = inp.spec
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     qb, qm = oracle.pack(inp.q, s.dtype)
     kb, km = oracle.pack(inp.k, s.dtype)
     assert np.array_equal(run.qbits.cpu().numpy().view(np.uint32), qb)
@@ -70,7 +70,7 @@ def test_prepass_bit_exact(name):
 def test_hamming_bit_exact(name):
     inp = make(name, **REDUCED[name])
     s = inp.spec
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     sig = torch.empty((s.B * s.H, s.N, s.N), dtype=torch.int32, device="cuda")
     ba.ba_debug_hamming_scores(run.qbits, run.kbits, s.d, 0, s.B * s.H, 0, s.N, sig)
     qb, _ = oracle.pack(inp.q, s.dtype)
@@ -80,26 +80,26 @@ def test_hamming_bit_exact(name):
 
 @pytest.mark.parametrize("name", sorted(REDUCED))
 def test_attention_parity(name):
-    run = GpuRun(make(name, **REDUCED[name]))
+    run = DeviceRun(make(name, **REDUCED[name]))
     check_out(run)
 
 
 @pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200])
 def test_token_counts(N):
-    run = GpuRun(make("long_4k", B=1, H=2, N=N))
+    run = DeviceRun(make("long_4k", B=1, H=2, N=N))
     check_out(run, label=f"N={N}")
 
 
 @pytest.mark.parametrize("d", [1, 5, 16, 31, 32, 33, 48, 63, 64, 65, 72, 80, 96, 100, 127, 128])
 def test_head_dims(d):
     dt_name = "deit_tiny" if d % 2 else "dit_256"
-    run = GpuRun(make(dt_name, B=1, H=2, N=150, d=d))
+    run = DeviceRun(make(dt_name, B=1, H=2, N=150, d=d))
     check_out(run, label=f"d={d}")
 
 
 def test_output_dtype_other_than_input():
     inp = make("dit_256", B=1, H=2, N=100)
-    run = GpuRun(inp, out_dt=F16)
+    run = DeviceRun(inp, out_dt=F16)
     ref = oracle.attention(inp.q, inp.k, inp.v, BF16)
     got = run.out_f32().reshape(2, 100, 72)
     assert np.abs(got - ref.out).max() <= TOL * vmax(inp)
@@ -108,7 +108,7 @@ def test_output_dtype_other_than_input():
 def test_zero_queries_give_uniform_attention():
     inp = make("long_4k", B=1, H=1, N=90)
     inp.q[...] = 0  # +0: mu = 0 and every score is 0
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     vq, vs = oracle.quant_v(inp.v, BF16)
     vq = vq.reshape(90, 64).astype(np.float64)
     vs = vs.reshape(64).astype(np.float64)
@@ -120,7 +120,7 @@ def test_zero_queries_give_uniform_attention():
 def test_uniform_keys_closed_form():
     inp = make("dit_256", B=1, H=2, N=200)
     inp.k[:, :, 1:, :] = inp.k[:, :, :1, :]  # every key identical
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     vq, vs = oracle.quant_v(inp.v, BF16)
     want = vs.reshape(2, 1, 72).astype(np.float64) * vq.reshape(2, 200, 72).sum(1, keepdims=True) / 200
     got = run.out_f32().reshape(2, 200, 72)
@@ -133,7 +133,7 @@ def test_per_batch_dense_bias():
     per_b = (0.5 * rng.standard_normal((3, 2, 150, 150))).astype(np.float32)
     inp.bias_data = per_b.astype(np.float16).view(np.uint16)
     inp.bias_batch_stride = 2 * 150 * 150
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     check_out(run, label="per-batch dense fp16 bias")
 
 
@@ -144,7 +144,7 @@ def test_one_hot_bias():
     for h in range(3):
         bias[h, np.arange(120), jstar[h]] = 1e4
     inp.bias_data = bias
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     vq, vs = oracle.quant_v(inp.v, F16)
     got = run.out_f32().reshape(3, 120, 64)
     for h in range(3):
@@ -155,26 +155,26 @@ def test_one_hot_bias():
 def test_relpos_equals_materialised_dense():
     from test_oracle_attention import relpos_dense
     inp = make("deit_small", B=2, H=6)
-    run_rp = GpuRun(inp)
+    run_rp = DeviceRun(inp)
     dense = relpos_dense(inp.bias_data, 14, 14, 1)
     inp2 = make("deit_small", B=2, H=6)
     inp2.bias_kind, inp2.bias_data, inp2.bias_dtype, inp2.bias_batch_stride = 1, dense, 2, 0
-    run_d = GpuRun(inp2)
+    run_d = DeviceRun(inp2)
     assert torch.equal(run_rp.out, run_d.out)
 
 
 def test_deterministic():
-    run = GpuRun(make("dit_512", B=2, H=2, N=300))
+    run = DeviceRun(make("dit_512", B=2, H=2, N=300))
     assert torch.equal(run.out, run.rerun())
 
 
 def test_key_permutation():
     inp = make("long_4k", B=1, H=2, N=257)
-    run0 = GpuRun(inp)
+    run0 = DeviceRun(inp)
     perm = np.random.default_rng(9).permutation(257)
     inp.k = np.ascontiguousarray(inp.k[:, :, perm])
     inp.v = np.ascontiguousarray(inp.v[:, :, perm])
-    run1 = GpuRun(inp)
+    run1 = DeviceRun(inp)
     d = (run0.out.float() - run1.out.float()).abs().max().item()
     assert d <= 2e-3 * vmax(inp)
 
@@ -215,7 +215,7 @@ def test_quant_v_launch_shapes(B, H, N, d, dt):
 def test_bias_kinds_small_head_dims(name, d):
     kw = dict(REDUCED[name])
     kw["d"] = d
-    run = GpuRun(make(name, **kw))
+    run = DeviceRun(make(name, **kw))
     check_out(run, label=f"{name} d={d}")
 
 
@@ -225,12 +225,12 @@ def test_bias_kinds_small_head_dims(name, d):
 @pytest.mark.parametrize("N,d", [(64, 72), (320, 72), (328, 72), (136, 96), (328, 80), (392, 64),
                                  (200, 48), (256, 16), (8, 72)])
 def test_dense_f16_aligned_rows(N, d):
-    run = GpuRun(make("dit_512", B=2, H=2, N=N, d=d))
+    run = DeviceRun(make("dit_512", B=2, H=2, N=N, d=d))
     check_out(run, label=f"fp16 bias N={N} d={d}")
 
 
 def test_dense_f16_aligned_rows_per_batch():
-    run = GpuRun(make("dit_512", B=3, H=2, N=264, bias_shared=False))
+    run = DeviceRun(make("dit_512", B=3, H=2, N=264, bias_shared=False))
     assert run.inp.bias_batch_stride == 2 * 264 * 264
     check_out(run, label="per-batch fp16 bias, aligned rows")
 
@@ -305,7 +305,7 @@ def test_pack_special_values(dt, d):
 def test_given_mu_per_head(name):
     inp = make(name, **REDUCED[name])
     s = inp.spec
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     qm = run.qmu.mean(dim=2, keepdim=True).expand_as(run.qmu).contiguous()
     km = (0.5 * run.kmu.mean(dim=2, keepdim=True)).expand_as(run.kmu).contiguous()
     out = torch.empty_like(run.out)
@@ -325,7 +325,7 @@ def test_given_mu_per_head(name):
 def test_given_mu_zero_no_bias():
     inp = make("dit_256", B=2, H=3, N=200)
     s = inp.spec
-    run = GpuRun(inp)
+    run = DeviceRun(inp)
     z = torch.zeros_like(run.qmu)
     out = torch.empty_like(run.out)
     ba.ba_attention_fwd(run.qbits, z, run.kbits, z, run.vq, run.vscale, run.vsum, None, out)
@@ -363,5 +363,5 @@ def _random_case(i):
 @pytest.mark.parametrize("i", range(24))
 def test_random_shapes(i):
     kw = _random_case(i)
-    run = GpuRun(make("dit_512", **kw))
+    run = DeviceRun(make("dit_512", **kw))
     check_out(run, label=f"random case {i}: {kw}")
