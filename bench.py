@@ -304,7 +304,7 @@ def main() -> int:
                          "times: the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: there is no multi-GPU path "
               "(the attention shards by head with no communication)", file=sys.stderr)
         return 2
     import torch
