@@ -31,6 +31,10 @@ _LIB = os.path.join(_HERE, "libbao_ref.so")
 
 F16, BF16, F32 = 0, 1, 2
 BIAS_NONE, BIAS_DENSE, BIAS_RELPOS = 0, 1, 2
+# Row normaliser of the quantised output (see bao_ref.h): the integer row sum
+# of P (the weights that multiply V; the library's reading) or the float sum
+# of the unquantised probabilities.
+NORM_P8, NORM_FLOAT = 0, 1
 
 
 def build(force: bool = True) -> str:
@@ -85,7 +89,7 @@ def lib():
         L.bao_pack.argtypes = [P, I, I64, I, P, P]
         L.bao_quant_v.argtypes = [P, I, I64, I, I, P, P]
         L.bao_hamming.argtypes = [P, P, I, I, I, I, I, I, P]
-        L.bao_attention_mu.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias), P, P,
+        L.bao_attention_mu.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias), P, P, I,
                                        I, I, I, I, I, P, P, P, P, P, P]
         L.bao_attention_fp_mu.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias), P, P,
                                           I, I, I, I, P, P]
@@ -184,7 +188,8 @@ class AttnResult:
     out: np.ndarray        # float64 [nbh, nrows, d] before output rounding
     out_bits: np.ndarray   # uint16 [nbh, nrows, d] rounded to the output dtype
     m: np.ndarray          # float64 [nbh, nrows] row max of the scores
-    l: np.ndarray          # float64 [nbh, nrows] sum of unquantised exp(s - m)
+    l: np.ndarray          # float64 [nbh, nrows] row normaliser: sum_j p8 / 255 (NORM_P8)
+                           # or sum_j exp(s - m) (NORM_FLOAT)
     acc: np.ndarray        # int64 [nbh, nrows, d] integer P.V accumulator
     p8: np.ndarray | None  # uint8 [nbh, nrows, N] quantised probabilities
 
@@ -199,11 +204,13 @@ def _mu_arg(mu, shape):
 
 
 def attention(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
-              nrows=None, out_dtype=None, want_p8=False, qmu=None, kmu=None) -> AttnResult:
+              nrows=None, out_dtype=None, want_p8=False, qmu=None, kmu=None,
+              norm=NORM_P8) -> AttnResult:
     """Quantised BinaryAttention forward from raw uint16 Q, K, V [B,H,N,d].
 
     qmu, kmu: optional given scales float32 [B,H,N] in place of the per-token
-    mean |x| (mu is an input of the attention step, e.g. a per-head scalar)."""
+    mean |x| (mu is an input of the attention step, e.g. a per-head scalar).
+    norm: NORM_P8 (l = sum_j p8 / 255) or NORM_FLOAT (l = sum_j exp(s - m))."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, H, N, d = q.shape
     qmu, kmu = _mu_arg(qmu, q.shape), _mu_arg(kmu, q.shape)
@@ -219,7 +226,7 @@ def attention(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
     p8 = np.empty((nbh, nrows, N), np.uint8) if want_p8 else None
     cb, keep = _cbias(bias)
     rc = lib().bao_attention_mu(_ptr(q), _ptr(k), _ptr(v), dtype, B, H, N, d, ctypes.byref(cb),
-                                _ptr(qmu), _ptr(kmu), bh0, nbh, row0, nrows, out_dtype, _ptr(out),
+                                _ptr(qmu), _ptr(kmu), norm, bh0, nbh, row0, nrows, out_dtype, _ptr(out),
                                 _ptr(bits), _ptr(m), _ptr(l), _ptr(p8), _ptr(acc))
     del keep
     if rc == -2:

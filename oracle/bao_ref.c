@@ -285,15 +285,21 @@ static void head_release(head_ws* ws) {
  * unnormalised probabilities become unsigned 8-bit over [0,1]
  * (p8 = rne(255 p~)), V is the channel-wise int8 above, P.V is summed in
  * integers and dequantised: O_ic = A_ic * scale_c / (255 * l_i).
- * Reading: l is the float sum of the unquantised p~. */
+ * The pages do not say what l is. Reading (BAO_NORM_P8): the sum of the
+ * dequantised weights that multiply V, l = sum_j p8_ij / 255, i.e. the
+ * integer row sum of P taken beside the integer P.V sum (in FlashAttention2
+ * the normaliser is the sum of the same weights that multiply V); then
+ * 255 l = sum_j p8_ij exactly. BAO_NORM_FLOAT keeps the alternative,
+ * l = sum_j p~_ij, the float sum of the unquantised values. */
 int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      int dtype, int B, int H, int N, int d, const bao_bias* bias,
-                     const float* qmu_in, const float* kmu_in,
+                     const float* qmu_in, const float* kmu_in, int norm,
                      int bh0, int nbh, int row0, int nrows, int out_dtype,
                      double* out_f64, uint16_t* out_bits, double* row_m,
                      double* row_l, uint8_t* p8, int64_t* acc) {
   if (check_args(dtype, B, H, N, d, bias, bh0, nbh, row0, nrows)) return -1;
   if (out_dtype != BAO_F16 && out_dtype != BAO_BF16) return -1;
+  if (norm != BAO_NORM_P8 && norm != BAO_NORM_FLOAT) return -1;
   const int W = bao_words(d);
   int status = 0;
   for (int hh = 0; hh < nbh; ++hh) {
@@ -317,12 +323,16 @@ int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         score_row(qb, qmu, ws.kbits, ws.kmu, W, N, d, bias, b, h, i, s);
         double m, l;
         softmax_row(s, N, pt, &m, &l);
+        int64_t psum = 0; /* sum_j p8_ij */
         for (int j = 0; j < N; ++j) {
           double x = rint(255.0 * pt[j]);
           if (x < 0.0) x = 0.0;
           if (x > 255.0) x = 255.0;
           q8[j] = (uint8_t)x;
+          psum += q8[j];
         }
+        /* 255 * l: the integer row sum of P, or 255 times the float one */
+        const double den = norm == BAO_NORM_P8 ? (double)psum : 255.0 * l;
         for (int c = 0; c < d; ++c) A[c] = 0;
         for (int j = 0; j < N; ++j) {
           const int64_t pj = q8[j];
@@ -336,13 +346,13 @@ int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #pragma omp atomic write
             status = -2;
           }
-          double out = (double)A[c] * (double)ws.vscale[c] / (255.0 * l);
+          double out = (double)A[c] * (double)ws.vscale[c] / den;
           if (out_f64) out_f64[o * d + c] = out;
           if (out_bits) out_bits[o * d + c] = bao_round16(out, out_dtype);
           if (acc) acc[o * d + c] = A[c];
         }
         if (row_m) row_m[o] = m;
-        if (row_l) row_l[o] = l;
+        if (row_l) row_l[o] = den / 255.0;
         if (p8) memcpy(p8 + o * N, q8, (size_t)N);
       }
       free(s); free(pt); free(q8); free(A);
@@ -404,12 +414,12 @@ int bao_attention_fp_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * per-token mean |x| as in bao_pack), e.g. a per-head scalar. */
 int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int dtype, int B, int H, int N, int d, const bao_bias* bias,
-                  int bh0, int nbh, int row0, int nrows, int out_dtype,
+                  int norm, int bh0, int nbh, int row0, int nrows, int out_dtype,
                   double* out_f64, uint16_t* out_bits, double* row_m,
                   double* row_l, uint8_t* p8, int64_t* acc) {
-  return bao_attention_mu(q, k, v, dtype, B, H, N, d, bias, NULL, NULL, bh0, nbh,
-                          row0, nrows, out_dtype, out_f64, out_bits, row_m, row_l,
-                          p8, acc);
+  return bao_attention_mu(q, k, v, dtype, B, H, N, d, bias, NULL, NULL, norm, bh0,
+                          nbh, row0, nrows, out_dtype, out_f64, out_bits, row_m,
+                          row_l, p8, acc);
 }
 
 int bao_attention_fp(const uint16_t* q, const uint16_t* k, const uint16_t* v,

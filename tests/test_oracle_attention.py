@@ -6,7 +6,7 @@ sections 2.1-2.3, nl Methodologie 1-3, it/fr/pt section 2. The pins are:
 brute-force +-1 dot products (numpy matmul) against the XOR/popcount route,
 exhaustive sign patterns for d <= 6, a textbook reduction to softmax(S)V
 (scipy), closed forms of the quantised path (uniform keys, one-hot bias,
-N = 1), invariants (key permutation, per-row bias shift, relpos = dense,
+N = 1, identical V rows), invariants (key permutation, per-row bias shift, relpos = dense,
 rows of P summing to 1) and hand-worked examples in tests/golden/.
 """
 import itertools
@@ -151,10 +151,19 @@ def test_p8_and_acc_from_numpy(oracle_lib):
     near_tie = np.abs(e - np.floor(e) - 0.5) < 1e-9
     assert np.array_equal(r.p8[~near_tie], p8[~near_tie].astype(np.uint8))
     assert np.allclose(r.m, m[..., 0], rtol=0, atol=1e-12)
-    assert np.allclose(r.l, np.exp(S - m).sum(-1), rtol=1e-13)
+    # integer normaliser (the default): the row sums of p8 from numpy
+    assert np.array_equal(r.l * 255.0, r.p8.astype(np.int64).sum(-1).astype(np.float64))
     vq, vs = oracle.quant_v(v16, F16)
     A = r.p8.astype(np.int64) @ vq.reshape(B * H, N, d).astype(np.int64)
     assert np.array_equal(r.acc, A)
+    want = A * vs.reshape(B * H, 1, d).astype(np.float64) / r.p8.astype(np.int64).sum(-1, keepdims=True)
+    assert np.allclose(r.out, want, rtol=1e-14, atol=0)
+    # float normaliser: the unquantised row sums from numpy, same p8 and A
+    rf = oracle.attention(q16, k16, v16, F16, want_p8=True, norm=oracle.NORM_FLOAT)
+    assert np.array_equal(rf.p8, r.p8) and np.array_equal(rf.acc, r.acc)
+    assert np.allclose(rf.l, np.exp(S - m).sum(-1), rtol=1e-13)
+    wantf = A * vs.reshape(B * H, 1, d).astype(np.float64) / (255.0 * np.exp(S - m).sum(-1)[..., None])
+    assert np.allclose(rf.out, wantf, rtol=1e-12, atol=0)
     # dequantised output against the unquantised reference: differs only by
     # quantisation error, far below max|V|/50
     fp, _ = oracle.attention_fp(q16, k16, v16, F16)
@@ -172,11 +181,34 @@ def test_uniform_keys_closed_form(oracle_lib):
     k = np.repeat(rng.standard_normal((B, H, 1, d)).astype(np.float32), N, axis=2)
     v = rng.standard_normal((B, H, N, d)).astype(np.float32)
     q16, k16, v16 = (to_bits(t, BF16) for t in (q, k, v))
-    r = oracle.attention(q16, k16, v16, BF16, want_p8=True)
-    assert np.all(r.p8 == 255) and np.all(r.l == N)
     vq, vs = oracle.quant_v(v16, BF16)
     want = vs.reshape(B * H, 1, d).astype(np.float64) * vq.reshape(B * H, N, d).sum(1, keepdims=True) / N
-    assert np.allclose(r.out, np.broadcast_to(want, r.out.shape), rtol=1e-14, atol=0)
+    for norm in (oracle.NORM_P8, oracle.NORM_FLOAT):
+        r = oracle.attention(q16, k16, v16, BF16, want_p8=True, norm=norm)
+        assert np.all(r.p8 == 255) and np.all(r.l == N)
+        assert np.allclose(r.out, np.broadcast_to(want, r.out.shape), rtol=1e-14, atol=0)
+
+
+def test_constant_v_rows_closed_form(oracle_lib):
+    """Every token carries the same V row: with the integer normaliser the
+    output is a weighted mean of identical dequantised rows whose weights
+    sum to exactly 1, so O_i = v8 * scale exactly for every query, whatever
+    Q, K and the bias are. The float normaliser misses this by
+    sum_j p8 / (255 * sum_j p~), which is not 1."""
+    rng = np.random.default_rng(34)
+    B, H, N, d = 1, 2, 90, 64
+    q = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    v = np.repeat(rng.standard_normal((B, H, 1, d)).astype(np.float32), N, axis=2)
+    bias = (0.5 * rng.standard_normal((H, N, N))).astype(np.float32)
+    q16, k16, v16 = (to_bits(t, F16) for t in (q, k, v))
+    ob = Bias(oracle.BIAS_DENSE, bias, oracle.F32, 0)
+    vq, vs = oracle.quant_v(v16, F16)
+    row = vq[0, :, :1].astype(np.float64) * vs[0, :, None].astype(np.float64)  # [H,1,d]
+    r = oracle.attention(q16, k16, v16, F16, bias=ob)
+    assert np.array_equal(r.out, np.broadcast_to(row, r.out.shape))
+    rf = oracle.attention(q16, k16, v16, F16, bias=ob, norm=oracle.NORM_FLOAT)
+    assert not np.allclose(rf.out, np.broadcast_to(row, rf.out.shape), rtol=1e-6, atol=0)
 
 
 def test_one_hot_bias_closed_form(oracle_lib):
@@ -331,15 +363,22 @@ def test_hand_example_attention(oracle_lib):
     qb, _ = oracle.pack(q16, F16)
     kb, _ = oracle.pack(k16, F16)
     assert oracle.hamming(qb, kb, 4)[0].tolist() == g["sigma"]
+    scale = np.array(g["vscale_num"]) / g["vscale_den"]
+    # integer normaliser: 255 l = row sum of p8
     r = oracle.attention(q16, k16, v16, F16, want_p8=True)
     assert r.p8[0].tolist() == g["p8"]
     assert r.acc[0].tolist() == g["acc"]
     assert np.allclose(r.m[0], g["m"], rtol=0, atol=1e-15)
-    l_hand = np.array([1 + np.exp(-1.96875), 1 + np.exp(-0.046875)])
-    assert np.allclose(r.l[0], l_hand, rtol=1e-15)
-    scale = np.array(g["vscale_num"]) / g["vscale_den"]
-    want = np.array(g["acc"]) * scale[None] / (255.0 * l_hand[:, None])
+    assert (r.l[0] * 255.0).tolist() == g["p8_row_sum"]
+    want = np.array(g["acc"]) * scale[None] / np.array(g["p8_row_sum"], np.float64)[:, None]
     assert np.allclose(r.out[0], want, rtol=1e-6)
+    # float normaliser: l = sum of the unquantised exp(s - m)
+    rf = oracle.attention(q16, k16, v16, F16, want_p8=True, norm=oracle.NORM_FLOAT)
+    assert rf.p8[0].tolist() == g["p8"] and rf.acc[0].tolist() == g["acc"]
+    l_hand = np.array([1 + np.exp(-1.96875), 1 + np.exp(-0.046875)])
+    assert np.allclose(rf.l[0], l_hand, rtol=1e-15)
+    wantf = np.array(g["acc"]) * scale[None] / (255.0 * l_hand[:, None])
+    assert np.allclose(rf.out[0], wantf, rtol=1e-6)
 
 
 def test_rejects_bad_arguments(oracle_lib):
@@ -349,6 +388,8 @@ def test_rejects_bad_arguments(oracle_lib):
     with pytest.raises(ValueError):
         oracle.attention(x, x, x, F16, bias=Bias(oracle.BIAS_RELPOS, np.zeros((1, 9), np.float32),
                                                  oracle.F32, 0, 2, 3, 0))
+    with pytest.raises(ValueError):
+        oracle.attention(x, x, x, F16, norm=2)
 
 
 # ---------------------------------------------------- given scales (mu in) --

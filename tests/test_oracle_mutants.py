@@ -29,7 +29,9 @@ MUTANTS = {
     "v_scale_128": ("const float inv = 127.0f / amax;", "const float inv = 128.0f / amax;"),
     "v_rounds_toward_zero": ("float r = rintf(decode1(v, dtype, base + (int64_t)j * d + c) * inv);",
                              "float r = truncf(decode1(v, dtype, base + (int64_t)j * d + c) * inv);"),
-    "dequant_256": ("/ (255.0 * l);", "/ (256.0 * l);"),
+    "dequant_256": (": 255.0 * l;", ": 256.0 * l;"),
+    "norm_p8_off_by_one": ("? (double)psum :", "? (double)psum + 1.0 :"),
+    "norm_p8_is_float_sum": ("? (double)psum :", "? 255.0 * l :"),
     "pv_channel_reversed": ("A[c] += pj * vj[c];", "A[c] += pj * vj[d - 1 - c];"),
     "l_from_squares": ("pt[j] = exp(s[j] - m); l += pt[j];", "pt[j] = exp(s[j] - m); l += pt[j] * pt[j];"),
     "bf16_decode_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
