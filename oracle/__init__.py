@@ -31,10 +31,10 @@ _LIB = os.path.join(_HERE, "libbao_ref.so")
 
 F16, BF16, F32 = 0, 1, 2
 BIAS_NONE, BIAS_DENSE, BIAS_RELPOS = 0, 1, 2
-# Row normaliser of the quantised output (see bao_ref.h): the integer row sum
-# of P (the weights that multiply V; the library's reading) or the float sum
-# of the unquantised probabilities.
-NORM_P8, NORM_FLOAT = 0, 1
+# Row normaliser of the quantised output (see bao_ref.h): the float sum of
+# the unquantised probabilities (the library's reading) or the integer row sum
+# of the quantised P.
+NORM_FLOAT, NORM_P8 = 0, 1
 
 
 def build(force: bool = True) -> str:
@@ -90,7 +90,7 @@ def lib():
         L.bao_quant_v.argtypes = [P, I, I64, I, I, P, P]
         L.bao_hamming.argtypes = [P, P, I, I, I, I, I, I, P]
         L.bao_attention_mu.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias), P, P, I,
-                                       I, I, I, I, I, P, P, P, P, P, P]
+                                       I, I, I, I, I, P, P, P, P, P, P, P]
         L.bao_attention_fp_mu.argtypes = [P, P, P, I, I, I, I, I, ctypes.POINTER(_Bias), P, P,
                                           I, I, I, I, P, P]
         L.bao_num_threads.restype = I
@@ -149,15 +149,6 @@ def quant_v(v: np.ndarray, dtype: int):
     return vq, vs
 
 
-def channel_sums(vq: np.ndarray) -> np.ndarray:
-    """vq int8 [B,H,N,d] -> int32 [B,H,d]: sum over the tokens of each channel.
-
-    Plain integer sums of the quantised V; the library's fused kernel uses them
-    to undo the 127 - p8 offset of its signed-byte product (the relation
-    sum_j p8_j v_j = 127 * sum_j v_j - sum_j (127 - p8_j) v_j)."""
-    return np.asarray(vq, np.int8).astype(np.int64).sum(axis=2).astype(np.int32)
-
-
 def hamming(qbits, kbits, d, bh0=0, nbh=None, row0=0, nrows=None):
     """qbits, kbits: uint32 [B,H,N,W] -> sigma int32 [nbh, nrows, N]."""
     qbits = np.ascontiguousarray(qbits, np.uint32)
@@ -188,10 +179,11 @@ class AttnResult:
     out: np.ndarray        # float64 [nbh, nrows, d] before output rounding
     out_bits: np.ndarray   # uint16 [nbh, nrows, d] rounded to the output dtype
     m: np.ndarray          # float64 [nbh, nrows] row max of the scores
-    l: np.ndarray          # float64 [nbh, nrows] row normaliser: sum_j p8 / 255 (NORM_P8)
-                           # or sum_j exp(s - m) (NORM_FLOAT)
+    l: np.ndarray          # float64 [nbh, nrows] row normaliser: sum_j exp(s - m) (NORM_FLOAT)
+                           # or sum_j p8 / 255 (NORM_P8)
     acc: np.ndarray        # int64 [nbh, nrows, d] integer P.V accumulator
     p8: np.ndarray | None  # uint8 [nbh, nrows, N] quantised probabilities
+    e255: np.ndarray | None = None  # float64 [nbh, nrows, N]: 255 * exp(s - m), before rounding
 
 
 def _mu_arg(mu, shape):
@@ -205,12 +197,12 @@ def _mu_arg(mu, shape):
 
 def attention(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
               nrows=None, out_dtype=None, want_p8=False, qmu=None, kmu=None,
-              norm=NORM_P8) -> AttnResult:
+              norm=NORM_FLOAT, want_e255=False) -> AttnResult:
     """Quantised BinaryAttention forward from raw uint16 Q, K, V [B,H,N,d].
 
     qmu, kmu: optional given scales float32 [B,H,N] in place of the per-token
     mean |x| (mu is an input of the attention step, e.g. a per-head scalar).
-    norm: NORM_P8 (l = sum_j p8 / 255) or NORM_FLOAT (l = sum_j exp(s - m))."""
+    norm: NORM_FLOAT (l = sum_j exp(s - m)) or NORM_P8 (l = sum_j p8 / 255)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, H, N, d = q.shape
     qmu, kmu = _mu_arg(qmu, q.shape), _mu_arg(kmu, q.shape)
@@ -224,16 +216,17 @@ def attention(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,
     l = np.empty((nbh, nrows), np.float64)
     acc = np.empty((nbh, nrows, d), np.int64)
     p8 = np.empty((nbh, nrows, N), np.uint8) if want_p8 else None
+    e255 = np.empty((nbh, nrows, N), np.float64) if want_e255 else None
     cb, keep = _cbias(bias)
     rc = lib().bao_attention_mu(_ptr(q), _ptr(k), _ptr(v), dtype, B, H, N, d, ctypes.byref(cb),
                                 _ptr(qmu), _ptr(kmu), norm, bh0, nbh, row0, nrows, out_dtype, _ptr(out),
-                                _ptr(bits), _ptr(m), _ptr(l), _ptr(p8), _ptr(acc))
+                                _ptr(bits), _ptr(m), _ptr(l), _ptr(p8), _ptr(acc), _ptr(e255))
     del keep
     if rc == -2:
         raise OverflowError("integer P.V accumulator left int32 range")
     if rc != 0:
         raise ValueError(f"bao_attention rejected its arguments (rc={rc})")
-    return AttnResult(out, bits, m, l, acc, p8)
+    return AttnResult(out, bits, m, l, acc, p8, e255)
 
 
 def attention_fp(q, k, v, dtype, bias: Bias | None = None, bh0=0, nbh=None, row0=0,

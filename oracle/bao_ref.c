@@ -285,18 +285,18 @@ static void head_release(head_ws* ws) {
  * unnormalised probabilities become unsigned 8-bit over [0,1]
  * (p8 = rne(255 p~)), V is the channel-wise int8 above, P.V is summed in
  * integers and dequantised: O_ic = A_ic * scale_c / (255 * l_i).
- * The pages do not say what l is. Reading (BAO_NORM_P8): the sum of the
- * dequantised weights that multiply V, l = sum_j p8_ij / 255, i.e. the
- * integer row sum of P taken beside the integer P.V sum (in FlashAttention2
- * the normaliser is the sum of the same weights that multiply V); then
- * 255 l = sum_j p8_ij exactly. BAO_NORM_FLOAT keeps the alternative,
- * l = sum_j p~_ij, the float sum of the unquantised values. */
+ * The pages do not say what l is. Reading (BAO_NORM_FLOAT): the float sum
+ * of the unquantised values, l = sum_j p~_ij, so the rows of the
+ * real-valued P sum to 1 before quantisation and keys whose p8 rounds to 0
+ * still count in l. BAO_NORM_P8 keeps the alternative l = sum_j p8_ij / 255
+ * (the integer row sum of the quantised weights; then 255 l = sum_j p8_ij
+ * exactly), which renormalises over the keys that survive quantisation. */
 int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      int dtype, int B, int H, int N, int d, const bao_bias* bias,
                      const float* qmu_in, const float* kmu_in, int norm,
                      int bh0, int nbh, int row0, int nrows, int out_dtype,
                      double* out_f64, uint16_t* out_bits, double* row_m,
-                     double* row_l, uint8_t* p8, int64_t* acc) {
+                     double* row_l, uint8_t* p8, int64_t* acc, double* e255) {
   if (check_args(dtype, B, H, N, d, bias, bh0, nbh, row0, nrows)) return -1;
   if (out_dtype != BAO_F16 && out_dtype != BAO_BF16) return -1;
   if (norm != BAO_NORM_P8 && norm != BAO_NORM_FLOAT) return -1;
@@ -354,6 +354,8 @@ int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         if (row_m) row_m[o] = m;
         if (row_l) row_l[o] = den / 255.0;
         if (p8) memcpy(p8 + o * N, q8, (size_t)N);
+        if (e255)
+          for (int j = 0; j < N; ++j) e255[o * N + j] = 255.0 * pt[j];
       }
       free(s); free(pt); free(q8); free(A);
     }
@@ -419,7 +421,7 @@ int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   double* row_l, uint8_t* p8, int64_t* acc) {
   return bao_attention_mu(q, k, v, dtype, B, H, N, d, bias, NULL, NULL, norm, bh0,
                           nbh, row0, nrows, out_dtype, out_f64, out_bits, row_m,
-                          row_l, p8, acc);
+                          row_l, p8, acc, NULL);
 }
 
 int bao_attention_fp(const uint16_t* q, const uint16_t* k, const uint16_t* v,

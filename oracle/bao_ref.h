@@ -30,11 +30,12 @@ enum { BAO_F16 = 0, BAO_BF16 = 1, BAO_F32 = 2 };
 enum { BAO_BIAS_NONE = 0, BAO_BIAS_DENSE = 1, BAO_BIAS_RELPOS = 2 };
 /* The row normaliser l_i that the integer P.V sum is divided by (the pages
  * leave it open):
+ *   BAO_NORM_FLOAT l_i = sum_j exp(s_ij - m_i): the unquantised row sum (the
+ *                  reading the library follows);
  *   BAO_NORM_P8    l_i = (sum_j p8_ij) / 255: the sum of the quantised
- *                  weights that multiply V, so every dequantised row of P
- *                  sums to exactly 1 (the reading the library follows);
- *   BAO_NORM_FLOAT l_i = sum_j exp(s_ij - m_i): the unquantised row sum. */
-enum { BAO_NORM_P8 = 0, BAO_NORM_FLOAT = 1 };
+ *                  weights that multiply V (an alternative: it drops the
+ *                  mass of keys whose p8 rounds to 0 from the normaliser). */
+enum { BAO_NORM_FLOAT = 0, BAO_NORM_P8 = 1 };
 
 typedef struct {
   int kind;              /* BAO_BIAS_*                                        */
@@ -69,9 +70,10 @@ void bao_hamming(const uint32_t* qbits, const uint32_t* kbits, int N, int d,
 /* Quantised BinaryAttention forward for heads [bh0,bh0+nbh) and query rows
  * [row0,row0+nrows), from the raw 16-bit Q, K, V, with the row normaliser
  * `norm` (BAO_NORM_*). Any output pointer may be NULL. Shapes:
- * out_f64/out_bits/acc [nbh,nrows,d]; row_m/row_l [nbh,nrows]; p8
- * [nbh,nrows,N]. Returns 0, or -1 on an argument error, -2 if an integer
- * accumulator would leave int32 range. */
+ * out_f64/out_bits/acc [nbh,nrows,d]; row_m/row_l [nbh,nrows]; p8 and e255
+ * [nbh,nrows,N] (e255: the unrounded 255 * p~ that p8 rounds). Returns 0, or
+ * -1 on an argument error, -2 if an integer accumulator would leave int32
+ * range. */
 int bao_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int dtype, int B, int H, int N, int d, const bao_bias* bias,
                   int norm, int bh0, int nbh, int row0, int nrows, int out_dtype,
@@ -95,7 +97,7 @@ int bao_attention_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const float* qmu_in, const float* kmu_in, int norm,
                      int bh0, int nbh, int row0, int nrows, int out_dtype,
                      double* out_f64, uint16_t* out_bits, double* row_m,
-                     double* row_l, uint8_t* p8, int64_t* acc);
+                     double* row_l, uint8_t* p8, int64_t* acc, double* e255);
 int bao_attention_fp_mu(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int dtype, int B, int H, int N, int d,
                         const bao_bias* bias, const float* qmu_in,
