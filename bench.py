@@ -148,18 +148,17 @@ class Workload:
         self.kmu = torch.empty_like(self.qmu)
         self.vq = torch.empty((B, H, N, d), dtype=torch.int8, device="cuda")
         self.vscale = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
-        self.vsum = torch.empty((B, H, d), dtype=torch.int32, device="cuda")
         self.out = torch.empty_like(self.q)
         self.stream = torch.cuda.current_stream()
 
     def step(self):
         ba = self.ba
         ba.ba_pack_qk_quant_v(self.q, self.k, self.v, self.qbits, self.qmu, self.kbits, self.kmu,
-                              self.vq, self.vscale, self.vsum, self.stream)
+                              self.vq, self.vscale, self.stream)
         self.attn()
 
     def attn(self):
-        self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale, self.vsum,
+        self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
                                  self.bias, self.out, self.stream)
 
     def time(self, fn, iters: int, warmup: int) -> float:

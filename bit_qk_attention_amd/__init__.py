@@ -58,16 +58,16 @@ def lib() -> ctypes.CDLL:
         L.ba_packed_words.restype = I
         L.ba_pack_qk.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P]
         L.ba_pack_qk.restype = I
-        L.ba_quant_v.argtypes = [P, I, I, I, I, I, P, P, P, P]
+        L.ba_quant_v.argtypes = [P, I, I, I, I, I, P, P, P]
         L.ba_quant_v.restype = I
-        L.ba_pack_qk_quant_v.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.ba_pack_qk_quant_v.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]
         L.ba_pack_qk_quant_v.restype = I
         L.ba_pack_qk_quant_v_strided.argtypes = [P, P, P, ctypes.POINTER(ba_strides), I, I, I, I, I,
-                                                 P, P, P, P, P, P, P, P]
+                                                 P, P, P, P, P, P, P]
         L.ba_pack_qk_quant_v_strided.restype = I
-        L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
+        L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
         L.ba_attention_fwd.restype = I
-        L.ba_attention_fwd_strided.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P,
+        L.ba_attention_fwd_strided.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P,
                                                ctypes.POINTER(ba_strides), I, P]
         L.ba_attention_fwd_strided.restype = I
         L.ba_debug_hamming_scores.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
@@ -172,58 +172,57 @@ def ba_pack_qk(q, k, qbits, qmu, kbits, kmu, stream=None) -> None:
                                           _ptr(kbits), _ptr(kmu), _stream(stream)))
 
 
-def ba_quant_v(v, vq, vscale, vsum, stream=None) -> None:
-    """v [B,H,N,d] fp16/bf16 -> vq int8 [B,H,N,d], vscale float32 [B,H,d],
-    vsum int32 [B,H,d] (channel sums of vq)."""
-    _require_gpu(v, vq, vscale, vsum)
+def ba_quant_v(v, vq, vscale, stream=None) -> None:
+    """v [B,H,N,d] fp16/bf16 -> vq int8 [B,H,N,d], vscale float32 [B,H,d]."""
+    _require_gpu(v, vq, vscale)
     B, H, N, d = v.shape
     _check("ba_quant_v", lib().ba_quant_v(_ptr(v), _dt(v), B, H, N, d, _ptr(vq), _ptr(vscale),
-                                          _ptr(vsum), _stream(stream)))
+                                          _stream(stream)))
 
 
-def ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream=None) -> None:
+def ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, stream=None) -> None:
     """ba_pack_qk and ba_quant_v in one call (same outputs, bit for bit)."""
-    _require_gpu(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum)
+    _require_gpu(q, k, v, qbits, qmu, kbits, kmu, vq, vscale)
     B, H, N, d = q.shape
     _check("ba_pack_qk_quant_v", lib().ba_pack_qk_quant_v(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu),
-        _ptr(vq), _ptr(vscale), _ptr(vsum), _stream(stream)))
+        _ptr(vq), _ptr(vscale), _stream(stream)))
 
 
-def ba_pack_qk_quant_v_strided(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream=None) -> None:
+def ba_pack_qk_quant_v_strided(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, stream=None) -> None:
     """ba_pack_qk_quant_v reading q, k, v through [B,H,N,d] views with one
     set of strides (e.g. the head slices of a [B,N,3,H,d] projection)."""
     _require_gpu(q, k, v, contiguous=False)
-    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum)
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale)
     if not (q.shape == k.shape == v.shape and q.stride() == k.stride() == v.stride()):
         raise ValueError("q, k and v must be views of one shape and one set of strides")
     st = view_strides(q)
     B, H, N, d = q.shape
     _check("ba_pack_qk_quant_v_strided", lib().ba_pack_qk_quant_v_strided(
         _ptr(q), _ptr(k), _ptr(v), ctypes.byref(st), _dt(q), B, H, N, d, _ptr(qbits), _ptr(qmu), _ptr(kbits),
-        _ptr(kmu), _ptr(vq), _ptr(vscale), _ptr(vsum), _stream(stream)))
+        _ptr(kmu), _ptr(vq), _ptr(vscale), _stream(stream)))
 
 
-def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream=None) -> None:
+def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream=None) -> None:
     """Fused forward; out [B,H,N,d] fp16/bf16 defines the shape and output dtype."""
-    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum, out)
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, out)
     B, H, N, d = out.shape
     cb = (bias or Bias()).to_c()
     _check("ba_attention_fwd", lib().ba_attention_fwd(
-        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), _ptr(vsum),
+        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale),
         ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
 
 
-def ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream=None) -> None:
+def ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream=None) -> None:
     """ba_attention_fwd writing through ``out``, any [B,H,N,d] view with
     contiguous channels (e.g. ``o.transpose(1, 2)`` of an o [B,N,H,d])."""
-    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, vsum)
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale)
     _require_gpu(out, contiguous=False)
     st = view_strides(out)
     B, H, N, d = out.shape
     cb = (bias or Bias()).to_c()
     _check("ba_attention_fwd_strided", lib().ba_attention_fwd_strided(
-        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), _ptr(vsum),
+        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale),
         ctypes.byref(cb), B, H, N, d, _ptr(out), ctypes.byref(st), _dt(out), _stream(stream)))
 
 
@@ -256,9 +255,8 @@ def quant_v(v, stream=None):
     B, H, N, d = v.shape
     vq = torch.empty((B, H, N, d), dtype=torch.int8, device=v.device)
     vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
-    vsum = torch.empty((B, H, d), dtype=torch.int32, device=v.device)
-    ba_quant_v(v, vq, vscale, vsum, stream)
-    return vq, vscale, vsum
+    ba_quant_v(v, vq, vscale, stream)
+    return vq, vscale
 
 
 def prepare(q, k, v, stream=None):
@@ -273,12 +271,11 @@ def prepare(q, k, v, stream=None):
     kmu = torch.empty_like(qmu)
     vq = torch.empty((B, H, N, d), dtype=torch.int8, device=v.device)
     vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
-    vsum = torch.empty((B, H, d), dtype=torch.int32, device=v.device)
     if q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
-        ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream)
+        ba_pack_qk_quant_v(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, stream)
     else:
-        ba_pack_qk_quant_v_strided(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, vsum, stream)
-    return qbits, qmu, kbits, kmu, vq, vscale, vsum
+        ba_pack_qk_quant_v_strided(q, k, v, qbits, qmu, kbits, kmu, vq, vscale, stream)
+    return qbits, qmu, kbits, kmu, vq, vscale
 
 
 def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
@@ -286,11 +283,11 @@ def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
     q, k, v and out may be strided [B,H,N,d] views (see prepare and
     ba_attention_fwd_strided)."""
     torch = _torch()
-    qbits, qmu, kbits, kmu, vq, vscale, vsum = prepare(q, k, v, stream)
+    qbits, qmu, kbits, kmu, vq, vscale = prepare(q, k, v, stream)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if out.is_contiguous():
-        ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream)
+        ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream)
     else:
-        ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out, stream)
+        ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream)
     return out

@@ -2,6 +2,7 @@
 // argument validation (before any HIP call), dispatch to the gfx950
 // launchers, and status mapping. No C++ exception crosses this layer.
 #include <stdint.h>
+#include <string.h>
 
 #include "common.h"
 
@@ -11,7 +12,18 @@ using namespace binattn;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool dtype16(ba_dtype dt) { return dt == BA_F16 || dt == BA_BF16; }
+// The value a caller passed for an enum argument or field, as an int. C
+// callers may pass any int there; loading such a value as the C++ enum type
+// is undefined, so its bytes are copied out instead.
+template <class E>
+int raw(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "the ABI's enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool dtype16(int dt) { return dt == BA_F16 || dt == BA_BF16; }
 
 // Shape checks shared by every call. Returns BA_OK or the status to report.
 ba_status check_shape(int B, int H, int N, int d) {
@@ -65,66 +77,66 @@ bool view_disjoint(const ba_strides& st, int B, int H, int N, int d) {
 // ba_pack_qk_quant_v on the view `in` (validated here); in_elems = the
 // elements each of q, k, v spans.
 ba_status prepass_checked(const void* q, const void* k, const void* v, const InView& in, int64_t in_elems,
-                          int in_align, ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
-                          uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, int32_t* vsum, void* stream) {
-  if (!q || !k || !v || !qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum) return BA_ERR_INVALID_ARG;
+                          int in_align, int dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
+                          uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, void* stream) {
+  if (!q || !k || !v || !qbits || !qmu || !kbits || !kmu || !vq || !vscale) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
   if (!aligned(q, in_align) || !aligned(k, in_align) || !aligned(v, in_align) || !aligned(qbits, 16) ||
-      !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) ||
-      !aligned(vsum, 4))
+      !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4))
     return BA_ERR_INVALID_ARG;
   const int64_t ntok = (int64_t)B * H * N;
   const int64_t W = (d + 31) / 32;
-  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale, of vsum
-  const void* outs[7] = {qbits, qmu, kbits, kmu, vq, vscale, vsum};
-  const int64_t osz[7] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d, nc, nc};
-  for (int i = 0; i < 7; ++i) {
+  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale
+  const void* outs[6] = {qbits, qmu, kbits, kmu, vq, vscale};
+  const int64_t osz[6] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d, nc};
+  for (int i = 0; i < 6; ++i) {
     if (overlap(outs[i], osz[i], q, in_elems * 2) || overlap(outs[i], osz[i], k, in_elems * 2) ||
         overlap(outs[i], osz[i], v, in_elems * 2))
       return BA_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 7; ++j)
+    for (int j = i + 1; j < 6; ++j)
       if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
   }
-  return from_hip(launch_prepass(q, k, v, dt, in, B * H, N, d, qbits, qmu, kbits, kmu, vq, vscale, vsum,
+  return from_hip(launch_prepass(q, k, v, (ba_dtype)dt, in, B * H, N, d, qbits, qmu, kbits, kmu, vq, vscale,
                                  static_cast<hipStream_t>(stream)));
 }
 
 ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint32_t* kbits, const float* kmu,
-                            const int8_t* vq, const float* vscale, const int32_t* vsum, const ba_bias* bias, int B,
-                            int H, int N, int d, void* out, const ba_strides& ost, int out_align, ba_dtype out_dt,
+                            const int8_t* vq, const float* vscale, const ba_bias* bias, int B,
+                            int H, int N, int d, void* out, const ba_strides& ost, int out_align, int out_dt,
                             void* stream) {
-  if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !vsum || !out) return BA_ERR_INVALID_ARG;
+  if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !out) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (!dtype16(out_dt)) return BA_ERR_UNSUPPORTED;
   if (!aligned(qbits, 16) || !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(out, out_align) ||
-      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(vsum, 4))
+      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4))
     return BA_ERR_INVALID_ARG;
   const int64_t ntok = (int64_t)B * H * N;
   const int64_t W = (d + 31) / 32;
   AttnArgs a = {};
   a.qbits = qbits; a.qmu = qmu; a.kbits = kbits; a.kmu = kmu; a.vq = vq; a.vscale = vscale;
-  a.vsum = vsum;
   a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt;
   a.out_sb = ost.batch; a.out_sh = ost.head; a.out_sn = ost.token;
   a.bias_kind = BA_BIAS_NONE;
   int64_t bias_bytes = 0;
-  if (bias && bias->kind != BA_BIAS_NONE) {
+  const int kind = bias ? raw(bias->kind) : BA_BIAS_NONE;
+  const int bdt = bias ? raw(bias->dtype) : BA_F32;
+  if (kind != BA_BIAS_NONE) {
     if (!bias->data) return BA_ERR_INVALID_ARG;
-    if (bias->kind == BA_BIAS_DENSE) {
-      if (bias->dtype != BA_F32 && bias->dtype != BA_F16) return BA_ERR_UNSUPPORTED;
+    if (kind == BA_BIAS_DENSE) {
+      if (bdt != BA_F32 && bdt != BA_F16) return BA_ERR_UNSUPPORTED;
       const int64_t slice = (int64_t)H * N * N;
       if (bias->batch_stride != 0 && bias->batch_stride < slice) return BA_ERR_INVALID_ARG;
-      const int esz = bias->dtype == BA_F32 ? 4 : 2;
+      const int esz = bdt == BA_F32 ? 4 : 2;
       if (!aligned(bias->data, esz)) return BA_ERR_INVALID_ARG;
       bias_bytes = ((int64_t)(B - 1) * bias->batch_stride + slice) * esz;
       a.bias_kind = BA_BIAS_DENSE;
-      a.bias_dtype = bias->dtype;
+      a.bias_dtype = bdt;
       a.bias_bstride = bias->batch_stride;
-    } else if (bias->kind == BA_BIAS_RELPOS) {
-      if (bias->dtype != BA_F32) return BA_ERR_UNSUPPORTED;
+    } else if (kind == BA_BIAS_RELPOS) {
+      if (bdt != BA_F32) return BA_ERR_UNSUPPORTED;
       if (bias->grid_h < 1 || bias->grid_w < 1 || bias->n_prefix < 0) return BA_ERR_INVALID_ARG;
       if (bias->grid_w > 256) return BA_ERR_UNSUPPORTED;  // table window must fit LDS
       if ((int64_t)bias->n_prefix + (int64_t)bias->grid_h * bias->grid_w != N) return BA_ERR_INVALID_ARG;
@@ -138,10 +150,10 @@ ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint3
     a.bias = bias->data;
   }
   const int64_t out_bytes = view_extent(ost, B, H, N, d) * 2;
-  const void* ins[8] = {qbits, qmu, kbits, kmu, vq, vscale, vsum, a.bias};
-  const int64_t isz[8] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
-                          (int64_t)B * H * d * 4, (int64_t)B * H * d * 4, bias_bytes};
-  for (int i = 0; i < 8; ++i)
+  const void* ins[7] = {qbits, qmu, kbits, kmu, vq, vscale, a.bias};
+  const int64_t isz[7] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
+                          (int64_t)B * H * d * 4, bias_bytes};
+  for (int i = 0; i < 7; ++i)
     if (overlap(out, out_bytes, ins[i], isz[i])) return BA_ERR_INVALID_ARG;
   return from_hip(launch_attention(a, static_cast<hipStream_t>(stream)));
 }
@@ -153,7 +165,7 @@ extern "C" {
 int ba_packed_words(int d) { return d < 1 ? 0 : (d + 31) / 32; }
 
 const char* ba_status_string(ba_status s) {
-  switch (s) {
+  switch (raw(s)) {
     case BA_OK: return "ok";
     case BA_ERR_INVALID_ARG: return "invalid argument";
     case BA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
@@ -167,7 +179,7 @@ ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H, in
   if (!q || !k || !qbits || !qmu || !kbits || !kmu) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
-  if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
+  if (!dtype16(raw(dt))) return BA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(qbits, 16) || !aligned(kbits, 16) ||
       !aligned(qmu, 4) || !aligned(kmu, 4))
     return BA_ERR_INVALID_ARG;
@@ -186,39 +198,32 @@ ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H, in
 }
 
 ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d, int8_t* vq,
-                     float* vscale, int32_t* vsum, void* stream) {
-  if (!v || !vq || !vscale || !vsum) return BA_ERR_INVALID_ARG;
+                     float* vscale, void* stream) {
+  if (!v || !vq || !vscale) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
-  if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
-  if (!aligned(v, 16) || !aligned(vq, 16) || !aligned(vscale, 4) || !aligned(vsum, 4))
-    return BA_ERR_INVALID_ARG;
+  if (!dtype16(raw(dt))) return BA_ERR_UNSUPPORTED;
+  if (!aligned(v, 16) || !aligned(vq, 16) || !aligned(vscale, 4)) return BA_ERR_INVALID_ARG;
   const int64_t n = (int64_t)B * H * N * d;
-  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale, of vsum
-  const void* outs[3] = {vq, vscale, vsum};
-  const int64_t osz[3] = {n, nc, nc};
-  for (int i = 0; i < 3; ++i) {
-    if (overlap(outs[i], osz[i], v, 2 * n)) return BA_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 3; ++j)
-      if (overlap(outs[i], osz[i], outs[j], osz[j])) return BA_ERR_INVALID_ARG;
-  }
-  return from_hip(launch_quant_v(v, dt, dense_view(H, N, d), B * H, N, d, vq, vscale, vsum,
+  const int64_t nc = (int64_t)B * H * d * 4;  // bytes of vscale
+  if (overlap(vq, n, v, 2 * n) || overlap(vscale, nc, v, 2 * n) || overlap(vq, n, vscale, nc))
+    return BA_ERR_INVALID_ARG;
+  return from_hip(launch_quant_v(v, dt, dense_view(H, N, d), B * H, N, d, vq, vscale,
                                  static_cast<hipStream_t>(stream)));
 }
 
 ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dtype dt, int B, int H,
                              int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu,
-                             int8_t* vq, float* vscale, int32_t* vsum, void* stream) {
+                             int8_t* vq, float* vscale, void* stream) {
   const ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
-  return prepass_checked(q, k, v, dense_view(H, N, d), (int64_t)B * H * N * d, 16, dt, B, H, N, d, qbits, qmu,
-                         kbits, kmu, vq, vscale, vsum, stream);
+  return prepass_checked(q, k, v, dense_view(H, N, d), (int64_t)B * H * N * d, 16, raw(dt), B, H, N, d, qbits, qmu,
+                         kbits, kmu, vq, vscale, stream);
 }
 
 ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v, const ba_strides* in_strides,
                                      ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
-                                     uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, int32_t* vsum,
-                                     void* stream) {
+                                     uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, void* stream) {
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (!strides_valid(in_strides, B, H, N)) return BA_ERR_INVALID_ARG;
@@ -229,31 +234,31 @@ ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v
   in.H = H;
   in.vec = d % 8 == 0 && in.sb % 8 == 0 && in.sh % 8 == 0 && in.sn % 8 == 0 && aligned(q, 16) &&
            aligned(k, 16) && aligned(v, 16);
-  return prepass_checked(q, k, v, in, view_extent(*in_strides, B, H, N, d), 2, dt, B, H, N, d, qbits, qmu, kbits,
-                         kmu, vq, vscale, vsum, stream);
+  return prepass_checked(q, k, v, in, view_extent(*in_strides, B, H, N, d), 2, raw(dt), B, H, N, d, qbits, qmu, kbits,
+                         kmu, vq, vscale, stream);
 }
 
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,
                            const float* kmu, const int8_t* vq, const float* vscale,
-                           const int32_t* vsum, const ba_bias* bias, int B, int H, int N,
+                           const ba_bias* bias, int B, int H, int N,
                            int d, void* out, ba_dtype out_dt, void* stream) {
   // head and token strides of a dense output (N * d <= 2^23) fit 32 bits
   const ba_strides dense = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
-  return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, B, H, N, d, out, dense, 16, out_dt,
+  return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, bias, B, H, N, d, out, dense, 16, raw(out_dt),
                            stream);
 }
 
 ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,
                                    const float* kmu, const int8_t* vq, const float* vscale,
-                                   const int32_t* vsum, const ba_bias* bias, int B, int H, int N,
+                                   const ba_bias* bias, int B, int H, int N,
                                    int d, void* out, const ba_strides* out_strides, ba_dtype out_dt,
                                    void* stream) {
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (!strides_valid(out_strides, B, H, N) || !view_disjoint(*out_strides, B, H, N, d)) return BA_ERR_INVALID_ARG;
   if (out_strides->head > 0x7FFFFFFF || out_strides->token > 0x7FFFFFFF) return BA_ERR_UNSUPPORTED;
-  return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, B, H, N, d, out, *out_strides, 2,
-                           out_dt, stream);
+  return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, bias, B, H, N, d, out, *out_strides, 2,
+                           raw(out_dt), stream);
 }
 
 ba_status ba_debug_hamming_scores(const uint32_t* qbits, const uint32_t* kbits, int B, int H,

@@ -34,10 +34,17 @@
 //    int8 MFMA is signed x signed and p8 reaches 255, so the product uses
 //    the signed byte 127 - p8 (= p8 XOR 0x7F): the accumulator ends at
 //    sum_j (127 - p8_j) v8_j, and sum_j p8_j v8_j = 127 * vsum - that, with
-//    vsum the channel sums of v8 (from the V quantisation). Exact in int32.
+//    vsum the channel sums of v8. The kernel forms vsum itself from the V^T
+//    operand it already holds (one v_dot4 per 4 keys, each wave taking a
+//    quarter of the key blocks). Exact in int32.
 //  * Softmax in base 2: x = s*log2(e) - m*log2(e) + log2(255), so a single
 //    v_exp_f32 gives 255*exp(s - m); v_cvt_pk_u8_f32 rounds to nearest even
-//    and clamps to [0, 255].
+//    and clamps to [0, 255]. The row normaliser is the float sum of the
+//    unquantised values (so the mass of keys whose p8 rounds to 0 still
+//    counts).
+//  * A sigma mode of the same kernel writes the integer similarity that its
+//    Q.K path produces (the staged-tile route, the raw-word route and the
+//    pass-1 route straight from global memory), for inspection.
 #include "common.h"
 
 namespace binattn {
@@ -59,6 +66,20 @@ constexpr int kTblMax = 2048;      // floats of relative-position window per til
 enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3, BIAS_DENSE_ANY = 4,
        BIAS_RELPOS_ROW = 5 };
 constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_RELPOS_ROW; }
+
+// What the kernel produces. MODE_ATTN: the attention output. The sigma
+// modes (no bias, no softmax) produce the integer similarity of a window of
+// query rows, each through one Q.K route of the attention:
+//  MODE_SIGMA       the staged-tile route (K words DMA'd into LDS and
+//                   expanded to fp4 once per tile), written out;
+//  MODE_SIGMA_RAW   the raw-word route (each wave expands the staged words
+//                   itself, as with the fp16 dense bias at 65..96 channels);
+//  MODE_SIGMA_SPLIT the pass-1 route without a bias (K words straight from
+//                   global memory into registers, four query groups);
+// the last two compare their result with what is already in the output and
+// overwrite every element that differs with kSigmaPoison.
+enum { MODE_ATTN = 0, MODE_SIGMA = 1, MODE_SIGMA_RAW = 2, MODE_SIGMA_SPLIT = 3 };
+constexpr int32_t kSigmaPoison = 0x7FFFFFFF;  // never a similarity (|sigma| <= 128)
 
 // Workgroups per CU the register allocation must allow (4 waves each; 2 ->
 // up to 256 VGPRs per wave, 3 -> 168, 4 -> 128), per instantiation, from
@@ -88,7 +109,6 @@ struct Params {
   const float* kmu;
   const int8_t* vq;
   const float* vscale;
-  const int32_t* vsum;
   const void* bias;
   int64_t bias_bstride;
   int grid_h, grid_w, n_prefix;
@@ -107,6 +127,10 @@ struct Params {
   int64_t out_sb;              // element strides of the output's [B, H, N, d] view
   int out_sh, out_sn;
   void* out;
+  // sigma modes: query rows [row0, row0 + nrows) of each head are written to
+  // sigma[head][row - row0][key]; the workgroups cover query blocks qb0 ..
+  int32_t* sigma;
+  int row0, nrows, qb0;
 };
 
 // fp4 expansion of 32 sign bits. Dword m (0..3) holds the channels
@@ -216,15 +240,16 @@ struct VStage {
 // target occupancy allows, else two (one tile ahead).
 // fp16 dense bias with three channel blocks: the waves expand the raw K
 // words themselves (no fp4 copy in LDS), so that three workgroups fit a CU
-template <int NCB, int BIAS>
+template <int NCB, int BIAS, int MODE>
 constexpr bool raw_k() {
-  return BIAS == BIAS_DENSE_F16 && NCB == 3;
+  return (BIAS == BIAS_DENSE_F16 && NCB == 3) || MODE == MODE_SIGMA_RAW;
 }
-template <int NKB, int NCB, int BIAS>
+template <int NKB, int NCB, int BIAS, int MODE>
 struct StageCfg {
-  static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS>()>);
+  static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS, MODE>()>);
   static constexpr int VSZ = (int)sizeof(VStage<NCB>);
-  static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS>() - 2048;  // less the pass-1 reduction buffer
+  // less the pass-1 reduction buffer and the channel sums
+  static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS>() - 2048 - 512;
   static constexpr int NS2 = 3 * KS + 3 * VSZ <= BUDGET ? 3 : 2;
   static constexpr int NS1 = 3 * KS + NS2 * VSZ <= BUDGET ? 3 : 2;
 };
@@ -234,13 +259,14 @@ struct StageCfg {
 // 16-byte bank groups.
 __device__ __forceinline__ int bswz(int row) { return (row ^ (row >> 3)) & 7; }
 
-template <int NKB, int NCB, int BIAS>
+template <int NKB, int NCB, int BIAS, int MODE>
 __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kernel(Params p) {
-  constexpr bool RAWK = raw_k<NCB, BIAS>();
+  constexpr bool RAWK = raw_k<NCB, BIAS, MODE>();
   static_assert(!RAWK || NKB == 2, "raw K words: four per key");
+  static_assert(MODE == MODE_ATTN || BIAS == BIAS_NONE, "the sigma modes take no bias");
   using KS = KeyStage<NKB, BIAS, RAWK>;
   using VSt = VStage<NCB>;
-  using Cfg = StageCfg<NKB, NCB, BIAS>;
+  using Cfg = StageCfg<NKB, NCB, BIAS, MODE>;
   constexpr int KROW = KS::KROW, VS = VSt::VS;
   constexpr int NS1 = Cfg::NS1, NS2 = Cfg::NS2;
   constexpr bool DENSE = BIAS == BIAS_DENSE_F32 || BIAS == BIAS_DENSE_F16 || BIAS == BIAS_DENSE_ANY;
@@ -249,6 +275,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   // would touch half-used 128-byte lines)
   constexpr bool P1_SPLIT = BIAS == BIAS_NONE;
   __shared__ float p1red[4][4][kQW];  // per-wave partial row maxima (pass 1 split)
+  __shared__ int32_t vtot[32 * NCB];  // channel sums of v8 over the head's keys
   __shared__ __attribute__((aligned(16))) KS ks0;
   __shared__ __attribute__((aligned(16))) KS ks1;
   __shared__ __attribute__((aligned(16))) KS ks2;
@@ -288,7 +315,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     qb = r % p.nqb;
     h = r / p.nqb;
   } else {
-    qb = u % p.nqb;
+    qb = p.qb0 + u % p.nqb;
     const int r = u / p.nqb;
     h = r % p.H;
     b = r / p.H;
@@ -318,12 +345,35 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   };
   v8i qop[NKB];
   q_operand(qi, qvalid, qop);
-  const float qmu = qvalid ? p.qmu[bh * N + qi] : 0.0f;
+  // (the sigma modes take no scales)
+  const float qmu = (MODE == MODE_ATTN && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
   const float c0 = qmu * p.inv_sqrt_d;  // natural-log units (bias path)
   const float cq = c0 * kLog2e;         // base-2 units (no-bias path)
 
   const int ntiles = (N + kBC - 1) / kBC;
   const bool ragged = (N % kBC) != 0;
+  if (MODE == MODE_ATTN && tid < 32 * NCB) vtot[tid] = 0;
+
+  // sigma modes: this lane's 16 similarities of query q, keys key0 .. key0 +
+  // 15 (those < N), written (CHECK false) or compared with the output, an
+  // element that differs being overwritten with kSigmaPoison (CHECK true)
+  auto put_sigma = [&](auto check, int q, int key0, const v16f& sg) {
+    constexpr bool CHECK = decltype(check)::value;
+    if (q < p.row0 || q >= p.row0 + p.nrows) return;
+    int32_t* row = p.sigma + ((int64_t)bh * p.nrows + (q - p.row0)) * N;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + i;
+      if (key < N) {
+        const int32_t sv = (int32_t)sg[i];  // an exact integer
+        if constexpr (CHECK) {
+          if (row[key] != sv) row[key] = kSigmaPoison;
+        } else {
+          row[key] = sv;
+        }
+      }
+    }
+  };
 
   // ---- relative-position bookkeeping ----
   const int gh = p.grid_h, gw = p.grid_w, npre = p.n_prefix;
@@ -492,7 +542,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16, v_src[i],
                                                    j0 * d, 0, 0);
     }
-    if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * lane, 4 * j0, 0, 0);
+    if (MODE == MODE_ATTN && wave == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * lane, 4 * j0, 0, 0);
     dma_tbl(t, bufc);
     stage_koff(t, bufc);
     __builtin_amdgcn_sched_barrier(0);
@@ -545,7 +596,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         copy_v_checked(t, bufc);
       }
     }
-    if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * (lane + j0), 0, 0, 0);
+    if (MODE == MODE_ATTN && wave == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * (lane + j0), 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kbits, (lptr_t*)(sb.kraw + 64 * wave), 4, kw_src + 4 * j0 * W, 0,
                                              0, 0);
     dma_tbl(t, bufc);
@@ -849,6 +901,20 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       else if constexpr (NS == 3) tail(IntC<2>());
     }
   };
+  if constexpr (MODE == MODE_SIGMA || MODE == MODE_SIGMA_RAW) {
+    // the Q.K of every staged tile, as pass 2 forms it, written out
+    // (MODE_SIGMA) or compared (MODE_SIGMA_RAW, after MODE_SIGMA wrote it)
+    auto sigma_tile = [&](auto tail, int t, auto bufc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u4v a[NKB];
+        k_operand(bufc, kb, a);
+        put_sigma(BoolC<MODE == MODE_SIGMA_RAW>(), qi, t * kBC + kb * 32 + 16 * g, qk_mfma(a));
+      }
+    };
+    run_pass(IntC<Cfg::NS2>(), false, sigma_tile);
+    return;
+  }
   float mrun;
   if constexpr (P1_SPLIT) {
     // Pass 1 splits the keys, not the queries, over the waves: wave w takes
@@ -864,7 +930,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     for (int q = 0; q < 4; ++q) {
       const int qq = qb * kQB + kQW * q + ql;
       q_operand(qq, qq < N, qop4[q]);
-      c04[q] = qq < N ? p.qmu[bh * N + qq] * p.inv_sqrt_d : 0.0f;
+      c04[q] = (MODE == MODE_ATTN && qq < N) ? p.qmu[bh * N + qq] * p.inv_sqrt_d : 0.0f;
     }
     struct Blk {
       uint32_t kw[NKB];
@@ -882,6 +948,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         const int w = 2 * kk + g;
         r.kw[kk] = w < W ? p.kbits[(bh * N + myk) * W + w] : 0u;
       }
+      if constexpr (MODE != MODE_ATTN) return;  // the sigma modes take no scales
       if (p.mk_vec) {
         const float4* src = reinterpret_cast<const float4*>(kmu_bh + k0 + 16 * g);
 #pragma unroll
@@ -910,6 +977,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         const int w = 2 * kk + g;
         r.kw[kk] = w < W ? p.kbits[(bh * N + myk) * W + w] : 0u;
       }
+      if constexpr (MODE != MODE_ATTN) return;
       float mv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) mv[i] = kmu_bh[min(k0 + 16 * g + i, N - 1)];
@@ -946,6 +1014,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk)
           sg = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kk], qop4[q][kk], sg, 4, 4, 0, 0, 0, 0);
+        if constexpr (MODE == MODE_SIGMA_SPLIT) {
+          put_sigma(BoolC<true>(), qb * kQB + kQW * q + ql, jb, sg);
+          continue;
+        }
         float sc[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -990,6 +1062,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       load_blk_tail(nfb, rt);
       comp_blk(BoolC<true>(), nfb, rt);
     }
+    if constexpr (MODE == MODE_SIGMA_SPLIT) return;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v = fmaxf(mx[q][0], mx[q][1]);
@@ -1008,8 +1081,11 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const float negm = __builtin_fmaf(-scale2, mrun, kLog2_255);
 
   // ================= pass 2: u8 P, row sum, integer P.V =================
-  float l0 = 0.0f, l1 = 0.0f, l2 = 0.0f, l3 = 0.0f;
-  v16i acc[NCB];  // ends at sum_j (127 - p8_j) v8_j
+  float l0 = 0.0f, l1 = 0.0f, l2 = 0.0f, l3 = 0.0f;  // 255 * row sum of exp(s - m)
+  v16i acc[NCB];      // ends at sum_j (127 - p8_j) v8_j
+  int vsacc[NCB];     // channel 32 cb + lane % 32: sum of v8 over this wave's key blocks
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) vsacc[cb] = 0;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = (v16i){};
   // transposing-read address of this lane for the V^T operand: row
@@ -1018,8 +1094,20 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const int tr_row = 16 * (lane >> 5) + ((lane & 15) >> 1);
   const int tr_col = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 
-  // u8 probabilities of one key block, as the s8 MFMA operand 127 - p8.
-  // Tail keys (past N) are masked after the scaling: -inf * 0 would be NaN.
+  // byte masks of this lane's 16 keys of block kb in tile t (dword r, byte
+  // e: key 16 g + 4 r + e), set where the key is < N
+  auto key_keep = [&](int t, int kb, uint32_t* keep) {
+    const int jb = t * kBC + kb * 32 + 16 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      keep[r] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keep[r] |= (jb + 4 * r + e < N ? 0xFFu : 0u) << (8 * e);
+    }
+  };
+  // u8 probabilities of one key block, as the s8 MFMA operand 127 - p8, and
+  // the float row sum. Tail keys (past N) are masked after the scaling:
+  // -inf * 0 would be NaN.
   auto probs = [&](auto tail, int t, int kb, float* sc) -> v4i {
     constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
@@ -1046,17 +1134,30 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     }
     if (TAIL) {
       // keys past N: operand 0, so the (unused) V rows staged for them add
-      // nothing
-      const int jb = t * kBC + kb * 32 + 16 * g;
+      // nothing (their p8 is already 0: exp2(-inf))
+      uint32_t keep[4];
+      key_keep(t, kb, keep);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t keep = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) keep |= (jb + 4 * r + e < N ? 0xFFu : 0u) << (8 * e);
-        pw[r] &= keep;
-      }
+      for (int r = 0; r < 4; ++r) pw[r] &= keep[r];
     }
     return (v4i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+  };
+  // Channel sums of v8 from the V^T operand of key block kb of tile t: lane
+  // l holds channel 32 cb + l % 32 of the keys 16 (l / 32) .. + 15, so four
+  // v_dot4 against 0x01010101 add them. Wave w takes the blocks whose index
+  // over the head is w mod 4 (a uniform branch); the waves' sums meet in
+  // LDS after the pass. Tail keys past N are masked: their V rows in LDS are
+  // stale.
+  auto vsum_blk = [&](auto tail, int t, int kb, const v4i* vt) {
+    constexpr bool TAIL = decltype(tail)::value;
+    if (((2 * t + kb) & 3) != wave) return;
+    uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
+    if (TAIL) key_keep(t, kb, keep);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vsacc[cb] = __builtin_amdgcn_sdot4((int)((uint32_t)vt[cb][r] & keep[r]), 0x01010101, vsacc[cb], false);
   };
   // V^T operand (NCB x 16 bytes per lane) of key block kb, read from LDS
   auto read_vt = [&](auto bufc, int kb, v4i* vt) {
@@ -1103,6 +1204,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     pv_regs(vt_held, p_held);
     v4i vt0[NCB];
     read_vt(bufc, 0, vt0);
+    vsum_blk(tail, t, 0, vt0);
+    __builtin_amdgcn_sched_barrier(0);
     const v4i p0 = probs2(tail, t, bufc, 0, sig0);
 #pragma unroll
     for (int i = 0; i < NKB + NCB; ++i) {
@@ -1118,11 +1221,12 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
-    // block 1's probabilities (and the row sums) are consumed only in the
+    // block 1's probabilities (and the row sum) are consumed only in the
     // next tile: pin their computation here, beside block 0's P.V, rather
     // than let it sink past the end-of-tile wait
     asm volatile("" ::"v"(p_held), "v"(l0), "v"(l1), "v"(l2), "v"(l3));
     __builtin_amdgcn_sched_barrier(0);
+    vsum_blk(tail, t, 1, vt_held);
   };
 
   // Lean tile: the two key blocks one after the other, nothing carried
@@ -1140,6 +1244,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       v4i vt[NCB];
       read_vt(bufc, kb, vt);
       pv_regs(vt, pk);
+      vsum_blk(tail, t, kb, vt);
     }
   };
   constexpr bool LEAN = (NCB == 3 && min_blocks<NCB, BIAS>() == 3) || min_blocks<NCB, BIAS>() == 4;
@@ -1152,18 +1257,26 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   }
 
   // ================= epilogue =================
-  float lrun = (l0 + l1) + (l2 + l3);
+  // the channel sums: lanes l and l ^ 32 hold the two halves of each
+  // block's keys; the four waves' sums meet in LDS (zeroed at the start)
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int v = vsacc[cb] + (int)__float_as_uint(partner32(__uint_as_float((uint32_t)vsacc[cb]), lane));
+    if (g == 0) atomicAdd(&vtot[32 * cb + ql], v);
+  }
+  __syncthreads();
+  float lrun = (l0 + l1) + (l2 + l3);  // 255 l over both halves of the keys
   lrun += partner32(lrun, lane);
   if (!qvalid) return;
   const float inv_l = 1.0f / lrun;
   uint16_t* outp = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)h * p.out_sh + (int64_t)qi * p.out_sn;
   const float* vs = p.vscale + bh * d;
-  const int32_t* vsm = p.vsum + bh * d;
+  const int32_t* vsm = vtot;
   if (p.out_mode & 2) {
     // whole groups of 4 channels: channel parameters at fixed offsets from
     // this lane's base, two elements per packed 16-bit conversion (rounding
     // to nearest even, as the scalar conversions); |vsum| <= 127 N < 2^23,
-    // so 127 vsum is a 24-bit multiply
+    // so 127 vsum is a 24-bit multiply. x = A * scale / (255 l).
     const float* vsl = vs + 4 * g;
     const int32_t* vsml = vsm + 4 * g;
     uint16_t* outl = outp + 4 * g;
@@ -1207,9 +1320,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   }
 }
 
-template <int NKB, int NCB, int BIAS>
+template <int NKB, int NCB, int BIAS, int MODE = MODE_ATTN>
 hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<NKB, NCB, BIAS>), dim3(nblocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<NKB, NCB, BIAS, MODE>), dim3(nblocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1227,10 +1340,24 @@ hipError_t launch_bias(const Params& p, int bias, int nblocks, hipStream_t s) {
 
 }  // namespace
 
+// Sigma modes for one window (the pointers already offset to its first
+// head, which the kernel sees as batch 0, heads 0 .. H - 1): the staged-tile
+// route writes every element, then the pass-1 route (and, at three channel
+// blocks, the raw-word route) compares and poisons what differs.
+template <int NKB, int NCB>
+hipError_t launch_sigma_routes(const Params& p, int nblocks, hipStream_t s) {
+  hipError_t e = launch_t<NKB, NCB, BIAS_NONE, MODE_SIGMA>(p, nblocks, s);
+  if (e == hipSuccess) e = launch_t<NKB, NCB, BIAS_NONE, MODE_SIGMA_SPLIT>(p, nblocks, s);
+  if constexpr (NCB == 3) {
+    if (e == hipSuccess) e = launch_t<NKB, NCB, BIAS_NONE, MODE_SIGMA_RAW>(p, nblocks, s);
+  }
+  return e;
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  Params p;
+  Params p = {};
   p.qbits = a.qbits; p.qmu = a.qmu; p.kbits = a.kbits; p.kmu = a.kmu;
-  p.vq = a.vq; p.vscale = a.vscale; p.vsum = a.vsum;
+  p.vq = a.vq; p.vscale = a.vscale;
   p.bias = a.bias; p.bias_bstride = a.bias_bstride;
   p.grid_h = a.grid_h; p.grid_w = a.grid_w; p.n_prefix = a.n_prefix;
   p.gw_magic = a.grid_w >= 2 ? (uint32_t)(((1ull << 32) + (uint64_t)a.grid_w - 1) / (uint64_t)a.grid_w) : 0u;
@@ -1272,6 +1399,29 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     case 2: return launch_bias<1, 2>(p, bias, (int)nblocks, s);
     case 3: return launch_bias<2, 3>(p, bias, (int)nblocks, s);
     default: return launch_bias<2, 4>(p, bias, (int)nblocks, s);
+  }
+}
+
+hipError_t launch_hamming(const uint32_t* qbits, const uint32_t* kbits, int N, int d, int bh_begin, int bh_count,
+                          int row_begin, int row_count, int32_t* sigma, hipStream_t s) {
+  Params p = {};
+  const int W = (d + 31) / 32;
+  p.qbits = qbits + (int64_t)bh_begin * N * W;
+  p.kbits = kbits + (int64_t)bh_begin * N * W;
+  p.B = 1; p.H = bh_count; p.N = N; p.d = d; p.W = W;
+  p.inv_sqrt_d = 1.0f;
+  p.v_swz_shift = -1;
+  p.sigma = sigma;
+  p.row0 = row_begin; p.nrows = row_count;
+  p.qb0 = row_begin / kQB;
+  p.nqb = (row_begin + row_count - 1) / kQB - p.qb0 + 1;
+  const int64_t nblocks = (int64_t)p.nqb * bh_count;
+  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch ((d + 31) / 32) {
+    case 1: return launch_sigma_routes<1, 1>(p, (int)nblocks, s);
+    case 2: return launch_sigma_routes<1, 2>(p, (int)nblocks, s);
+    case 3: return launch_sigma_routes<2, 3>(p, (int)nblocks, s);
+    default: return launch_sigma_routes<2, 4>(p, (int)nblocks, s);
   }
 }
 

@@ -65,14 +65,17 @@ struct InView {
 };
 InView dense_view(int H, int N, int d);
 
+// zero, nzero: a buffer of nzero words the packing launch also zeroes
 hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InView& in, int nbh, int N,
                           int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
-                          float* kmu, hipStream_t s);
+                          float* kmu, hipStream_t s, uint32_t* zero = nullptr, int64_t nzero = 0);
 hipError_t launch_quant_v(const void* v, ba_dtype dt, const InView& in, int nbh, int N, int d,
-                          int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s);
+                          int8_t* vq, float* vscale, hipStream_t s);
 hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, const InView& in, int nbh,
                           int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
-                          float* vscale, int32_t* vsum, hipStream_t s);
+                          float* vscale, hipStream_t s);
+// The integer similarity of a window, computed by the attention kernel's own
+// Q.K routes (attention.hip).
 hipError_t launch_hamming(const uint32_t* qbits, const uint32_t* kbits, int N,
                           int d, int bh_begin, int bh_count, int row_begin,
                           int row_count, int32_t* sigma, hipStream_t s);
@@ -84,7 +87,6 @@ struct AttnArgs {
   const float* kmu;
   const int8_t* vq;
   const float* vscale;
-  const int32_t* vsum;     // channel sums of vq
   int bias_kind;           // ba_bias_kind
   const void* bias;
   int bias_dtype;          // dense: BA_F32 / BA_F16

@@ -1,13 +1,11 @@
 // prepass.hip — gfx950 kernels for the steps before the fused attention:
-// sign/scale packing of Q and K, channel-wise int8 quantisation of V, and
-// the integer Hamming-score debug view.
+// sign/scale packing of Q and K and channel-wise int8 quantisation of V.
 //
 // Method: BinaryAttention (gist.science summaries). Scaled binary Q/K: zh
 // technical summary section 2.2 item 1 (nl Methodologie 2, it/fr/pt section
 // 2B). Channel-wise 8-bit V: zh section 2.2 item 3 (nl Methodologie 2).
-// Hamming similarity: zh sections 2.1 and 2.2 item 1.
 //
-// All three are memory-bound; the kernels aim at coalesced 16-byte accesses
+// Both are memory-bound; the kernels aim at coalesced 16-byte accesses
 // and an XCD-aware block order where blocks share cache lines.
 #include <algorithm>
 
@@ -122,13 +120,16 @@ __device__ __forceinline__ void pack_block(const uint16_t* __restrict__ x, int64
 
 // Dense inputs: the blocks take consecutive runs of the B*H*N tokens. A
 // strided view (STR): nbph blocks per head, each within one head.
+// zero[0 .. nzero) is zeroed on the side (the split V quantiser's start).
 template <int DT, bool STR>
 __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, InView in, int N, int64_t nbph,
     int64_t ntok, int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
-    uint32_t* __restrict__ kbits, float* __restrict__ kmu) {
+    uint32_t* __restrict__ kbits, float* __restrict__ kmu, uint32_t* __restrict__ zero, int64_t nzero) {
   __shared__ uint32_t bits_s[256 * kPackU];
   __shared__ double sum_s[256 * kPackU];
+  if (blockIdx.y == 0)
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nzero; i += (int64_t)gridDim.x * 256) zero[i] = 0u;
   if constexpr (STR) {
     const bool isk = blockIdx.y != 0;
     const int64_t bh = blockIdx.x / nbph, tb = blockIdx.x - bh * nbph;
@@ -143,6 +144,8 @@ __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
   }
 }
 
+__global__ void zero_kernel(uint32_t* __restrict__ a, int64_t n);
+
 InView dense_view(int H, int N, int d) {
   InView v;
   v.sn = d;
@@ -155,7 +158,7 @@ InView dense_view(int H, int N, int d) {
 
 hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InView& in, int nbh, int N,
                           int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
-                          float* kmu, hipStream_t s) {
+                          float* kmu, hipStream_t s, uint32_t* zero, int64_t nzero) {
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const int64_t ntok = (int64_t)nbh * N;
@@ -168,8 +171,13 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InVie
     const dim3 grid((unsigned)nblk, 2);
     auto kern = dt == BA_F16 ? (str ? pack_qk_coop_kernel<BA_F16, true> : pack_qk_coop_kernel<BA_F16, false>)
                              : (str ? pack_qk_coop_kernel<BA_BF16, true> : pack_qk_coop_kernel<BA_BF16, false>);
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, q16, k16, in, N, nbph, ntok, d, qbits, qmu, kbits, kmu);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, q16, k16, in, N, nbph, ntok, d, qbits, qmu, kbits, kmu, zero,
+                       nzero);
     return hipGetLastError();
+  }
+  if (nzero > 0) {
+    if ((nzero + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nzero + 255) / 256)), dim3(256), 0, s, zero, nzero);
   }
   if ((ntok + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((ntok + 255) / 256), 2);
@@ -185,21 +193,16 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InVie
 // 16-byte aligned): one block per head, one thread per (row, channel)
 // element with scalar accesses. Pass 1 takes the per-channel max |v| (an
 // LDS atomic max on the float bits, valid because the values are
-// non-negative), pass 2 quantises with inv = 127/amax, writes int8 and
-// gathers the channel sums of the int8 values (LDS atomic adds).
+// non-negative), pass 2 quantises with inv = 127/amax and writes int8.
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(256) void quant_v_kernel(
     const uint16_t* __restrict__ v, InView in, int N, int d,
-    int8_t* __restrict__ vq, float* __restrict__ vscale, int32_t* __restrict__ vsum) {
+    int8_t* __restrict__ vq, float* __restrict__ vscale) {
   __shared__ uint32_t amax_bits[128];
   __shared__ float inv_s[128];
-  __shared__ int32_t sum_s[128];
   const int bh = blockIdx.x;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    amax_bits[i] = 0u;
-    sum_s[i] = 0;
-  }
+  for (int i = threadIdx.x; i < d; i += blockDim.x) amax_bits[i] = 0u;
   __syncthreads();
   const uint16_t* vh = v + (int64_t)(bh / in.H) * in.sb + (int64_t)(bh % in.H) * in.sh;  // row j at j * in.sn
   int8_t* qh = vq + (int64_t)bh * N * d;
@@ -219,10 +222,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
     float y = __builtin_rintf(to_f32<DT>(vh[(int64_t)j * in.sn + c]) * inv_s[c]);
     y = fminf(fmaxf(y, -127.0f), 127.0f);
     qh[(int64_t)j * d + c] = (int8_t)(int)y;
-    atomicAdd(&sum_s[c], (int)y);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < d; i += blockDim.x) vsum[(int64_t)bh * d + i] = sum_s[i];
 }
 
 // quant_v for heads that fit in registers (d % 8 == 0): a block of 1024
@@ -233,31 +233,26 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
 // of rows t / P + k*R: every load of the group is one contiguous run of
 // 16*R*P bytes. Channel maxima go through an LDS atomic max on the float
 // bits (non-negative), then the held values are quantised and written as
-// int8, and their channel sums gathered with LDS atomic adds.
+// int8.
 constexpr int kQvRows = 12;  // rows per thread held in registers
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 // heads bh0 .. bh0 + HB - 1 (those below nbh) by one block of 1024
-// threads; smem holds 3 * 128 words per head
+// threads; smem holds 2 * 128 words per head
 template <int DT>
 __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v, const InView& in, int N, int d,
                                                   int64_t bh0,
                                                   int64_t nbh, int HB, int8_t* __restrict__ vq,
-                                                  float* __restrict__ vscale, int32_t* __restrict__ vsum,
-                                                  uint32_t* smem) {
+                                                  float* __restrict__ vscale, uint32_t* smem) {
   const int T = 1024 / HB;
   const int hs = threadIdx.x / T, t = threadIdx.x % T;
   const int64_t bh = bh0 + hs;
   const bool hvalid = bh < nbh;
-  uint32_t* amax_bits = smem + 384 * hs;
+  uint32_t* amax_bits = smem + 256 * hs;
   float* inv_s = reinterpret_cast<float*>(amax_bits + 128);
-  int32_t* sum_s = reinterpret_cast<int32_t*>(amax_bits + 256);
   const int P = d >> 3, R = T / P;
   const int piece = t % P, r0 = t / P;
   const bool active = hvalid && r0 < R;
-  if (t < d) {
-    amax_bits[t] = 0u;
-    sum_s[t] = 0;
-  }
+  if (t < d) amax_bits[t] = 0u;
   __syncthreads();
   const uint16_t* vh = v + (hvalid ? (bh / in.H) * in.sb + (bh % in.H) * in.sh : 0) + 8 * piece;
   int8_t* qh = vq + (hvalid ? bh * N * d : 0) + 8 * piece;
@@ -293,7 +288,6 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
   float inv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
-  int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k) {
     const int r = r0 + k * R;
@@ -303,19 +297,12 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
       for (int e = 0; e < 8; ++e) {
         float y = __builtin_rintf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16))) * inv[e]);
         y = fminf(fmaxf(y, -127.0f), 127.0f);
-        csum[e] += (int)y;
         const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
         if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
       }
       *reinterpret_cast<uint2*>(qh + (int64_t)r * d) = make_uint2(lo, hi);
     }
   }
-  if (active) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) atomicAdd(&sum_s[8 * piece + e], csum[e]);
-  }
-  __syncthreads();
-  if (hvalid && t < d) vsum[bh * d + t] = sum_s[t];
 }
 
 // Heads per 1024-thread block for the register-resident quantiser: the most
@@ -335,9 +322,9 @@ int quant_heads_per_block(int nbh, int N, int d) {
 template <int DT>
 __global__ __launch_bounds__(1024) void quant_v_head_kernel(
     const uint16_t* __restrict__ v, InView in, int nbh, int N, int d, int HB, int8_t* __restrict__ vq,
-    float* __restrict__ vscale, int32_t* __restrict__ vsum) {
-  __shared__ uint32_t smem[8 * 3 * 128];
-  quant_heads_block<DT>(v, in, N, d, (int64_t)blockIdx.x * HB, nbh, HB, vq, vscale, vsum, smem);
+    float* __restrict__ vscale) {
+  __shared__ uint32_t smem[8 * 2 * 128];
+  quant_heads_block<DT>(v, in, N, d, (int64_t)blockIdx.x * HB, nbh, HB, vq, vscale, smem);
 }
 
 // Pack Q and K and quantise V in one launch (d % 8 == 0, heads that fit the
@@ -350,13 +337,13 @@ __global__ __launch_bounds__(1024) void prepass_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, InView in,
     int nbh, int N, int d, int HB, int64_t nvb, int64_t npb, int64_t nbph, uint32_t* __restrict__ qbits,
     float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
-    float* __restrict__ vscale, int32_t* __restrict__ vsum) {
+    float* __restrict__ vscale) {
   __shared__ uint32_t bits_s[1024 * kPackU];
   __shared__ double sum_s[1024 * kPackU];
   const int64_t ntok = (int64_t)nbh * N;
   const int64_t b = blockIdx.x;
   if (b < nvb) {
-    quant_heads_block<DT>(v, in, N, d, b * HB, nbh, HB, vq, vscale, vsum, bits_s);
+    quant_heads_block<DT>(v, in, N, d, b * HB, nbh, HB, vq, vscale, bits_s);
   } else if constexpr (STR) {
     const bool isk = b - nvb >= npb;
     const int64_t pb = b - nvb - (isk ? npb : 0);
@@ -374,44 +361,56 @@ __global__ __launch_bounds__(1024) void prepass_fused_kernel(
 
 // quant_v for long heads (16-byte rows, heads past the register-resident
 // quantiser): the rows of each head are split over S blocks so that the whole
-// chip streams V. After a zero fill of vscale and vsum, pass A takes each
-// block's channel maxima of |v| and combines them with a global atomic max
-// on the float bits kept in vscale (valid for non-negative values); pass B
-// reads them back, quantises with inv = 127 / amax, writes int8 and combines
-// the channel sums with global atomic adds into vsum; a last pass turns the
-// maxima into vscale = amax / 127. The arithmetic is that of the one-block
-// quantisers, so the outputs are the same bit for bit.
-__global__ __launch_bounds__(256) void zero2_kernel(uint32_t* __restrict__ a, int32_t* __restrict__ b, int64_t n) {
+// chip streams V, in two passes after a zero fill of vscale (folded into the
+// packing launch when ba_pack_qk_quant_v runs it).
+//  * Pass A: each block takes the channel maxima of |v| over its rows and
+//    combines them into vscale with a global atomic max on the float bits
+//    with the top bit set (unsigned order = order of the non-negative
+//    values; the set bit marks "a maximum, not yet a scale").
+//  * Pass B: each block reads the head's maxima, quantises its rows with
+//    inv = 127 / amax, writes int8, and stores vscale = amax / 127. Every
+//    block of the head stores the same value, and a block that reads a word
+//    already turned into a scale recovers amax exactly as the 16-bit
+//    rounding of scale * 127 (amax is a 16-bit value and the two float
+//    roundings move it by far less than half a 16-bit step; exhaustively
+//    true for every finite fp16 and bf16 value), so no block depends on
+//    which form it finds.
+// The arithmetic is that of the one-block quantisers, so the outputs are the
+// same bit for bit.
+constexpr uint32_t kAmaxMark = 0x80000000u;
+
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ a, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) {
-    a[i] = 0u;
-    b[i] = 0;
-  }
+  if (i < n) a[i] = 0u;
 }
 
-__global__ __launch_bounds__(256) void amax_to_scale_kernel(float* __restrict__ vscale, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) vscale[i] = vscale[i] / 127.0f;  // amax, held as its float bits, to the scale
+// amax of a channel from its vscale word (either form, see above)
+template <int DT>
+__device__ __forceinline__ float amax_of_word(uint32_t w) {
+  if (w & kAmaxMark) return __uint_as_float(w & ~kAmaxMark);
+  const float y = __uint_as_float(w) * 127.0f;
+  return DT == BA_F16 ? f16_to_f32(f32_to_f16(y)) : bf16_to_f32(f32_to_bf16(y));
 }
 
 // Block x: head x / S, rows [s * RB, min(N, s * RB + RB)) with s = x % S.
-// QUANT false: pass A (maxima into amax_bits); true: pass B.
+// QUANT false: pass A; true: pass B.
 template <int DT, bool QUANT>
 __global__ __launch_bounds__(256) void quant_v_split_kernel(
     const uint16_t* __restrict__ v, InView in, int N, int d, int S, int RB, int8_t* __restrict__ vq,
-    uint32_t* __restrict__ amax_bits, int32_t* __restrict__ vsum) {
-  __shared__ uint32_t red[128];  // channel maxima (pass A) or sums (pass B)
+    uint32_t* __restrict__ vs_bits) {
+  __shared__ uint32_t red[128];  // channel maxima (pass A)
   __shared__ float inv_s[128];
   const int64_t bh = blockIdx.x / S;
   const int r_begin = (int)(blockIdx.x - bh * S) * RB, r_end = min(N, r_begin + RB);
   const int P = d >> 3, rows = 256 / P;  // 16-byte pieces per row, rows per sweep
   const int piece = threadIdx.x % P, r0 = threadIdx.x / P;
   const bool active = r0 < rows;
+  float amax = 0.0f;
   if (threadIdx.x < d) {
     red[threadIdx.x] = 0u;
     if (QUANT) {
-      const float a = __uint_as_float(amax_bits[bh * d + threadIdx.x]);
-      inv_s[threadIdx.x] = a > 0.0f ? 127.0f / a : 0.0f;
+      amax = amax_of_word<DT>(vs_bits[bh * d + threadIdx.x]);
+      inv_s[threadIdx.x] = amax > 0.0f ? 127.0f / amax : 0.0f;
     }
   }
   __syncthreads();
@@ -437,19 +436,17 @@ __global__ __launch_bounds__(256) void quant_v_split_kernel(
       for (int e = 0; e < 8; ++e) atomicMax(&red[8 * piece + e], __float_as_uint(m[e]));
     }
     __syncthreads();
-    if (threadIdx.x < d && red[threadIdx.x] != 0u) atomicMax(&amax_bits[bh * d + threadIdx.x], red[threadIdx.x]);
+    if (threadIdx.x < d) atomicMax(&vs_bits[bh * d + threadIdx.x], red[threadIdx.x] | kAmaxMark);
   } else {
     float inv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
-    int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     auto quant8 = [&](const u4v& raw) -> uint2 {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
         y = fminf(fmaxf(y, -127.0f), 127.0f);
-        csum[e] += (int)y;
         const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
         if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
       }
@@ -467,78 +464,91 @@ __global__ __launch_bounds__(256) void quant_v_split_kernel(
       }
       for (; j < r_end; j += rows)
         *reinterpret_cast<uint2*>(qh + (int64_t)j * d) = quant8(*reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) atomicAdd(reinterpret_cast<int32_t*>(&red[8 * piece + e]), csum[e]);
     }
-    __syncthreads();
-    const int32_t sum = (int32_t)red[threadIdx.x < d ? threadIdx.x : 0];
-    if (threadIdx.x < d && sum != 0) atomicAdd(&vsum[bh * d + threadIdx.x], sum);
+    // the scale, the same value from every block of the head
+    if (threadIdx.x < d) vs_bits[bh * d + threadIdx.x] = __float_as_uint(amax / 127.0f);
   }
 }
 
-template <int DT>
-hipError_t launch_quant_v_split(const uint16_t* v, const InView& in, int nbh, int N, int d, int8_t* vq,
-                                float* vscale, int32_t* vsum, hipStream_t s) {
+// rows per block of the split quantiser: about four blocks per CU, each with
+// at least one full sweep of 8 rows per thread
+void split_shape(int nbh, int N, int d, int& S, int& RB) {
   const int rows = 256 / (d / 8);
-  // about four blocks per CU, each with at least one full sweep of 8 rows per thread
   const int64_t want = (1024 + (int64_t)nbh - 1) / nbh;
   const int64_t cap = std::max<int64_t>(1, N / (8 * rows));
   const int S0 = (int)std::min(want, cap);
-  const int RB = (N + S0 - 1) / S0;
-  const int S = (N + RB - 1) / RB;
-  const int64_t nblk = (int64_t)nbh * S, n = (int64_t)nbh * d;
-  if (nblk > 0x7FFFFFFF || (n + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(vscale);
-  const unsigned nz = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(zero2_kernel, dim3(nz), dim3(256), 0, s, amax_bits, vsum, n);
-  hipLaunchKernelGGL((quant_v_split_kernel<DT, false>), dim3((unsigned)nblk), dim3(256), 0, s, v, in, N, d, S, RB, vq,
-                     amax_bits, vsum);
-  hipLaunchKernelGGL((quant_v_split_kernel<DT, true>), dim3((unsigned)nblk), dim3(256), 0, s, v, in, N, d, S, RB, vq,
-                     amax_bits, vsum);
-  hipLaunchKernelGGL(amax_to_scale_kernel, dim3(nz), dim3(256), 0, s, vscale, n);
+  RB = (N + S0 - 1) / S0;
+  S = (N + RB - 1) / RB;
+}
+
+// passes A and B (vscale already zero)
+template <int DT>
+hipError_t launch_quant_v_split_ab(const uint16_t* v, const InView& in, int nbh, int N, int d, int8_t* vq,
+                                   float* vscale, hipStream_t s) {
+  int S, RB;
+  split_shape(nbh, N, d, S, RB);
+  const int64_t nblk = (int64_t)nbh * S;
+  if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+  uint32_t* vs_bits = reinterpret_cast<uint32_t*>(vscale);
+  hipLaunchKernelGGL((quant_v_split_kernel<DT, false>), dim3((unsigned)nblk), dim3(256), 0, s, v, in, N, d, S, RB,
+                     vq, vs_bits);
+  hipLaunchKernelGGL((quant_v_split_kernel<DT, true>), dim3((unsigned)nblk), dim3(256), 0, s, v, in, N, d, S, RB,
+                     vq, vs_bits);
   return hipGetLastError();
+}
+
+bool quant_in_registers(int N, int d) {
+  return d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8));
 }
 
 hipError_t launch_quant_v(const void* v, ba_dtype dt, const InView& in, int nbh, int N, int d,
-                          int8_t* vq, float* vscale, int32_t* vsum, hipStream_t s) {
-  if (in.vec && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8))) {
-    const uint16_t* v16 = static_cast<const uint16_t*>(v);
+                          int8_t* vq, float* vscale, hipStream_t s) {
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  if (in.vec && quant_in_registers(N, d)) {
     const int HB = quant_heads_per_block(nbh, N, d);
     const unsigned nvb = (unsigned)((nbh + HB - 1) / HB);
     if (dt == BA_F16)
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3(nvb), dim3(1024), 0, s, v16, in, nbh, N, d, HB, vq, vscale,
-                         vsum);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_F16>, dim3(nvb), dim3(1024), 0, s, v16, in, nbh, N, d, HB, vq, vscale);
     else
-      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3(nvb), dim3(1024), 0, s, v16, in, nbh, N, d, HB, vq, vscale,
-                         vsum);
+      hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3(nvb), dim3(1024), 0, s, v16, in, nbh, N, d, HB, vq, vscale);
     return hipGetLastError();
   }
   if (in.vec) {
-    const uint16_t* v16 = static_cast<const uint16_t*>(v);
-    return dt == BA_F16 ? launch_quant_v_split<BA_F16>(v16, in, nbh, N, d, vq, vscale, vsum, s)
-                        : launch_quant_v_split<BA_BF16>(v16, in, nbh, N, d, vq, vscale, vsum, s);
+    const int64_t n = (int64_t)nbh * d;
+    if ((n + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(vscale), n);
+    return dt == BA_F16 ? launch_quant_v_split_ab<BA_F16>(v16, in, nbh, N, d, vq, vscale, s)
+                        : launch_quant_v_split_ab<BA_BF16>(v16, in, nbh, N, d, vq, vscale, s);
   }
   // element path (d % 8 != 0 or rows not 16-byte aligned): one block per head
-  const uint16_t* v16 = static_cast<const uint16_t*>(v);
   if (dt == BA_F16)
-    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nbh), dim3(256), 0, s, v16, in, N, d, vq, vscale, vsum);
+    hipLaunchKernelGGL(quant_v_kernel<BA_F16>, dim3((unsigned)nbh), dim3(256), 0, s, v16, in, N, d, vq, vscale);
   else
-    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nbh), dim3(256), 0, s, v16, in, N, d, vq, vscale, vsum);
+    hipLaunchKernelGGL(quant_v_kernel<BA_BF16>, dim3((unsigned)nbh), dim3(256), 0, s, v16, in, N, d, vq, vscale);
   return hipGetLastError();
-}
-
-bool prepass_fusable(int N, int d) {
-  return d % 8 == 0 && (int64_t)N <= (int64_t)kQvRows * (1024 / (d / 8));
 }
 
 hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype dt, const InView& in, int nbh,
                           int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
-                          float* vscale, int32_t* vsum, hipStream_t s) {
+                          float* vscale, hipStream_t s) {
   const int64_t ntok = (int64_t)nbh * N;
-  if (!in.vec || !prepass_fusable(N, d)) {
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  if (!in.vec) {
     hipError_t e = launch_pack_qk(q, k, dt, in, nbh, N, d, qbits, qmu, kbits, kmu, s);
     if (e != hipSuccess) return e;
-    return launch_quant_v(v, dt, in, nbh, N, d, vq, vscale, vsum, s);
+    return launch_quant_v(v, dt, in, nbh, N, d, vq, vscale, s);
+  }
+  if (!quant_in_registers(N, d)) {
+    // long heads: the packing launch also zeroes vscale, then the split
+    // quantiser's two passes
+    hipError_t e = launch_pack_qk(q, k, dt, in, nbh, N, d, qbits, qmu, kbits, kmu, s,
+                                  reinterpret_cast<uint32_t*>(vscale), (int64_t)nbh * d);
+    if (e != hipSuccess) return e;
+    return dt == BA_F16 ? launch_quant_v_split_ab<BA_F16>(v16, in, nbh, N, d, vq, vscale, s)
+                        : launch_quant_v_split_ab<BA_BF16>(v16, in, nbh, N, d, vq, vscale, s);
   }
   const int TB = 1024 * kPackU / (d / 8);
   const bool str = !in.dense(N, d);
@@ -548,52 +558,11 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
   const int64_t nvb = (nbh + HB - 1) / HB;
   const int64_t nblk = nvb + 2 * npb;
   if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const uint16_t* q16 = static_cast<const uint16_t*>(q);
-  const uint16_t* k16 = static_cast<const uint16_t*>(k);
-  const uint16_t* v16 = static_cast<const uint16_t*>(v);
   auto kern = dt == BA_F16 ? (str ? prepass_fused_kernel<BA_F16, true> : prepass_fused_kernel<BA_F16, false>)
                            : (str ? prepass_fused_kernel<BA_BF16, true> : prepass_fused_kernel<BA_BF16, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, nvb, npb, nbph,
-                     qbits, qmu, kbits, kmu, vq, vscale, vsum);
+                     qbits, qmu, kbits, kmu, vq, vscale);
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Hamming debug view: sigma = d - 2*popcount(q xor k), one thread per key.
-// Grid: x = key blocks of 256, y = query rows of the window, z = heads.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void hamming_kernel(
-    const uint32_t* __restrict__ qbits, const uint32_t* __restrict__ kbits, int N,
-    int d, int W, int bh_begin, int row_begin, int row_count, int32_t* __restrict__ sigma) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  const int r = blockIdx.y;
-  const int hb = blockIdx.z;
-  if (j >= N) return;
-  const int64_t bh = bh_begin + hb;
-  const uint32_t* qi = qbits + (bh * N + row_begin + r) * W;
-  const uint32_t* kj = kbits + (bh * N + j) * W;
-  int h = 0;
-  for (int w = 0; w < W; ++w) h += __builtin_popcount(qi[w] ^ kj[w]);
-  sigma[((int64_t)hb * row_count + r) * N + j] = d - 2 * h;
-}
-
-hipError_t launch_hamming(const uint32_t* qbits, const uint32_t* kbits, int N,
-                          int d, int bh_begin, int bh_count, int row_begin,
-                          int row_count, int32_t* sigma, hipStream_t s) {
-  const int W = (d + 31) / 32;
-  // grid.y is limited to 65535 rows per launch; split larger windows
-  for (int r0 = 0; r0 < row_count; r0 += 65535) {
-    const int rc = min(65535, row_count - r0);
-    for (int h0 = 0; h0 < bh_count; h0 += 65535) {
-      const int hc = min(65535, bh_count - h0);
-      hipLaunchKernelGGL(hamming_kernel, dim3((N + 255) / 256, rc, hc), dim3(256), 0, s,
-                         qbits, kbits, N, d, W, bh_begin + h0, row_begin + r0, row_count,
-                         sigma + ((int64_t)h0 * row_count + r0) * N);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  return hipSuccess;
 }
 
 }  // namespace binattn

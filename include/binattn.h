@@ -32,7 +32,7 @@
  *    faults surface at the caller's next synchronisation. No C++ exception
  *    crosses this interface. The library is stateless and re-entrant.
  *  - Alignment: bits / vq / out / Q / K / V pointers 16-byte aligned; mu,
- *    vscale, vsum and bias pointers 4-byte aligned (fp16 bias: 2-byte).
+ *    vscale and bias pointers 4-byte aligned (fp16 bias: 2-byte).
  */
 #ifndef BINATTN_H
 #define BINATTN_H
@@ -114,12 +114,11 @@ ba_status ba_pack_qk(const void* q, const void* k, ba_dtype dt, int B, int H,
 /* Channel-wise 8-bit V (zh section 2.2 item 3; nl Methodologie 2): for each
  * (b,h,c), amax = max_j |v_jc| over the N tokens; vq = clamp(rne(v * (127 /
  * amax)), -127, 127) in float32; vscale = amax / 127; an all-zero channel
- * gives vq = 0 and vscale = 0. vsum = sum_j vq_jc, the channel sums of the
- * quantised V (exact; ba_attention_fwd uses them, see there).
- * v: [B,H,N,d] fp16 or bf16; vq: int8 [B,H,N,d]; vscale: float [B,H,d];
- * vsum: int32 [B,H,d]. */
+ * gives vq = 0 and vscale = 0.
+ * v: [B,H,N,d] fp16 or bf16; vq: int8 [B,H,N,d]; vscale: float [B,H,d].
+ * vq and vscale must not overlap each other or v. */
 ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
-                     int8_t* vq, float* vscale, int32_t* vsum, void* stream);
+                     int8_t* vq, float* vscale, void* stream);
 
 /* ba_pack_qk and ba_quant_v in one call, for callers that run both before
  * ba_attention_fwd (as every forward pass does): the same outputs, bit for
@@ -127,11 +126,12 @@ ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
  * (q, k, v all [B,H,N,d] of dt). Where d % 8 == 0 and a head fits the
  * register-resident V quantiser (N <= 12 * 1024 / (d / 8)) it is a single
  * launch in which the V heads and the Q/K token blocks run side by side;
- * otherwise it enqueues the two calls' kernels in turn. No output may
- * overlap another output or an input. */
+ * with longer heads the packing launch also clears vscale and the V
+ * quantiser's two passes follow; otherwise it enqueues the two calls'
+ * kernels in turn. No output may overlap another output or an input. */
 ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dtype dt, int B, int H,
                              int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu,
-                             int8_t* vq, float* vscale, int32_t* vsum, void* stream);
+                             int8_t* vq, float* vscale, void* stream);
 
 /* ba_pack_qk_quant_v with q, k and v read through strided views that share
  * in_strides (typically the head slices of one QKV projection output, so no
@@ -145,31 +145,30 @@ ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dty
  * spanning more than about 2^40 elements: BA_ERR_INVALID_ARG. */
 ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v, const ba_strides* in_strides,
                                      ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
-                                     uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, int32_t* vsum,
-                                     void* stream);
+                                     uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, void* stream);
 
 /* Fused BinaryAttention forward (zh sections 2.1-2.3; nl Methodologie 1-3;
  * it section 2; fr section 2B; pt section 2B-2C), non-causal, self-attention
  * (N queries and N keys per head). For each head and query i:
  *   sigma_ij = d - 2*popcount(qbits_i XOR kbits_j)
  *   s_ij     = qmu_i * kmu_j * sigma_ij / sqrt(d) + b_ij
- *   m_i      = max_j s_ij,  p_ij = exp(s_ij - m_i),  l_i = sum_j p_ij
+ *   m_i      = max_j s_ij,  p_ij = exp(s_ij - m_i)
  *   p8_ij    = rne(255 * p_ij)                  (unsigned 8 bit over [0,1])
  *   A_ic     = sum_j p8_ij * vq_jc              (exact, int32)
- *   out_ic   = A_ic * vscale_c / (255 * l_i)    rounded to out_dt
+ *   out_ic   = A_ic * vscale_c / sum_j p8_ij    rounded to out_dt
+ * i.e. the row normaliser is the integer row sum of the quantised P (the
+ * weights that multiply V), so each dequantised row of P sums to 1.
  * m_i is the exact row maximum (the kernel finds it in a first pass over the
  * keys), so p8 matches the plain definition up to float rounding.
- * The matrix cores multiply signed bytes only, so the kernel accumulates
- * sum_j (127 - p8_ij) * vq_jc and forms A_ic = 127 * vsum_c - that sum;
- * vsum must therefore be the channel sums of vq (as ba_quant_v writes them).
- * Inputs are the outputs of ba_pack_qk / ba_quant_v (or equivalent data);
- * mu may be any non-negative per-token scale (e.g. a learned one).
+ * Any int8 vq with any non-negative scales is accepted (the outputs of
+ * ba_pack_qk / ba_quant_v or equivalent data; e.g. a learned mu); the
+ * kernel needs nothing besides these arrays.
  * bias: NULL or kind BA_BIAS_NONE for no bias.
  * out: [B,H,N,d] of out_dt, which must be BA_F16 or BA_BF16. */
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu,
                            const uint32_t* kbits, const float* kmu,
                            const int8_t* vq, const float* vscale,
-                           const int32_t* vsum, const ba_bias* bias,
+                           const ba_bias* bias,
                            int B, int H, int N, int d,
                            void* out, ba_dtype out_dt, void* stream);
 
@@ -187,7 +186,7 @@ ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu,
 ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu,
                                    const uint32_t* kbits, const float* kmu,
                                    const int8_t* vq, const float* vscale,
-                                   const int32_t* vsum, const ba_bias* bias,
+                                   const ba_bias* bias,
                                    int B, int H, int N, int d, void* out,
                                    const ba_strides* out_strides, ba_dtype out_dt,
                                    void* stream);
@@ -198,7 +197,12 @@ ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu,
  *   sigma[hb, r, j] = d - 2*popcount(qbits[bh_begin+hb, row_begin+r] XOR
  *                                    kbits[bh_begin+hb, j])
  * sigma: int32 [bh_count, row_count, N], device. The window must lie inside
- * [0, B*H) x [0, N). */
+ * [0, B*H) x [0, N).
+ * The values come from the fused attention kernel's own Q.K code, every
+ * route it has for that d: the staged-tile route writes them, then the
+ * route without staging (and, at 65..96 channels, the raw-word route)
+ * recompute them and overwrite any element they disagree on with
+ * 0x7FFFFFFF, which no similarity equals. */
 ba_status ba_debug_hamming_scores(const uint32_t* qbits, const uint32_t* kbits,
                                   int B, int H, int N, int d, int bh_begin,
                                   int bh_count, int row_begin, int row_count,

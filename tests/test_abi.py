@@ -30,6 +30,41 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+# The four calls of the hot path, in the form their contract states
+# (argument types and order); extension calls may add to, but not alter them.
+CONTRACT = {
+    "ba_pack_qk": "const void* q, const void* k, ba_dtype dt, int B, int H, int N, int d, uint32_t* qbits, "
+                  "float* qmu, uint32_t* kbits, float* kmu, void* stream",
+    "ba_quant_v": "const void* v, ba_dtype dt, int B, int H, int N, int d, int8_t* vq, float* vscale, void* stream",
+    "ba_attention_fwd": "const uint32_t* qbits, const float* qmu, const uint32_t* kbits, const float* kmu, "
+                        "const int8_t* vq, const float* vscale, const ba_bias* bias, int B, int H, int N, int d, "
+                        "void* out, ba_dtype out_dt, void* stream",
+    "ba_debug_hamming_scores": "const uint32_t* qbits, const uint32_t* kbits, int B, int H, int N, int d, "
+                               "int bh_begin, int bh_count, int row_begin, int row_count, int32_t* sigma, "
+                               "void* stream",
+}
+
+
+def _prototypes():
+    import re
+    text = re.sub(r"/\*.*?\*/", "", open(ba.HEADER_PATH).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"ba_status\s+(ba_[a-z_]+)\s*\(([^;]*?)\)\s*;", text):
+        out[m.group(1)] = " ".join(m.group(2).split())
+    return out
+
+
+def test_contract_prototypes():
+    protos = _prototypes()
+    for name, args in CONTRACT.items():
+        assert protos.get(name) == args, (name, protos.get(name))
+    # every argument of every declared call is a plain C type (no torch or C++ types)
+    for name, args in protos.items():
+        for a in args.split(","):
+            assert a.strip().split()[0] in {"const", "void*", "int", "ba_dtype", "uint32_t*", "float*",
+                                            "int8_t*", "int32_t*"}, (name, a)
+
+
 def test_small_helpers(L):
     assert [L.ba_packed_words(d) for d in (0, 1, 32, 33, 64, 72, 128)] == [0, 1, 1, 2, 2, 3, 4]
     for s in range(4):
@@ -53,48 +88,48 @@ def test_pack_rejections(L):
     assert pack(L, kb=A(2)) == INV                        # outputs overlap
 
 
-def quant(L, v=A(0), dt=ba.BA_F16, B=1, H=1, N=8, d=64, vq=A(1), vs=A(2), vsum=A(3)):
-    return L.ba_quant_v(v, dt, B, H, N, d, vq, vs, vsum, None)
+def quant(L, v=A(0), dt=ba.BA_F16, B=1, H=1, N=8, d=64, vq=A(1), vs=A(2)):
+    return L.ba_quant_v(v, dt, B, H, N, d, vq, vs, None)
 
 
 def test_quant_rejections(L):
-    assert quant(L, v=None) == INV and quant(L, vs=None) == INV and quant(L, vsum=None) == INV
-    assert quant(L, vsum=ctypes.c_void_p(P + 3 * (1 << 32) + 2)) == INV  # not 4-byte aligned
-    assert quant(L, vsum=A(2)) == INV  # outputs overlap
+    assert quant(L, v=None) == INV and quant(L, vs=None) == INV and quant(L, vq=None) == INV
+    assert quant(L, vs=ctypes.c_void_p(P + 2 * (1 << 32) + 2)) == INV  # not 4-byte aligned
+    assert quant(L, vs=A(1)) == INV  # outputs overlap
     assert quant(L, H=0) == INV and quant(L, d=200) == UNS and quant(L, dt=ba.BA_F32) == UNS
     assert quant(L, vq=ctypes.c_void_p(P + 1 * (1 << 32) + 8)) == INV
     assert quant(L, vq=A(0)) == INV  # output aliases the input
 
 
 def prep(L, q=A(0), k=A(1), v=A(2), dt=ba.BA_BF16, B=1, H=1, N=8, d=64, **kw):
-    o = dict(qb=A(3), qm=A(4), kb=A(5), km=A(6), vq=A(7), vs=A(8), vsum=A(9))
+    o = dict(qb=A(3), qm=A(4), kb=A(5), km=A(6), vq=A(7), vs=A(8))
     o.update(kw)
     return L.ba_pack_qk_quant_v(q, k, v, dt, B, H, N, d, o["qb"], o["qm"], o["kb"], o["km"], o["vq"], o["vs"],
-                                o["vsum"], None)
+                                None)
 
 
 def test_pack_qk_quant_v_rejections(L):
-    assert prep(L, v=None) == INV and prep(L, km=None) == INV and prep(L, vsum=None) == INV
+    assert prep(L, v=None) == INV and prep(L, km=None) == INV and prep(L, vs=None) == INV
     assert prep(L, N=0) == INV and prep(L, d=129) == UNS and prep(L, dt=ba.BA_F32) == UNS
     assert prep(L, N=ba.BA_MAX_TOKENS + 1) == UNS
     assert prep(L, v=ctypes.c_void_p(P + 2 * (1 << 32) + 8)) == INV   # not 16-byte aligned
     assert prep(L, vs=ctypes.c_void_p(P + 8 * (1 << 32) + 2)) == INV  # not 4-byte aligned
     assert prep(L, vq=A(3)) == INV    # outputs overlap (vq on qbits)
-    assert prep(L, vsum=A(2)) == INV  # output aliases the V input
+    assert prep(L, vs=A(2)) == INV    # output aliases the V input
     assert prep(L, qb=A(1)) == INV    # output aliases the K input
 
 
 def attn(L, bias=None, B=2, H=2, N=16, d=64, out=A(9), out_dt=ba.BA_BF16, **kw):
-    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6), vsum=A(7))
+    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6))
     args.update(kw)
     pb = ctypes.byref(bias) if bias is not None else None
     return L.ba_attention_fwd(args["qb"], args["qm"], args["kb"], args["km"], args["vq"], args["vs"],
-                              args["vsum"], pb, B, H, N, d, out, out_dt, None)
+                              pb, B, H, N, d, out, out_dt, None)
 
 
 def test_attention_rejections(L):
-    assert attn(L, qb=None) == INV and attn(L, out=None) == INV and attn(L, vsum=None) == INV
-    assert attn(L, out=A(7)) == INV  # output aliases vsum
+    assert attn(L, qb=None) == INV and attn(L, out=None) == INV and attn(L, vs=None) == INV
+    assert attn(L, out=A(6)) == INV  # output aliases vscale
     assert attn(L, d=0) == INV and attn(L, d=129) == UNS
     assert attn(L, N=ba.BA_MAX_TOKENS + 1) == UNS
     assert attn(L, out_dt=ba.BA_F32) == UNS and attn(L, out_dt=5) == UNS
@@ -129,18 +164,18 @@ def prep_s(L, st=ba_strides(3 * 8 * 64, 64, 3 * 64), q=A(0), k=None, v=None, dt=
     # default: q, k, v are the head slices of one [B, N, 3, H, d] buffer
     k = k or ctypes.c_void_p(P + 2 * H * d)
     v = v or ctypes.c_void_p(P + 4 * H * d)
-    o = dict(qb=A(3), qm=A(4), kb=A(5), km=A(6), vq=A(7), vs=A(8), vsum=A(9))
+    o = dict(qb=A(3), qm=A(4), kb=A(5), km=A(6), vq=A(7), vs=A(8))
     o.update(kw)
     pst = ctypes.byref(st) if st is not None else None
     return L.ba_pack_qk_quant_v_strided(q, k, v, pst, dt, B, H, N, d, o["qb"], o["qm"], o["kb"], o["km"],
-                                        o["vq"], o["vs"], o["vsum"], None)
+                                        o["vq"], o["vs"], None)
 
 
 def test_pack_qk_quant_v_strided_rejections(L):
     assert prep_s(L, st=None) == INV
     assert prep_s(L, st=ba_strides(0, 0, -1)) == INV
     assert prep_s(L, st=ba_strides(1 << 40, 0, 64), B=2) == INV      # span above 2^40 elements
-    assert prep_s(L, q=None) == INV and prep_s(L, vsum=None) == INV
+    assert prep_s(L, q=None) == INV and prep_s(L, vs=None) == INV
     assert prep_s(L, q=ctypes.c_void_p(P + 1)) == INV                 # not 2-byte aligned
     assert prep_s(L, N=0) == INV and prep_s(L, d=129) == UNS and prep_s(L, dt=ba.BA_F32) == UNS
     # an output inside the span of the V view: V's last token starts at element 2*C + 7*3*C
@@ -149,11 +184,11 @@ def test_pack_qk_quant_v_strided_rejections(L):
 
 
 def attn_s(L, st=ba_strides(16 * 2 * 64, 64, 2 * 64), B=2, H=2, N=16, d=64, out=A(9), **kw):
-    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6), vsum=A(7))
+    args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6))
     args.update(kw)
     pst = ctypes.byref(st) if st is not None else None
     return L.ba_attention_fwd_strided(args["qb"], args["qm"], args["kb"], args["km"], args["vq"], args["vs"],
-                                      args["vsum"], None, B, H, N, d, out, pst, ba.BA_BF16, None)
+                                      None, B, H, N, d, out, pst, ba.BA_BF16, None)
 
 
 def test_attention_strided_rejections(L):
@@ -165,7 +200,7 @@ def test_attention_strided_rejections(L):
     assert attn_s(L, st=ba_strides(2048, 32, 128)) == INV                  # heads overlap channels
     assert attn_s(L, st=ba_strides(2048, 64, 0)) == INV                    # tokens alias
     assert attn_s(L, st=ba_strides(2048, 64, 64)) == INV                   # tokens land on the next head
-    # the span of the view reaches an input (vsum at A(7))
-    assert attn_s(L, out=ctypes.c_void_p(P + 7 * (1 << 32) - 1024)) == INV
+    # the span of the view reaches an input (vscale at A(6))
+    assert attn_s(L, out=ctypes.c_void_p(P + 6 * (1 << 32) - 1024)) == INV
     assert attn_s(L, d=129) == UNS
     assert attn_s(L, st=ba_strides(1 << 33, 1 << 32, 64), N=1) == UNS   # head stride above 2^31 - 1

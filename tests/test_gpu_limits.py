@@ -30,12 +30,12 @@ def test_max_tokens_uniform_extreme_sums(d, dt):
     col = np.array([(1 if c % 2 == 0 else -1) * (c + 1) / 8.0 for c in range(d)], np.float32)
     v = np.broadcast_to(col, (1, 1, N, d)).copy()              # every row the same
     qd, kd, vd = (to_dev(to_bits(x, dt), dt) for x in (q, k, v))
-    qbits, qmu, kbits, kmu, vq, vscale, vsum = ba.prepare(qd, kd, vd)
+    qbits, qmu, kbits, kmu, vq, vscale = ba.prepare(qd, kd, vd)
     out = torch.empty_like(qd)
-    ba.ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, None, out)
+    ba.ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, None, out)
     torch.cuda.synchronize()
     assert bool((vq.abs() == 127).all())                       # every v8 at the int8 limit
-    assert np.array_equal(vsum.cpu().numpy().ravel(), np.where(col > 0, 127, -127) * N)
+    # the kernel's channel sums reach 127 * N and its P.V sum 255 * 127 * N
     got = out.float().cpu().numpy()
     want = from_bits(to_bits(v, dt), dt)
     err = np.abs(got - want).max() / np.abs(want).max()
@@ -52,9 +52,9 @@ def test_max_tokens_widest_relpos_table():
     table = (0.1 * rng.standard_normal((H, (2 * side - 1) ** 2))).astype(np.float32)
     qd, kd, vd = (to_dev(b, dt) for b in (q16, k16, v16))
     bias = ba.Bias(ba.BA_BIAS_RELPOS, torch.from_numpy(table).cuda(), 0, side, side, 0)
-    qbits, qmu, kbits, kmu, vq, vscale, vsum = ba.prepare(qd, kd, vd)
+    qbits, qmu, kbits, kmu, vq, vscale = ba.prepare(qd, kd, vd)
     out = torch.empty_like(qd)
-    ba.ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, vsum, bias, out)
+    ba.ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out)
     torch.cuda.synchronize()
 
     qb, qm = oracle.pack(q16, dt)

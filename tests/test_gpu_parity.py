@@ -1,9 +1,11 @@
 """Parity of the gfx950 library with the CPU oracle, through the C ABI.
 
-Bar: sign bits, integer Hamming scores and int8 V bit-exact; mu and V scales
-exact; attention outputs within 2e-2 * max|V| of the oracle and of the
-unquantised reference (the bound stated for this method's kernel; the
-measured ratio is printed and is far smaller).
+Bar: sign bits, integer Hamming scores (from every Q.K route of the fused
+kernel) and int8 V bit-exact; mu and V scales exact; attention outputs
+within 1 ulp of the oracle's rounded output in every row without a near-tie
+p8, and within the near-tie bound of tests/parity.py elsewhere; all outputs
+also within 2e-2 * max|V| of the oracle and of the unquantised reference
+(the bound stated for this method's kernel).
 """
 import numpy as np
 import pytest
@@ -11,7 +13,8 @@ import torch
 
 import bit_qk_attention_amd as ba
 import oracle
-from gpu_helpers import DeviceRun, to_dev, vmax
+from gpu_helpers import DeviceRun, out_bits, tdtype, to_dev, vmax
+from parity import check_output
 from workloads import BF16, F16, from_bits, make, to_bits
 
 pytestmark = pytest.mark.gpu
@@ -31,22 +34,29 @@ REDUCED = {
 }
 
 
-def check_out(run, rows=None, label=""):
+def check_out(run, rows=None, label="", out=None, qmu=None, kmu=None):
+    """The output of run (or `out`, computed from run's inputs with the given
+    scales) against the oracle: the parity bar of tests/parity.py, and
+    2e-2 * max|V| against the unquantised reference."""
     inp = run.inp
     s = inp.spec
-    got = run.out_f32().reshape(s.B * s.H, s.N, s.d)
-    kw = {} if rows is None else dict(bh0=rows[0], nbh=rows[1], row0=rows[2], nrows=rows[3])
-    ref = oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias, **kw)
+    out = run.out if out is None else out
+    odt = F16 if out.dtype == torch.float16 else BF16
+    BH = s.B * s.H
+    bh0, nbh, row0, nrows = (0, BH, 0, s.N) if rows is None else rows
+    kw = dict(bh0=bh0, nbh=nbh, row0=row0, nrows=nrows, qmu=qmu, kmu=kmu)
+    ref = oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias, out_dtype=odt, want_e255=True, **kw)
     fp, _ = oracle.attention_fp(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias, **kw)
-    if rows is not None:
-        got = got[rows[0]:rows[0] + rows[1], rows[2]:rows[2] + rows[3]]
+    got_bits = out_bits(out).reshape(BH, s.N, s.d)[bh0:bh0 + nbh, row0:row0 + nrows]
+    vq, vs = oracle.quant_v(inp.v, s.dtype)
+    vq = vq.reshape(BH, s.N, s.d)[bh0:bh0 + nbh]
+    vs = vs.reshape(BH, s.d)[bh0:bh0 + nbh]
     vm = vmax(inp)
-    e_q = np.abs(got - ref.out).max() / vm
-    e_fp = np.abs(got - fp).max() / vm
-    print(f"{label or s.name}: max|gpu-oracle|/max|V| = {e_q:.2e}, max|gpu-fp|/max|V| = {e_fp:.2e}")
-    assert np.isfinite(got).all()
-    assert e_q <= TOL and e_fp <= TOL
-    return e_q, e_fp
+    stats = check_output(got_bits, ref, vq, vs, odt, vm, label=label or s.name, loose=TOL)
+    e_fp = np.abs(from_bits(got_bits, odt) - fp).max() / vm
+    print(f"{label or s.name}: max|gpu-fp|/max|V| = {e_fp:.2e}")
+    assert e_fp <= TOL
+    return stats
 
 
 @pytest.mark.parametrize("name", sorted(REDUCED))
@@ -63,9 +73,11 @@ def test_prepass_bit_exact(name):
     vq, vs = oracle.quant_v(inp.v, s.dtype)
     assert np.array_equal(run.vq.cpu().numpy(), vq)
     assert np.array_equal(run.vscale.cpu().numpy(), vs)
-    assert np.array_equal(run.vsum.cpu().numpy(), oracle.channel_sums(vq))
 
 
+# sigma comes from the fused kernel's own Q.K routes (staged tiles, keys
+# straight from global memory, and at 65..96 channels the raw-word route);
+# an element on which they disagree would read 0x7FFFFFFF
 @pytest.mark.parametrize("name", sorted(REDUCED))
 def test_hamming_bit_exact(name):
     inp = make(name, **REDUCED[name])
@@ -76,6 +88,28 @@ def test_hamming_bit_exact(name):
     qb, _ = oracle.pack(inp.q, s.dtype)
     kb, _ = oracle.pack(inp.k, s.dtype)
     assert np.array_equal(sig.cpu().numpy(), oracle.hamming(qb, kb, s.d))
+
+
+# every head dim class (1-4 channel blocks, one or two fp4 k-steps), ragged
+# key tiles and 32-key blocks, windows that start and end inside a 128-query
+# block
+@pytest.mark.parametrize("d", [1, 16, 31, 40, 64, 65, 72, 96, 97, 128])
+@pytest.mark.parametrize("N,win", [(333, (0, 333)), (1000, (130, 300)), (64, (63, 1))])
+def test_hamming_windows_every_route(d, N, win):
+    dt = BF16 if d % 2 == 0 else F16
+    rng = np.random.default_rng(d * 1009 + N)
+    x = rng.standard_normal((2, 1, 3, N, d)).astype(np.float32)
+    x[0, 0, 1, :5] = 0.0  # zero queries: all bits clear
+    q16, k16 = to_bits(x[0], dt), to_bits(x[1], dt)
+    qb, _ = oracle.pack(q16, dt)
+    kb, _ = oracle.pack(k16, dt)
+    qd, kd = to_dev(q16, dt), to_dev(k16, dt)
+    qbits, _, kbits, _ = ba.pack_qk(qd, kd)
+    r0, nr = win
+    sig = torch.empty((2, nr, N), dtype=torch.int32, device="cuda")
+    ba.ba_debug_hamming_scores(qbits, kbits, d, 1, 2, r0, nr, sig)
+    want = oracle.hamming(qb, kb, d, bh0=1, nbh=2, row0=r0, nrows=nr)
+    assert np.array_equal(sig.cpu().numpy(), want)
 
 
 @pytest.mark.parametrize("name", sorted(REDUCED))
@@ -100,9 +134,7 @@ def test_head_dims(d):
 def test_output_dtype_other_than_input():
     inp = make("dit_256", B=1, H=2, N=100)
     run = DeviceRun(inp, out_dt=F16)
-    ref = oracle.attention(inp.q, inp.k, inp.v, BF16)
-    got = run.out_f32().reshape(2, 100, 72)
-    assert np.abs(got - ref.out).max() <= TOL * vmax(inp)
+    check_out(run, label="bf16 in, fp16 out")
 
 
 def test_zero_queries_give_uniform_attention():
@@ -163,6 +195,22 @@ def test_relpos_equals_materialised_dense():
     assert torch.equal(run_rp.out, run_d.out)
 
 
+def test_relpos_grid_rows_equal_materialised_dense():
+    """The grid-run relative-position path (no prefix token, grid width a
+    multiple of 16: 16 consecutive keys read one reversed table window), at
+    the long sequences' real shape (64 x 64 grid, 4096 tokens, d = 64),
+    against the same table materialised as a dense fp32 bias."""
+    from test_oracle_attention import relpos_dense
+    inp = make("long_4k_rp", B=1, H=2)
+    run_rp = DeviceRun(inp)
+    dense = relpos_dense(inp.bias_data, 64, 64, 0)
+    inp2 = make("long_4k_rp", B=1, H=2)
+    inp2.bias_kind, inp2.bias_data, inp2.bias_dtype, inp2.bias_batch_stride = 1, dense, 2, 0
+    run_d = DeviceRun(inp2)
+    assert torch.equal(run_rp.out, run_d.out)
+    check_out(run_rp, rows=(0, 2, 2040, 16), label="grid rows, sampled")
+
+
 def test_deterministic():
     run = DeviceRun(make("dit_512", B=2, H=2, N=300))
     assert torch.equal(run.out, run.rerun())
@@ -175,8 +223,8 @@ def test_key_permutation():
     inp.k = np.ascontiguousarray(inp.k[:, :, perm])
     inp.v = np.ascontiguousarray(inp.v[:, :, perm])
     run1 = DeviceRun(inp)
-    d = (run0.out.float() - run1.out.float()).abs().max().item()
-    assert d <= 2e-3 * vmax(inp)
+    # the same scores per key and integer sums: the same bits
+    assert torch.equal(run0.out, run1.out)
 
 
 # V quantisation over the launch shapes the library chooses between: whole
@@ -199,12 +247,11 @@ def test_quant_v_launch_shapes(B, H, N, d, dt):
         v[..., 3] = 0.0        # an all-zero channel
     bits = to_bits(v, dt)
     vd = to_dev(bits, dt)
-    vq, vs, vsum = ba.quant_v(vd)
+    vq, vs = ba.quant_v(vd)
     torch.cuda.synchronize()
     rq, rs = oracle.quant_v(bits, dt)
     assert np.array_equal(vq.cpu().numpy(), rq)
     assert np.array_equal(vs.cpu().numpy(), rs)
-    assert np.array_equal(vsum.cpu().numpy(), oracle.channel_sums(rq))
 
 
 # every bias kind at head dims that select the smaller kernel instantiations
@@ -258,7 +305,6 @@ def test_pack_qk_quant_v_one_call(B, H, N, d, dt):
     assert np.array_equal(got[1].cpu().numpy(), qm)
     assert np.array_equal(got[4].cpu().numpy(), vq)
     assert np.array_equal(got[5].cpu().numpy(), vs)
-    assert np.array_equal(got[6].cpu().numpy(), oracle.channel_sums(vq))
 
 
 # sign bits and scales of the special 16-bit values, on the cooperative
@@ -309,17 +355,9 @@ def test_given_mu_per_head(name):
     qm = run.qmu.mean(dim=2, keepdim=True).expand_as(run.qmu).contiguous()
     km = (0.5 * run.kmu.mean(dim=2, keepdim=True)).expand_as(run.kmu).contiguous()
     out = torch.empty_like(run.out)
-    ba.ba_attention_fwd(run.qbits, qm, run.kbits, km, run.vq, run.vscale, run.vsum, run.lib_bias, out)
+    ba.ba_attention_fwd(run.qbits, qm, run.kbits, km, run.vq, run.vscale, run.lib_bias, out)
     torch.cuda.synchronize()
-    qm_h, km_h = qm.cpu().numpy(), km.cpu().numpy()
-    ref = oracle.attention(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias, qmu=qm_h, kmu=km_h)
-    fp, _ = oracle.attention_fp(inp.q, inp.k, inp.v, s.dtype, bias=run.ora_bias, qmu=qm_h, kmu=km_h)
-    got = out.float().cpu().numpy().reshape(s.B * s.H, s.N, s.d)
-    vm = vmax(inp)
-    e_q = np.abs(got - ref.out).max() / vm
-    e_fp = np.abs(got - fp).max() / vm
-    print(f"{name} per-head mu: max|gpu-oracle|/max|V| = {e_q:.2e}, max|gpu-fp|/max|V| = {e_fp:.2e}")
-    assert e_q <= TOL and e_fp <= TOL
+    check_out(run, out=out, qmu=qm.cpu().numpy(), kmu=km.cpu().numpy(), label=f"{name} per-head mu")
 
 
 def test_given_mu_zero_no_bias():
@@ -328,7 +366,7 @@ def test_given_mu_zero_no_bias():
     run = DeviceRun(inp)
     z = torch.zeros_like(run.qmu)
     out = torch.empty_like(run.out)
-    ba.ba_attention_fwd(run.qbits, z, run.kbits, z, run.vq, run.vscale, run.vsum, None, out)
+    ba.ba_attention_fwd(run.qbits, z, run.kbits, z, run.vq, run.vscale, None, out)
     torch.cuda.synchronize()
     vq, vs = oracle.quant_v(inp.v, s.dtype)
     mean = vq.astype(np.float64).sum(axis=2) * vs.astype(np.float64) / s.N  # [B,H,d]

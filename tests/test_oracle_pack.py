@@ -137,23 +137,22 @@ def test_quant_v_invariants(oracle_lib):
     assert vq.min() >= -127
 
 
-def test_channel_sums_closed_forms(oracle_lib):
+def test_quant_v_closed_forms(oracle_lib):
     # a constant channel quantises to +-127 in every token; a channel with one
-    # non-zero token sums to +-127; all-zero channels sum to 0
+    # non-zero token has +-127 there and 0 elsewhere; all-zero channels give 0
     v = np.zeros((1, 2, 30, 16), np.float32)
     v[0, 0, :, 3] = 2.5
     v[0, 1, :, 5] = -0.75
     v[0, 0, 7, 9] = 1.0
-    vq, _ = oracle.quant_v(to_bits(v, F16), F16)
-    cs = oracle.channel_sums(vq)
-    assert cs.shape == (1, 2, 16) and cs.dtype == np.int32
-    assert cs[0, 0, 3] == 127 * 30 and cs[0, 1, 5] == -127 * 30 and cs[0, 0, 9] == 127
-    assert np.count_nonzero(cs) == 3
-    # quantisation is odd-symmetric, so negating V negates every channel sum
+    vq, vs = oracle.quant_v(to_bits(v, F16), F16)
+    assert np.all(vq[0, 0, :, 3] == 127) and np.all(vq[0, 1, :, 5] == -127)
+    assert vq[0, 0, 7, 9] == 127 and np.count_nonzero(vq) == 2 * 30 + 1
+    assert vs[0, 0, 3] == np.float32(2.5) / np.float32(127) and vs[0, 1, 0] == 0.0
+    # quantisation is odd-symmetric: negating V negates every code
     rv = np.random.default_rng(12).standard_normal((2, 2, 40, 24)).astype(np.float32)
-    pos = oracle.channel_sums(oracle.quant_v(to_bits(rv, BF16), BF16)[0])
-    neg = oracle.channel_sums(oracle.quant_v(to_bits(-rv, BF16), BF16)[0])
-    assert np.array_equal(neg, -pos) and np.any(pos != 0)
+    pos = oracle.quant_v(to_bits(rv, BF16), BF16)
+    neg = oracle.quant_v(to_bits(-rv, BF16), BF16)
+    assert np.array_equal(neg[0], -pos[0]) and np.array_equal(neg[1], pos[1]) and np.any(pos[0] != 0)
 
 
 def test_hand_example_pack_and_quant(oracle_lib):
