@@ -39,6 +39,18 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, tera-ops/s
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+# Vector ALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one lane-op
+# per lane per cycle (a wave64 instruction takes 4 cycles on a 16-lane SIMD).
+VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # 39.32 tera lane-ops/s
+
+
+def valu_ops_per_score(s) -> float:
+    """Vector issue slots one score element needs at least, whatever the
+    tiling: the score's scaling (sigma * mu_k, then one fma into base-2
+    units; one more fma with a bias), one exp2 (a transcendental: two issue
+    slots), the u8 conversion, the row-sum add, and half a slot for the row
+    maximum (a three-input max takes two elements)."""
+    return 6.5 + (1.0 if s.bias != "none" else 0.0)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "bit_qk_attention_amd", "csrc", "attention.hip")
 
@@ -49,12 +61,12 @@ def kernel_sha() -> str:
 
 def algorithmic_bytes(s) -> int:
     """HBM bytes one attention launch must move at minimum: packed Q and K
-    (bits + scale), int8 V + channel scales + channel sums, the output, and
-    the bias (a shared dense bias once, not per batch element; a relative-
-    position table)."""
+    (bits + scale), int8 V + channel scales, the output, and the bias (a
+    shared dense bias once, not per batch element; a relative-position
+    table)."""
     W = (s.d + 31) // 32
     BH, N, d = s.B * s.H, s.N, s.d
-    nb = 2 * BH * N * (4 * W + 4) + BH * N * d + 8 * BH * d + 2 * BH * N * d
+    nb = 2 * BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d + 2 * BH * N * d
     if s.bias.startswith("dense"):
         esz = 4 if s.bias == "dense_f32" else 2
         nb += (1 if s.bias_shared else s.B) * s.H * N * N * esz
@@ -228,6 +240,8 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
         "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
         "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
+        "scores": s.B * s.H * s.N * s.N,
+        "valu_tops": s.B * s.H * s.N * s.N * valu_ops_per_score(s) / (attn_ms * 1e-3) / 1e12,
     }
 
 
@@ -350,13 +364,18 @@ def main() -> int:
             "attn_ms": round(r["attn_ms"], 5), "attn_min_ms": round(r["attn_min_ms"], 5),
             "attn_tops": round(r["attn_tops"], 3),
             "roofline": {
-                "bound": "mfma", "achieved": round(r["attn_tops"], 3), "peak": INT8_PEAK_TOPS,
-                "unit": "TFLOP/s", "frac": round(r["attn_tops"] / INT8_PEAK_TOPS, 4),
+                "bound": "alu", "achieved": round(r["valu_tops"], 3), "peak": round(VALU_PEAK_TLANEOPS, 2),
+                "unit": "T lane-ops/s", "frac": round(r["valu_tops"] / VALU_PEAK_TLANEOPS, 4),
                 "traffic": traffic_for(name),
-                "kernel": "attn_fwd_kernel", "ops_per_launch": r["ops"],
-                "note": "int8 tera-ops/s: effective ops 4*B*H*N^2*d per launch / launch time (HIP events; "
-                        "median of 5 runs of back-to-back launches)",
+                "kernel": "attn_fwd_kernel", "scores_per_launch": r["scores"],
+                "lane_ops_per_score": valu_ops_per_score(s),
+                "note": "vector-ALU bound: B*H*N^2 scores x the minimum issue slots per score / launch time "
+                        "(HIP events on the launch stream; median of 5 runs of back-to-back launches); peak "
+                        "256 CUs x 64 lanes x 2.4 GHz",
             },
+            "int8_mfma": {"achieved": round(r["attn_tops"], 3), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                          "frac": round(r["attn_tops"] / INT8_PEAK_TOPS, 4),
+                          "note": "effective ops 4*B*H*N^2*d per launch / launch time"},
             "hbm": {"alg_bytes_per_launch": r["alg_bytes"], "achieved_GBs": round(r["attn_gbs"], 1),
                     "peak_GBs": HBM_PEAK_GBS, "frac": round(r["attn_gbs"] / HBM_PEAK_GBS, 4)},
         }
@@ -370,7 +389,8 @@ def main() -> int:
             line["secondary"] = {"config": config_of(r2["spec"]), "value": round(r2["tops"], 3),
                                  "ms_per_step": round(r2["step_ms"], 5), "attn_ms": round(r2["attn_ms"], 5),
                                  "attn_tops": round(r2["attn_tops"], 3),
-                                 "frac_int8_peak": round(r2["attn_tops"] / INT8_PEAK_TOPS, 4)}
+                                 "frac_int8_peak": round(r2["attn_tops"] / INT8_PEAK_TOPS, 4),
+                                 "frac_valu_peak": round(r2["valu_tops"] / VALU_PEAK_TLANEOPS, 4)}
         line["cpu_baseline"] = None
         if not args.all and not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(r["inp"])

@@ -222,7 +222,7 @@ struct IntC {
 template <int NKB, int BIAS, bool RAWK>
 struct KeyStage {
   static constexpr int KROW = 32 * NKB;
-  static constexpr int NT = is_relpos(BIAS) ? kTblMax + 4 : 4;  // [kTblMax]: a 0.0 slot
+  static constexpr int NT = is_relpos(BIAS) ? kTblMax + 4 : 4;  // [0]: a 0.0 slot, then the window
   static constexpr int NB = BIAS == BIAS_DENSE_F16 ? kQB * kBC : 8;
   static constexpr int NKO = is_relpos(BIAS) ? kBC : 4;
   uint8_t kx[RAWK ? 16 : kBC * KROW];  // fp4 K operand (unused when the waves expand raw words)
@@ -326,6 +326,11 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   const int64_t bh = (int64_t)b * p.H + h;
   const int qi = qb * kQB + wave * kQW + ql;
   const bool qvalid = qi < N;
+  // a wave whose 32 queries are all past N (the last query block of a head)
+  // skips the score work of pass 1 and of the interleaved pass-2 tile: it
+  // still stages its share of the tiles and adds its share of the V channel
+  // sums
+  const bool wave_live = qb * kQB + wave * kQW < N;
   const int qc = qvalid ? qi : N - 1;  // clamped query index for addressing
 
   // ---- query operand: fp4 signs, padding channels zero ----
@@ -435,21 +440,26 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   };
   // Window index of (query, key) = qwin - koff[key]: qwin = (r_i + gh - 1) * T2
   // + c_i + gw - 1 depends on the query only, koff = (r_j + dr_lo) * T2 + c_j
-  // on the key and the tile's window start dr_lo; -1 marks keys with no grid
-  // position or past N. Written by wave 2 while the tile is staged (plain LDS
-  // stores, visible after the step's barrier).
-  const int qwin = (q_rr + gh - 1) * T2 + q_cc + gw - 1;
+  // on the key and the tile's window start dr_lo. The window sits at slot 1
+  // of the stage's table, slot 0 holds 0.0, and the slot of a pair is the
+  // unsigned saturating difference qwin1 - koff with qwin1 = qwin + 1 for a
+  // query on the grid, 0 for one off it, and koff = kKoffNone for a key off
+  // the grid or past N: both land on slot 0 (bias 0), every pair on the grid
+  // on slot >= 1. koff is written by wave 2 while the tile is staged (plain
+  // LDS stores, visible after the step's barrier).
+  constexpr int kKoffNone = 0x3FFFFFFF;
+  const int qwin1 = q_grid ? (q_rr + gh - 1) * T2 + q_cc + gw : 0;
   if (is_relpos(BIAS) && tid == 0) {  // the 0.0 slot of each stage's table window
-    ks0.tbl[kTblMax] = 0.0f;
-    ks1.tbl[kTblMax] = 0.0f;
-    if constexpr (NS1 == 3 || NS2 == 3) ks2.tbl[kTblMax] = 0.0f;
+    ks0.tbl[0] = 0.0f;
+    ks1.tbl[0] = 0.0f;
+    if constexpr (NS1 == 3 || NS2 == 3) ks2.tbl[0] = 0.0f;
   }
   auto stage_koff = [&](int t, auto bufc) {
     if (is_relpos(BIAS) && wave == 2) {
       int dr_lo, count;
       tbl_window(t, dr_lo, count);
       const int j = t * kBC + lane;
-      int ko = -1;
+      int ko = kKoffNone;
       if (j >= npre && j < N) {
         const int r = div_gw(j - npre, gwm);
         ko = (r + dr_lo) * T2 + (j - npre - r * gw);
@@ -550,7 +560,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         if (x0 >= count) break;  // uniform: the wave's later rows are past the window
         // lanes past the window reload its last entry into slots past it
         // (inside tbl, never read), so no lane is masked off
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t*)(sb.tbl + x0), 4, 4 * min(x0 + lane, count - 1),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t*)(sb.tbl + 1 + x0), 4, 4 * min(x0 + lane, count - 1),
                                                  4 * dr_lo * T2, 0, 0);
       }
     }
@@ -782,7 +792,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         // inside the stage would not fit the paired read's offset fields,
         // and the compiler would add it per pair).
         typedef __attribute__((address_space(3))) const float lds_f32;
-        lds_f32* lo = (lds_f32*)(tb + (qwin - sb.koff[jl] - 15));
+        lds_f32* lo = (lds_f32*)(tb + (qwin1 - sb.koff[jl] - 15));
         asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int i = 0; i < 16; ++i) bv[i] = lo[15 - i];
@@ -793,7 +803,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
           const int4 ko = kop[r];
           const int k4[4] = {ko.x, ko.y, ko.z, ko.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bv[4 * r + e] = tb[(q_grid && k4[e] >= 0) ? qwin - k4[e] : kTblMax];
+          for (int e = 0; e < 4; ++e)
+            bv[4 * r + e] = tb[__builtin_elementwise_sub_sat((uint32_t)qwin1, (uint32_t)k4[e])];
         }
       }
 #pragma unroll
@@ -855,6 +866,11 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       scores_kv(sig0, kv0, sc);
       max16(sc);
       scores_kv(sig1, kv1, sc);
+      max16(sc);
+    } else if (TAIL && t * kBC + 32 >= N) {
+      // the ragged tile's second block holds no key < N
+      const v16f sig0 = qk_block(bufc, 0);
+      scores(tail, tail, t, bufc, 0, sig0, sc);
       max16(sc);
     } else {
       const v16f sig0 = qk_block(bufc, 0);
@@ -1030,7 +1046,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     float mx[4][2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) mx[q][0] = mx[q][1] = -INFINITY;
-    auto comp_blk = [&](auto tail, int blk, const Blk& r) {
+    // ALLQ: all four query groups hold a query < N (only the last query
+    // block of a head may have groups past N, which are skipped)
+    auto comp_blk = [&](auto allq, auto tail, int blk, const Blk& r) {
+      constexpr bool ALLQ = decltype(allq)::value;
       constexpr bool TAIL = decltype(tail)::value;
       v8i a[NKB];
 #pragma unroll
@@ -1040,6 +1059,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       const int jb = blk * 32 + 16 * g;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        if (!ALLQ && qb * kQB + kQW * q >= N) continue;  // no query of the group < N
         v16f sg = {};
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk)
@@ -1076,22 +1096,26 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       }
     };
     const int nfb = N >> 5;  // full 32-key blocks
-    Blk ra, rb;
-    if (wave < nfb) load_blk(wave, ra);
-    for (int blk = wave; blk < nfb; blk += 8) {
-      const bool hb = blk + 4 < nfb;
-      if (hb) load_blk(blk + 4, rb);
-      comp_blk(BoolC<false>(), blk, ra);
-      if (hb) {
-        if (blk + 8 < nfb) load_blk(blk + 8, ra);
-        comp_blk(BoolC<false>(), blk + 4, rb);
+    auto split_pass = [&](auto allq) {
+      Blk ra, rb;
+      if (wave < nfb) load_blk(wave, ra);
+      for (int blk = wave; blk < nfb; blk += 8) {
+        const bool hb = blk + 4 < nfb;
+        if (hb) load_blk(blk + 4, rb);
+        comp_blk(allq, BoolC<false>(), blk, ra);
+        if (hb) {
+          if (blk + 8 < nfb) load_blk(blk + 8, ra);
+          comp_blk(allq, BoolC<false>(), blk + 4, rb);
+        }
       }
-    }
-    if ((N & 31) != 0 && wave == (nfb & 3)) {
-      Blk rt;
-      load_blk_tail(nfb, rt);
-      comp_blk(BoolC<true>(), nfb, rt);
-    }
+      if ((N & 31) != 0 && wave == (nfb & 3)) {
+        Blk rt;
+        load_blk_tail(nfb, rt);
+        comp_blk(allq, BoolC<true>(), nfb, rt);
+      }
+    };
+    if (qb * kQB + kQB <= N) split_pass(BoolC<true>());
+    else split_pass(BoolC<false>());
     if constexpr (MODE == MODE_SIGMA_SPLIT) return;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1102,7 +1126,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     __syncthreads();
     mrun = fmaxf(fmaxf(p1red[0][wave][ql], p1red[1][wave][ql]), fmaxf(p1red[2][wave][ql], p1red[3][wave][ql]));
   } else {
-    run_pass(IntC<NS1>(), false, pass1_tile);
+    // (a wave with no live query stages its share of the tiles only; every
+    // wave meets the same barriers)
+    if (wave_live) run_pass(IntC<NS1>(), false, pass1_tile);
+    else run_pass(IntC<NS1>(), false, [](auto, int, auto) {});
     mrun = fmaxf(m0, m1);
     mrun = fmaxf(mrun, partner32(mrun, lane));
   }
@@ -1224,7 +1251,39 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   for (int cb = 0; cb < NCB; ++cb) vt_held[cb] = (v4i){0, 0, 0, 0};
   v4i p_held = (v4i){0, 0, 0, 0};
   constexpr int kValuPerMfma = 10;
+  // a wave with no live query: its share of the channel sums only
+  auto vsum_only = [&](auto tail, int t, auto bufc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (((2 * t + kb) & 3) != wave) continue;
+      v4i vt[NCB];
+      read_vt(bufc, kb, vt);
+      vsum_blk(tail, t, kb, vt);
+    }
+  };
   auto pass2_tile = [&](auto tail, int t, auto bufc) {
+    constexpr bool TAIL = decltype(tail)::value;
+    if (!wave_live) {
+      vsum_only(tail, t, bufc);
+      return;
+    }
+    if (TAIL && t * kBC + 32 >= N) {
+      // ragged tile with no key < N in its second block: the deferred
+      // product of the previous tile, then block 0 alone (nothing deferred)
+      pv_regs(vt_held, p_held);
+      u4v a0[NKB];
+      k_operand(bufc, 0, a0);
+      const v16f sig0 = qk_mfma(a0);
+      v4i vt0[NCB];
+      read_vt(bufc, 0, vt0);
+      vsum_blk(tail, t, 0, vt0);
+      const v4i p0 = probs2(tail, t, bufc, 0, sig0);
+      pv_regs(vt0, p0);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) vt_held[cb] = (v4i){0, 0, 0, 0};
+      p_held = (v4i){0, 0, 0, 0};
+      return;
+    }
     u4v a0[NKB], a1[NKB];
     k_operand(bufc, 0, a0);
     k_operand(bufc, 1, a1);
@@ -1265,8 +1324,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   // workgroups and one or two blocks it measures the same as the
   // interleaved tile, which is kept there).
   auto pass2_tile_lean = [&](auto tail, int t, auto bufc) {
+    constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      if (TAIL && kb == 1 && t * kBC + 32 >= N) break;  // no key < N in the block
       u4v a[NKB];
       k_operand(bufc, kb, a);
       const v16f sig = qk_mfma(a);
@@ -1280,6 +1341,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   constexpr bool LEAN = (NCB == 3 && min_blocks<NCB, BIAS>() == 3) || min_blocks<NCB, BIAS>() == 4;
   __syncthreads();  // pass 1 is done with both buffers
   if constexpr (LEAN) {
+    // (a wave with no live query runs the lean tile on clamped queries and
+    // stores nothing: a check per tile or a second copy of the pass measured
+    // slower on the four-workgroup kernels than the wasted work)
     run_pass(IntC<NS2>(), true, pass2_tile_lean);
   } else {
     run_pass(IntC<NS2>(), true, pass2_tile);

@@ -155,11 +155,13 @@ ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v
  *   m_i      = max_j s_ij,  p_ij = exp(s_ij - m_i)
  *   p8_ij    = rne(255 * p_ij)                  (unsigned 8 bit over [0,1])
  *   A_ic     = sum_j p8_ij * vq_jc              (exact, int32)
- *   out_ic   = A_ic * vscale_c / sum_j p8_ij    rounded to out_dt
- * i.e. the row normaliser is the integer row sum of the quantised P (the
- * weights that multiply V), so each dequantised row of P sums to 1.
+ *   l_i      = sum_j p_ij                       (fp32, the unquantised p)
+ *   out_ic   = A_ic * vscale_c / (255 * l_i)    rounded to out_dt
+ * i.e. the row normaliser is the softmax denominator of the unquantised
+ * probabilities, so the mass of keys whose p8 rounds to 0 still counts.
  * m_i is the exact row maximum (the kernel finds it in a first pass over the
- * keys), so p8 matches the plain definition up to float rounding.
+ * keys), so p8 matches the plain definition up to float rounding. The
+ * kernel uses no scratch memory and allocates nothing.
  * Any int8 vq with any non-negative scales is accepted (the outputs of
  * ba_pack_qk / ba_quant_v or equivalent data; e.g. a learned mu); the
  * kernel needs nothing besides these arrays.

@@ -1,20 +1,22 @@
 """The output parity bar: the library's 16-bit outputs against the oracle's.
 
 No GPU and none of the method's arithmetic here: the oracle (oracle/) gives
-the exact output, its rounding to the 16-bit format (out_bits), the integer
-row normaliser (l) and the unrounded 255 * p~ that each p8 rounds (e255);
-this module only compares.
+the exact output, its rounding to the 16-bit format (out_bits), the row
+normaliser (l, the float sum of the unquantised p~) and the unrounded
+255 * p~ that each p8 rounds (e255); this module only compares.
 
 The bar, per output element:
   * in a row where no 255 * p~ lies within TIE of a rounding tie, the
     library's bits are at most 1 ulp from the oracle's out_bits (the kernel
-    forms the same integers A and sum p8 and differs only in the float
-    rounding of the last multiply);
+    forms the same integer A; its float32 row sum and last multiply differ
+    from the oracle's float64 ones by far less than one 16-bit ulp);
   * in a row with such near-tie keys (float32 scores in the kernel, float64
     in the oracle, may round one of those p8 the other way), the distance to
     the oracle's exact output is at most one 16-bit spacing plus what those
-    keys can move it: each changes A_c by v8_jc and 255 l by 1, i.e. the
-    output by at most (|v8_jc| scale_c + |O_c|) / (255 l - n).
+    keys can move it: each changes A_c by v8_jc, i.e. the output by
+    |v8_jc| scale_c / (255 l). The allowance used, (|v8_jc| scale_c +
+    |O_c|) / (255 l - n), is that bound widened so that it also holds for
+    the integer normaliser (sum p8, which such a key moves by 1).
 The looser bound of the method's statement, 2e-2 * max|V|, is reported and
 checked beside it.
 """
@@ -60,7 +62,7 @@ def tie_allowance(ref, vq: np.ndarray, vscale: np.ndarray):
     frac = e - np.floor(e)
     near = np.abs(frac - 0.5) < TIE
     n = near.sum(-1)                                     # [nbh, nrows]
-    den = np.maximum(255.0 * ref.l - n, 1.0)             # 255 l = sum p8
+    den = np.maximum(255.0 * ref.l - n, 1.0)
     av = np.abs(vq.astype(np.float64)) * vscale[:, None, :].astype(np.float64)  # [nbh, N, d]
     move = np.einsum("hrn,hnd->hrd", near.astype(np.float64), av)
     allow = (move + n[..., None] * np.abs(ref.out)) / den[..., None]
