@@ -1048,7 +1048,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
     for (int q = 0; q < 4; ++q) mx[q][0] = mx[q][1] = -INFINITY;
     // ALLQ: all four query groups hold a query < N (only the last query
     // block of a head may have groups past N, which are skipped)
-    auto comp_blk = [&](auto allq, auto tail, int blk, const Blk& r) {
+    auto comp_blk = [&](auto allq, auto tail, int blk, const Blk& r) __attribute__((always_inline)) {
       constexpr bool ALLQ = decltype(allq)::value;
       constexpr bool TAIL = decltype(tail)::value;
       v8i a[NKB];
