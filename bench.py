@@ -173,6 +173,10 @@ class Workload:
         self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
                                  self.bias, self.out, self.stream)
 
+    def attn_online(self):
+        self.ba.ba_attention_fwd_online(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
+                                        self.bias, self.out, self.stream)
+
     def time(self, fn, iters: int, warmup: int) -> float:
         """Mean ms per call of fn over `iters` calls, HIP events on the stream."""
         torch = self.torch
@@ -233,10 +237,15 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
     runs = sorted(w.time(w.attn, iters=max(steps, 20), warmup=3 if i == 0 else 0) for i in range(5))
     attn_ms = runs[2]
     attn_cold_ms = w.time_cold(w.attn) if cold else None
+    # the one-pass (running maximum) form beside it, d <= 64
+    online_ms = None
+    if s.d <= 64:
+        online_ms = sorted(w.time(w.attn_online, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
+        w.attn()  # leave the two-pass output in place
     nbytes = algorithmic_bytes(s)
     return {
         "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
-        "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms,
+        "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms, "online_ms": online_ms,
         "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
         "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
@@ -384,10 +393,15 @@ def main() -> int:
             line["attn_cold"] = {"ms": round(c, 5), "tops": round(r["ops"] / (c * 1e-3) / 1e12, 3),
                                  "hbm_GBs": round(r["alg_bytes"] / (c * 1e-3) / 1e9, 1),
                                  "note": "single launches after a 512 MB write that evicts L2 and the MALL"}
+        if r["online_ms"] is not None:
+            line["attn_online"] = {"ms": round(r["online_ms"], 5), "vs_two_pass": round(r["online_ms"] / r["attn_ms"], 3),
+                                   "note": "ba_attention_fwd_online: one pass over the keys with a running "
+                                           "row maximum (same timing protocol)"}
         if not args.all and args.secondary:
             r2 = measure(args.secondary, args.steps, args.warmup)
             line["secondary"] = {"config": config_of(r2["spec"]), "value": round(r2["tops"], 3),
                                  "ms_per_step": round(r2["step_ms"], 5), "attn_ms": round(r2["attn_ms"], 5),
+                                 "attn_online_ms": None if r2["online_ms"] is None else round(r2["online_ms"], 5),
                                  "attn_tops": round(r2["attn_tops"], 3),
                                  "frac_int8_peak": round(r2["attn_tops"] / INT8_PEAK_TOPS, 4),
                                  "frac_valu_peak": round(r2["valu_tops"] / VALU_PEAK_TLANEOPS, 4)}

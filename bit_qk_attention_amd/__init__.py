@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
                                                  P, P, P, P, P, P, P]
         L.ba_pack_qk_quant_v_strided.restype = I
         L.ba_attention_fwd.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
+        L.ba_attention_fwd_online.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
         L.ba_attention_fwd.restype = I
         L.ba_attention_fwd_strided.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P,
                                                ctypes.POINTER(ba_strides), I, P]
@@ -209,6 +210,16 @@ def ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream=None)
     B, H, N, d = out.shape
     cb = (bias or Bias()).to_c()
     _check("ba_attention_fwd", lib().ba_attention_fwd(
+        _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale),
+        ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
+
+
+def ba_attention_fwd_online(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream=None) -> None:
+    """The one-pass (running row maximum) form of ba_attention_fwd, d <= 64."""
+    _require_gpu(qbits, qmu, kbits, kmu, vq, vscale, out)
+    B, H, N, d = out.shape
+    cb = (bias or Bias()).to_c()
+    _check("ba_attention_fwd_online", lib().ba_attention_fwd_online(
         _ptr(qbits), _ptr(qmu), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale),
         ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
 

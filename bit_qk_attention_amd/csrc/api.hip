@@ -105,10 +105,11 @@ ba_status prepass_checked(const void* q, const void* k, const void* v, const InV
 ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint32_t* kbits, const float* kmu,
                             const int8_t* vq, const float* vscale, const ba_bias* bias, int B,
                             int H, int N, int d, void* out, const ba_strides& ost, int out_align, int out_dt,
-                            void* stream) {
+                            void* stream, int online = 0) {
   if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !out) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
+  if (online && d > 64) return BA_ERR_UNSUPPORTED;
   if (!dtype16(out_dt)) return BA_ERR_UNSUPPORTED;
   if (!aligned(qbits, 16) || !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(out, out_align) ||
       !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4))
@@ -117,7 +118,7 @@ ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint3
   const int64_t W = (d + 31) / 32;
   AttnArgs a = {};
   a.qbits = qbits; a.qmu = qmu; a.kbits = kbits; a.kmu = kmu; a.vq = vq; a.vscale = vscale;
-  a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt;
+  a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt; a.online = online;
   a.out_sb = ost.batch; a.out_sh = ost.head; a.out_sn = ost.token;
   a.bias_kind = BA_BIAS_NONE;
   int64_t bias_bytes = 0;
@@ -246,6 +247,15 @@ ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32
   const ba_strides dense = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
   return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, bias, B, H, N, d, out, dense, 16, raw(out_dt),
                            stream);
+}
+
+ba_status ba_attention_fwd_online(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,
+                                  const float* kmu, const int8_t* vq, const float* vscale,
+                                  const ba_bias* bias, int B, int H, int N,
+                                  int d, void* out, ba_dtype out_dt, void* stream) {
+  const ba_strides dense = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  return attention_checked(qbits, qmu, kbits, kmu, vq, vscale, bias, B, H, N, d, out, dense, 16, raw(out_dt),
+                           stream, 1);
 }
 
 ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,

@@ -68,7 +68,10 @@ enum { BIAS_NONE = 0, BIAS_DENSE_F32 = 1, BIAS_DENSE_F16 = 2, BIAS_RELPOS = 3, B
        BIAS_RELPOS_ROW = 5 };
 constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_RELPOS_ROW; }
 
-// What the kernel produces. MODE_ATTN: the attention output. The sigma
+// What the kernel produces. MODE_ATTN: the attention output, two passes
+// over the keys (the exact row maximum, then P and P.V). MODE_ONLINE: the
+// same attention in one pass with a running row maximum (see the online
+// pass below; d <= 64). The sigma
 // modes (no bias, no softmax) produce the integer similarity of a window of
 // query rows, each through one Q.K route of the attention:
 //  MODE_SIGMA       the staged-tile route (K words DMA'd into LDS and
@@ -79,7 +82,8 @@ constexpr bool is_relpos(int bias) { return bias == BIAS_RELPOS || bias == BIAS_
 //                   global memory into registers, four query groups);
 // the last two compare their result with what is already in the output and
 // overwrite every element that differs with kSigmaPoison.
-enum { MODE_ATTN = 0, MODE_SIGMA = 1, MODE_SIGMA_RAW = 2, MODE_SIGMA_SPLIT = 3 };
+enum { MODE_ATTN = 0, MODE_SIGMA = 1, MODE_SIGMA_RAW = 2, MODE_SIGMA_SPLIT = 3, MODE_ONLINE = 4 };
+constexpr bool is_attn(int mode) { return mode == MODE_ATTN || mode == MODE_ONLINE; }
 constexpr int32_t kSigmaPoison = 0x7FFFFFFF;  // never a similarity (|sigma| <= 128)
 
 // Workgroups per CU the register allocation must allow (4 waves each; 2 ->
@@ -92,8 +96,10 @@ constexpr int32_t kSigmaPoison = 0x7FFFFFFF;  // never a similarity (|sigma| <= 
 // K words to make room in LDS); the third workgroup wins even where values
 // of the ragged-tile code spill. Two: the fp32 and unaligned dense-bias
 // loads go through registers, and d > 96.
-template <int NCB, int BIAS>
+template <int NCB, int BIAS, int MODE = MODE_ATTN>
 constexpr int min_blocks() {
+  // the online pass holds an fp32 output and two int32 accumulators
+  if (MODE == MODE_ONLINE) return NCB <= 2 ? 3 : 2;
   if ((BIAS == BIAS_NONE || BIAS == BIAS_RELPOS_ROW) && NCB <= 2) return 4;
   return ((BIAS == BIAS_NONE || is_relpos(BIAS) || BIAS == BIAS_DENSE_F16) && NCB <= 2) ||
                  ((BIAS == BIAS_NONE || BIAS == BIAS_DENSE_F16) && NCB == 3)
@@ -252,7 +258,7 @@ struct StageCfg {
   static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS, MODE>()>);
   static constexpr int VSZ = (int)sizeof(VStage<NCB>);
   // less the pass-1 reduction buffer and the channel sums
-  static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS>() - 2048 - 512;
+  static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS, MODE>() - 2048 - 512;
   static constexpr int NS2 = 3 * KS + 3 * VSZ <= BUDGET ? 3 : 2;
   static constexpr int NS1 = 3 * KS + NS2 * VSZ <= BUDGET ? 3 : 2;
 };
@@ -263,10 +269,11 @@ struct StageCfg {
 __device__ __forceinline__ int bswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 template <int NKB, int NCB, int BIAS, int MODE>
-__global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd_kernel(Params p) {
   constexpr bool RAWK = raw_k<NCB, BIAS, MODE>();
   static_assert(!RAWK || NKB == 2, "raw K words: four per key");
-  static_assert(MODE == MODE_ATTN || BIAS == BIAS_NONE, "the sigma modes take no bias");
+  static_assert(is_attn(MODE) || BIAS == BIAS_NONE, "the sigma modes take no bias");
+  static_assert(MODE != MODE_ONLINE || NCB <= 2, "the online pass takes d <= 64");
   using KS = KeyStage<NKB, BIAS, RAWK>;
   using VSt = VStage<NCB>;
   using Cfg = StageCfg<NKB, NCB, BIAS, MODE>;
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
   v8i qop[NKB];
   q_operand(qi, qvalid, qop);
   // (the sigma modes take no scales)
-  const float qmu = (MODE == MODE_ATTN && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
+  const float qmu = (is_attn(MODE) && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
   const float c0 = qmu * p.inv_sqrt_d;  // natural-log units (bias path)
   const float cq = c0 * kLog2e;         // base-2 units (no-bias path)
 
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16, v_src[i],
                                                    j0 * d, 0, 0);
     }
-    if (MODE == MODE_ATTN && wave == 1)
+    if (is_attn(MODE) && wave == 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * lane, 4 * j0, 0, 0);
     dma_tbl(t, bufc);
     stage_koff(t, bufc);
@@ -634,7 +641,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
         copy_v_checked(t, bufc);
       }
     }
-    if (MODE == MODE_ATTN && wave == 1)
+    if (is_attn(MODE) && wave == 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * (lane + j0), 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kbits, (lptr_t*)(sb.kraw + 64 * wave), 4, kw_src + 4 * j0 * W, 0,
                                              0, 0);
@@ -959,6 +966,130 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS>())) void attn_fwd_kerne
       }
     };
     run_pass(IntC<Cfg::NS2>(), false, sigma_tile);
+    return;
+  }
+  if constexpr (MODE == MODE_ONLINE) {
+    // ======== one pass with a running row maximum (FlashAttention-2 order) ========
+    // The keys stream once. Per 32-key block a lane takes the block maximum
+    // of its query (its 16 keys and the partner lane's 16); when the running
+    // maximum m of any query of the wave grows, every lane folds: O <- (O +
+    // A) * exp(m_old - m_new), l <- l * exp(m_old - m_new), A <- 0 (O and A
+    // both hold sums taken against m_old; for a query whose maximum did not
+    // grow the factor is exactly 1). Then p8 =
+    // rne(255 * exp(s - m)) with the current m, l += 255 * exp(s - m), and A
+    // += p8 v8 on the int8 matrix cores. p8 reaches 255 while the int8 MFMA
+    // is signed, and A must fold exactly at any point, so the product takes
+    // p8 as two nibble operands (0..15): A = 16 A_hi + A_lo, both exact.
+    // At the end out = (O + A) * vscale / l.
+    const float sc2 = (BIAS == BIAS_NONE) ? cq : kLog2e;  // score -> base-2 units
+    float mo = -INFINITY;   // running maximum (score units of the pass-1 code)
+    float ngm = 0.0f;       // log2(255) - m * sc2
+    float ls = 0.0f;        // 255 * running sum over this lane's keys
+    v16i ah[NCB], al[NCB];  // A_hi and A_lo since the last fold
+    float of[NCB][16];      // folded output, fp32
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      ah[cb] = (v16i){};
+      al[cb] = (v16i){};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) of[cb][i] = 0.0f;
+    }
+    const int tr_row = 16 * (lane >> 5) + ((lane & 15) >> 1);  // transposing read, as in pass 2
+    const int tr_col = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    auto fold = [&](float alpha) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) of[cb][i] = (of[cb][i] + (float)(16 * ah[cb][i] + al[cb][i])) * alpha;
+        ah[cb] = (v16i){};
+        al[cb] = (v16i){};
+      }
+    };
+    auto oblock = [&](auto tail, int t, auto bufc, int kb) {
+      u4v a[NKB];
+      k_operand(bufc, kb, a);
+      const v16f sig = qk_mfma(a);
+      float sc[16];
+      scores(tail, tail, t, bufc, kb, sig, sc);  // keys past N: -inf
+      float b0 = -INFINITY, b1 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        b0 = fmaxf(fmaxf(b0, sc[i]), sc[i + 1]);
+        b1 = fmaxf(fmaxf(b1, sc[i + 2]), sc[i + 3]);
+      }
+      float bm = fmaxf(b0, b1);
+      bm = fmaxf(bm, partner32(bm, lane));
+      const float mn = fmaxf(mo, bm);
+      if (__builtin_amdgcn_ballot_w64(mn > mo) != 0) {  // wave-uniform
+        const float alpha = mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mo - mn) * sc2);
+        fold(alpha);
+        ls *= alpha;
+        mo = mn;
+        ngm = __builtin_fmaf(-sc2, mo, kLog2_255);
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * r + k], sc2, ngm));
+          ls += e[k];
+        }
+        uint32_t wd = __builtin_amdgcn_cvt_pk_u8_f32(e[0], 0, 0u);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(e[1], 1, wd);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(e[2], 2, wd);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(e[3], 3, wd);
+        hi[r] = (wd >> 4) & 0x0F0F0F0Fu;  // keys past N: p8 = 0 in both
+        lo[r] = wd & 0x0F0F0F0Fu;
+      }
+      const v4i bhi = (v4i){(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const v4i blo = (v4i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+      const uint8_t* vb = pick_v(bufc).vr;
+      const int r0 = kb * 32 + tr_row, r1 = r0 + 8;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const v2i vlo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + vaddr(r0, tr_col + 32 * cb)));
+        const v2i vhi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + vaddr(r1, tr_col + 32 * cb)));
+        const v4i vt = (v4i){vlo[0], vlo[1], vhi[0], vhi[1]};
+        ah[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vt, bhi, ah[cb], 0, 0, 0);
+        al[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vt, blo, al[cb], 0, 0, 0);
+      }
+    };
+    auto otile = [&](auto tail, int t, auto bufc) {
+      constexpr bool TAIL = decltype(tail)::value;
+      oblock(tail, t, bufc, 0);
+      if (!(TAIL && t * kBC + 32 >= N)) oblock(tail, t, bufc, 1);  // (a block holding a key < N)
+    };
+    run_pass(IntC<NS2>(), true, otile);
+    fold(1.0f);
+    const float lr = ls + partner32(ls, lane);  // 255 l over both halves of the keys
+    if (!qvalid) return;
+    const float inv_l = 1.0f / lr;
+    uint16_t* outp = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)h * p.out_sh + (int64_t)qi * p.out_sn;
+    const float* vs = p.vscale + bh * d;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = cb * 32 + 8 * r + 4 * g;  // channels c .. c + 3 of acc[cb][4 r ..]
+        uint16_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = of[cb][4 * r + e] * (vs[min(c + e, d - 1)] * inv_l);
+          o[e] = (c + e < d) ? ((p.out_mode & 1) ? f32_to_f16(x) : f32_to_bf16(x)) : (uint16_t)0;
+        }
+        if (p.out_mode & 2) {
+          if (c < d)
+            *reinterpret_cast<uint2*>(outp + c) =
+                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < d) outp[c + e] = o[e];
+        }
+      }
+    }
     return;
   }
   float mrun;
@@ -1422,22 +1553,22 @@ hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
 
 // Workgroups of an instantiation that the chip holds at once: the CUs times
 // the occupancy its register budget allows.
-template <int NKB, int NCB, int BIAS>
+template <int NKB, int NCB, int BIAS, int MODE>
 hipError_t launch_b(Params p, int nblocks, hipStream_t s) {
-  p.slots = kCUs * min_blocks<NCB, BIAS>();
+  p.slots = kCUs * min_blocks<NCB, BIAS, MODE>();
   p.balance = nblocks <= p.slots ? 1 : 2;
-  return launch_t<NKB, NCB, BIAS>(p, nblocks, s);
+  return launch_t<NKB, NCB, BIAS, MODE>(p, nblocks, s);
 }
 
-template <int NKB, int NCB>
+template <int NKB, int NCB, int MODE = MODE_ATTN>
 hipError_t launch_bias(const Params& p, int bias, int nblocks, hipStream_t s) {
   switch (bias) {
-    case BIAS_NONE: return launch_b<NKB, NCB, BIAS_NONE>(p, nblocks, s);
-    case BIAS_DENSE_F32: return launch_b<NKB, NCB, BIAS_DENSE_F32>(p, nblocks, s);
-    case BIAS_DENSE_F16: return launch_b<NKB, NCB, BIAS_DENSE_F16>(p, nblocks, s);
-    case BIAS_DENSE_ANY: return launch_b<NKB, NCB, BIAS_DENSE_ANY>(p, nblocks, s);
-    case BIAS_RELPOS_ROW: return launch_b<NKB, NCB, BIAS_RELPOS_ROW>(p, nblocks, s);
-    default: return launch_b<NKB, NCB, BIAS_RELPOS>(p, nblocks, s);
+    case BIAS_NONE: return launch_b<NKB, NCB, BIAS_NONE, MODE>(p, nblocks, s);
+    case BIAS_DENSE_F32: return launch_b<NKB, NCB, BIAS_DENSE_F32, MODE>(p, nblocks, s);
+    case BIAS_DENSE_F16: return launch_b<NKB, NCB, BIAS_DENSE_F16, MODE>(p, nblocks, s);
+    case BIAS_DENSE_ANY: return launch_b<NKB, NCB, BIAS_DENSE_ANY, MODE>(p, nblocks, s);
+    case BIAS_RELPOS_ROW: return launch_b<NKB, NCB, BIAS_RELPOS_ROW, MODE>(p, nblocks, s);
+    default: return launch_b<NKB, NCB, BIAS_RELPOS, MODE>(p, nblocks, s);
   }
 }
 
@@ -1497,6 +1628,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int64_t nblocks = (int64_t)p.nqb * a.B * a.H;
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int ncb = (a.d + 31) / 32;
+  if (a.online) {
+    switch (ncb) {
+      case 1: return launch_bias<1, 1, MODE_ONLINE>(p, bias, (int)nblocks, s);
+      case 2: return launch_bias<1, 2, MODE_ONLINE>(p, bias, (int)nblocks, s);
+      default: return hipErrorInvalidValue;  // d > 64 (checked by the caller)
+    }
+  }
   switch (ncb) {
     case 1: return launch_bias<1, 1>(p, bias, (int)nblocks, s);
     case 2: return launch_bias<1, 2>(p, bias, (int)nblocks, s);

@@ -96,6 +96,7 @@ struct AttnArgs {
   void* out;
   int out_dt;
   int64_t out_sb, out_sh, out_sn;  // element strides of out's [B, H, N, d] view
+  int online;                      // one pass with a running maximum (d <= 64)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

@@ -174,6 +174,26 @@ ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu,
                            int B, int H, int N, int d,
                            void* out, ba_dtype out_dt, void* stream);
 
+/* Extension (not one of the four calls): the same attention in one pass
+ * over the keys with a running row maximum, the FlashAttention-2 order that
+ * the pages' kernel keeps (zh section 2.3; nl Methodologie 3). Keys go in
+ * blocks of 32 in index order; for query i and a key j of block b, p8_ij =
+ * rne(255 * exp(s_ij - m_ib)) where m_ib is the maximum of s_i over blocks
+ * 0..b, and the sums gathered so far are scaled by exp(m_old - m_new) (in
+ * fp32) whenever the maximum grows. p8 therefore depends on the key order
+ * and differs from that of ba_attention_fwd, which quantises against the
+ * exact row maximum; the two outputs agree within 2e-2 * max|V|, the bound
+ * that covers this blocking. On MI355X this form is the slower one (its
+ * rescales cost more vector work than the maximum pass of the two-pass
+ * kernel); it is kept for comparison. d <= 64 only (BA_ERR_UNSUPPORTED
+ * otherwise); arguments, layouts and errors as ba_attention_fwd. */
+ba_status ba_attention_fwd_online(const uint32_t* qbits, const float* qmu,
+                                  const uint32_t* kbits, const float* kmu,
+                                  const int8_t* vq, const float* vscale,
+                                  const ba_bias* bias,
+                                  int B, int H, int N, int d,
+                                  void* out, ba_dtype out_dt, void* stream);
+
 /* ba_attention_fwd writing the output through a strided view: element
  * (b, h, i, c) of the result goes to out + b*batch + h*head + i*token + c
  * (e.g. {N*H*d, d, H*d} writes [B, N, H, d], the input layout of an output

@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol(L):
     names = ba.header_symbols()
     assert set(names) == {"ba_packed_words", "ba_pack_qk", "ba_quant_v", "ba_pack_qk_quant_v",
                           "ba_pack_qk_quant_v_strided", "ba_attention_fwd", "ba_attention_fwd_strided",
+                          "ba_attention_fwd_online",
                           "ba_debug_hamming_scores", "ba_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -119,12 +120,12 @@ def test_pack_qk_quant_v_rejections(L):
     assert prep(L, qb=A(1)) == INV    # output aliases the K input
 
 
-def attn(L, bias=None, B=2, H=2, N=16, d=64, out=A(9), out_dt=ba.BA_BF16, **kw):
+def attn(L, bias=None, B=2, H=2, N=16, d=64, out=A(9), out_dt=ba.BA_BF16, fn="ba_attention_fwd", **kw):
     args = dict(qb=A(1), qm=A(2), kb=A(3), km=A(4), vq=A(5), vs=A(6))
     args.update(kw)
     pb = ctypes.byref(bias) if bias is not None else None
-    return L.ba_attention_fwd(args["qb"], args["qm"], args["kb"], args["km"], args["vq"], args["vs"],
-                              pb, B, H, N, d, out, out_dt, None)
+    return getattr(L, fn)(args["qb"], args["qm"], args["kb"], args["km"], args["vq"], args["vs"],
+                          pb, B, H, N, d, out, out_dt, None)
 
 
 def test_attention_rejections(L):
@@ -147,6 +148,15 @@ def test_attention_rejections(L):
     assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, -1)) == INV
     assert attn(L, bias=ba_bias(7, P + 7 * (1 << 32), ba.BA_F32, 0, 0, 0, 0)) == INV
     assert attn(L, N=257 * 4, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 4, 257, 0)) == UNS
+
+
+def test_online_rejections(L):
+    """The one-pass form validates as ba_attention_fwd and takes d <= 64 only."""
+    f = "ba_attention_fwd_online"
+    assert attn(L, qb=None, fn=f) == INV and attn(L, out=A(6), fn=f) == INV
+    assert attn(L, d=0, fn=f) == INV and attn(L, d=65, fn=f) == UNS and attn(L, d=129, fn=f) == UNS
+    assert attn(L, out_dt=ba.BA_F32, fn=f) == UNS
+    assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, 0), fn=f) == INV
 
 
 def test_hamming_rejections(L):
