@@ -13,6 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbinattn.so")
+PROBE_LIB = os.path.join(HERE, "libbaprobe.so")
 SOURCES = ["api.hip", "prepass.hip", "attention.hip"]
 # attention.hip: fmaxf without NaN canonicalisation (scores are never NaN;
 # masked keys are -inf, which stays honoured)
@@ -51,6 +52,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
     os.replace(tmp, LIB)
+    # the microbenchmarks behind the kernel's design (not the attention path)
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "probe.hip"), "-o", tmp], check=True,
+                   stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

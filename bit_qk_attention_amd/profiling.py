@@ -9,6 +9,9 @@
         --fetch <a>/..._counter_collection.csv --write <b>/..._counter_collection.csv \\
         --copy-fetch <c>/... --copy-write <d>/... --copy-bytes N --out file.json
 
+    # instruction issue rates and the three Q.K routes on the GPU
+    python -m bit_qk_attention_amd.profiling probe
+
 FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch. The copy kernel
 reads and writes exactly N bytes, so the counter's reading for it gives a
 scale factor (N / measured) applied to the kernel's reading.
@@ -72,6 +75,43 @@ def traffic(kernel, fetch, write, copy_fetch, copy_write, copy_bytes, copy_kerne
     }
 
 
+# probe modes of libbaprobe.so (csrc/probe.hip): name, loop iterations,
+# vector instructions per chain and iteration (rate modes) or None (Q.K modes)
+PROBES = [
+    ("v_fma_f32", 4096, 1),
+    ("v_exp_f32", 2048, 1),
+    ("v_add_f32 + v_cvt_pk_u8_f32", 2048, 2),
+    ("pass-2 mix: mul, fma, exp, add, cvt, xor", 1024, 6),
+    ("sigma by v_xor + v_bcnt (VALU)", 2048, None),
+    ("sigma by 2 x v_mfma_i32_32x32x32_i8", 2048, None),
+    ("sigma by 1 x v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", 2048, None),
+]
+
+
+def probe() -> str:
+    """Run every probe mode; a markdown table of the rates."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(_HERE, "libbaprobe.so"))
+    L.bap_time.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    assert L.bap_count() == len(PROBES)
+    waves_per_simd = 2048 * 4 / 1024  # 2048 workgroups of 4 waves on 1024 SIMDs
+    out = ["| probe | ms per launch | result |", "|---|---|---|"]
+    for mode, (name, iters, ops) in enumerate(PROBES):
+        ms = ctypes.c_float()
+        rc = L.bap_time(mode, iters, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"probe {name}: HIP error {rc}")
+        if ops is not None:
+            per = ms.value * 1e6 / (waves_per_simd * iters * 8 * ops)
+            res = f"{per:.2f} ns per wave instruction per SIMD"
+        else:
+            per = ms.value * 1e6 / (waves_per_simd * iters)
+            tops = 2048 * 4 * iters * 1024 * 64 * 2 / (ms.value * 1e-3) / 1e12
+            res = f"{per:.1f} ns per 32x32 block per SIMD ({tops:.0f} effective TOPS for the sigma alone)"
+        out.append(f"| {name} | {ms.value:.3f} | {res} |")
+    return "\n".join(out)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -86,7 +126,11 @@ def main(argv=None) -> int:
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--copy-kernel", default="copy")
     b.add_argument("--out")
+    sub.add_parser("probe")
     args = ap.parse_args(argv)
+    if args.cmd == "probe":
+        print(probe())
+        return 0
     if args.cmd == "stats":
         print(stats_table(args.csv))
         return 0

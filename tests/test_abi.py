@@ -214,3 +214,17 @@ def test_attention_strided_rejections(L):
     assert attn_s(L, out=ctypes.c_void_p(P + 6 * (1 << 32) - 1024)) == INV
     assert attn_s(L, d=129) == UNS
     assert attn_s(L, st=ba_strides(1 << 33, 1 << 32, 64), N=1) == UNS   # head stride above 2^31 - 1
+
+
+def test_probe_library_loads():
+    """The microbenchmark library (profiling.py probe) is built and rejects
+    bad arguments before any GPU call."""
+    import os
+    L = ctypes.CDLL(os.path.join(os.path.dirname(ba.__file__), "libbaprobe.so"))
+    from bit_qk_attention_amd.profiling import PROBES
+    assert L.bap_count() == len(PROBES)
+    L.bap_time.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    ms = ctypes.c_float()
+    assert L.bap_time(-1, 10, ctypes.byref(ms)) != 0
+    assert L.bap_time(len(PROBES), 10, ctypes.byref(ms)) != 0
+    assert L.bap_time(0, 0, ctypes.byref(ms)) != 0
