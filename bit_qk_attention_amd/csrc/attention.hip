@@ -452,10 +452,12 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   // unsigned saturating difference qwin1 - koff with qwin1 = qwin + 1 for a
   // query on the grid, 0 for one off it, and koff = kKoffNone for a key off
   // the grid or past N: both land on slot 0 (bias 0), every pair on the grid
-  // on slot >= 1. koff is written by wave 2 while the tile is staged (plain
-  // LDS stores, visible after the step's barrier).
+  // on slot >= 1. Both terms are kept in bytes (x 4), so the difference is
+  // the slot's byte offset in the table and needs no shift. koff is written
+  // by wave 2 while the tile is staged (plain LDS stores, visible after the
+  // step's barrier).
   constexpr int kKoffNone = 0x3FFFFFFF;
-  const int qwin1 = q_grid ? (q_rr + gh - 1) * T2 + q_cc + gw : 0;
+  const int qwin1 = q_grid ? 4 * ((q_rr + gh - 1) * T2 + q_cc + gw) : 0;
   if (is_relpos(BIAS) && tid == 0) {  // the 0.0 slot of each stage's table window
     ks0.tbl[0] = 0.0f;
     ks1.tbl[0] = 0.0f;
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       int ko = kKoffNone;
       if (j >= npre && j < N) {
         const int r = div_gw(j - npre, gwm);
-        ko = (r + dr_lo) * T2 + (j - npre - r * gw);
+        ko = 4 * ((r + dr_lo) * T2 + (j - npre - r * gw));
       }
       pick(bufc).koff[lane] = ko;
     }
@@ -799,7 +801,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
         // inside the stage would not fit the paired read's offset fields,
         // and the compiler would add it per pair).
         typedef __attribute__((address_space(3))) const float lds_f32;
-        lds_f32* lo = (lds_f32*)(tb + (qwin1 - sb.koff[jl] - 15));
+        lds_f32* lo = (lds_f32*)(reinterpret_cast<const char*>(tb) + (qwin1 - sb.koff[jl])) - 15;
         asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int i = 0; i < 16; ++i) bv[i] = lo[15 - i];
@@ -811,7 +813,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
           const int k4[4] = {ko.x, ko.y, ko.z, ko.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            bv[4 * r + e] = tb[__builtin_elementwise_sub_sat((uint32_t)qwin1, (uint32_t)k4[e])];
+            bv[4 * r + e] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(tb) +
+                                                            __builtin_elementwise_sub_sat((uint32_t)qwin1, (uint32_t)k4[e]));
         }
       }
 #pragma unroll
