@@ -45,6 +45,9 @@
 //  * A sigma mode of the same kernel writes the integer similarity that its
 //    Q.K path produces (the staged-tile route, the raw-word route and the
 //    pass-1 route straight from global memory), for inspection.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 
 namespace binattn {
@@ -225,10 +228,12 @@ struct IntC {
 // separate __shared__ objects, one per stage, selected at compile time: the
 // compiler then tells a DMA into one stage from reads of another and does
 // not wait for the prefetch before reading.
-template <int NKB, int BIAS, bool RAWK>
+// TBL: the stage holds its tile's relative-position table window (the
+// resident mode keeps one window for all keys instead).
+template <int NKB, int BIAS, bool RAWK, bool TBL = is_relpos(BIAS)>
 struct KeyStage {
   static constexpr int KROW = 32 * NKB;
-  static constexpr int NT = is_relpos(BIAS) ? kTblMax + 4 : 4;  // [0]: a 0.0 slot, then the window
+  static constexpr int NT = TBL ? kTblMax + 4 : 4;  // [0]: a 0.0 slot, then the window
   static constexpr int NB = BIAS == BIAS_DENSE_F16 ? kQB * kBC : 8;
   static constexpr int NKO = is_relpos(BIAS) ? kBC : 4;
   uint8_t kx[RAWK ? 16 : kBC * KROW];  // fp4 K operand (unused when the waves expand raw words)
@@ -253,6 +258,20 @@ template <int NCB, int BIAS, int MODE>
 constexpr bool raw_k() {
   return (BIAS == BIAS_DENSE_F16 && NCB == 3) || MODE == MODE_SIGMA_RAW;
 }
+// Resident mode (heads of at most kResTiles tiles, N <= 256): every tile
+// has a stage of its own, all staged at the start, and both passes read
+// them with no further wait or barrier. For the instantiations whose LDS
+// allows it at their occupancy: no bias, dense fp32, relative position.
+constexpr int kResTiles = 4;
+template <int NKB, int NCB, int BIAS, int MODE>
+constexpr bool res_fits() {
+  if (MODE != MODE_ATTN || NCB > 3) return false;
+  if (!(BIAS == BIAS_NONE || BIAS == BIAS_DENSE_F32 || is_relpos(BIAS))) return false;
+  constexpr int bytes = kResTiles * ((int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS, MODE>(), false>) +
+                                     (int)sizeof(VStage<NCB>)) +
+                        (is_relpos(BIAS) ? 4 * (kTblMax + 4) : 0) + 2048 + 512;
+  return bytes <= 160 * 1024 / min_blocks<NCB, BIAS, MODE>();
+}
 template <int NKB, int NCB, int BIAS, int MODE>
 struct StageCfg {
   static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS, MODE>()>);
@@ -268,13 +287,14 @@ struct StageCfg {
 // 16-byte bank groups.
 __device__ __forceinline__ int bswz(int row) { return (row ^ (row >> 3)) & 7; }
 
-template <int NKB, int NCB, int BIAS, int MODE>
+template <int NKB, int NCB, int BIAS, int MODE, bool RES>
 __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd_kernel(Params p) {
   constexpr bool RAWK = raw_k<NCB, BIAS, MODE>();
   static_assert(!RAWK || NKB == 2, "raw K words: four per key");
   static_assert(is_attn(MODE) || BIAS == BIAS_NONE, "the sigma modes take no bias");
   static_assert(MODE != MODE_ONLINE || NCB <= 2, "the online pass takes d <= 64");
-  using KS = KeyStage<NKB, BIAS, RAWK>;
+  static_assert(!RES || res_fits<NKB, NCB, BIAS, MODE>(), "resident mode outside its instantiations");
+  using KS = KeyStage<NKB, BIAS, RAWK, is_relpos(BIAS) && !RES>;
   using VSt = VStage<NCB>;
   using Cfg = StageCfg<NKB, NCB, BIAS, MODE>;
   constexpr int KROW = KS::KROW, VS = VSt::VS;
@@ -283,7 +303,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   // pass 1 with the keys split over the waves (no staging) when there is no
   // bias; with a bias, staged tiles (a dense bias read row-wise per wave
   // would touch half-used 128-byte lines)
-  constexpr bool P1_SPLIT = BIAS == BIAS_NONE;
+  constexpr bool P1_SPLIT = BIAS == BIAS_NONE && !RES;
   __shared__ float p1red[4][4][kQW];  // per-wave partial row maxima (pass 1 split)
   __shared__ int32_t vtot[32 * NCB];  // channel sums of v8 over the head's keys
   __shared__ __attribute__((aligned(16))) KS ks0;
@@ -292,17 +312,36 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   __shared__ __attribute__((aligned(16))) VSt vs0;
   __shared__ __attribute__((aligned(16))) VSt vs1;
   __shared__ __attribute__((aligned(16))) VSt vs2;
+  // resident mode: tile t in stage t (a runtime index), one table window
+  using KSR = std::conditional_t<RES, KS, char>;
+  using VSR = std::conditional_t<RES, VSt, char>;
+  __shared__ __attribute__((aligned(16))) KSR ksr[RES ? kResTiles : 1];
+  __shared__ __attribute__((aligned(16))) VSR vsr[RES ? kResTiles : 1];
+  __shared__ float tblr[(RES && is_relpos(BIAS)) ? kTblMax + 4 : 1];
   auto pick = [&](auto bufc) -> KS& {
-    constexpr int i = decltype(bufc)::value;
-    if constexpr (i == 0) return ks0;
-    else if constexpr (i == 1) return ks1;
-    else return ks2;
+    if constexpr (std::is_integral_v<decltype(bufc)>) {
+      return ksr[bufc];
+    } else {
+      constexpr int i = decltype(bufc)::value;
+      if constexpr (i == 0) return ks0;
+      else if constexpr (i == 1) return ks1;
+      else return ks2;
+    }
+  };
+  // the stage's relative-position table window (slot 0 holds 0.0)
+  auto tbl_of = [&](KS& sb) -> float* {
+    if constexpr (RES) return tblr;
+    else return sb.tbl;
   };
   auto pick_v = [&](auto bufc) -> VSt& {
-    constexpr int i = decltype(bufc)::value;
-    if constexpr (i == 0) return vs0;
-    else if constexpr (i == 1) return vs1;
-    else return vs2;
+    if constexpr (std::is_integral_v<decltype(bufc)>) {
+      return vsr[bufc];
+    } else {
+      constexpr int i = decltype(bufc)::value;
+      if constexpr (i == 0) return vs0;
+      else if constexpr (i == 1) return vs1;
+      else return vs2;
+    }
   };
 
   const int N = p.N, d = p.d, W = p.W;
@@ -435,9 +474,10 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       wq_hi = div_gw(q1 - npre, gwm);
     }
   }
-  // table rows dr_lo.. of the window tile t needs, and its size in floats
+  // table rows dr_lo.. of the window tile t needs (in the resident mode,
+  // all keys), and its size in floats
   auto tbl_window = [&](int t, int& dr_lo, int& count) {
-    const int j0 = t * kBC, j1 = min(t * kBC + kBC - 1, N - 1);
+    const int j0 = RES ? 0 : t * kBC, j1 = RES ? N - 1 : min(t * kBC + kBC - 1, N - 1);
     dr_lo = 0;
     count = 0;
     if (wq_hi < wq_lo || j1 < npre) return;
@@ -459,9 +499,13 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   constexpr int kKoffNone = 0x3FFFFFFF;
   const int qwin1 = q_grid ? 4 * ((q_rr + gh - 1) * T2 + q_cc + gw) : 0;
   if (is_relpos(BIAS) && tid == 0) {  // the 0.0 slot of each stage's table window
-    ks0.tbl[0] = 0.0f;
-    ks1.tbl[0] = 0.0f;
-    if constexpr (NS1 == 3 || NS2 == 3) ks2.tbl[0] = 0.0f;
+    if constexpr (RES) {
+      tblr[0] = 0.0f;
+    } else {
+      ks0.tbl[0] = 0.0f;
+      ks1.tbl[0] = 0.0f;
+      if constexpr (NS1 == 3 || NS2 == 3) ks2.tbl[0] = 0.0f;
+    }
   }
   auto stage_koff = [&](int t, auto bufc) {
     if (is_relpos(BIAS) && wave == 2) {
@@ -557,8 +601,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   };
   // relative-position window rows of tile t (always in bounds of the table)
   auto dma_tbl = [&](int t, auto bufc) {
-    KS& sb = pick(bufc);
-    if (is_relpos(BIAS)) {
+    float* tb = tbl_of(pick(bufc));
+    if (is_relpos(BIAS) && (!RES || t == 0)) {  // (resident mode: one window, with tile 0)
       int dr_lo, count;
       tbl_window(t, dr_lo, count);
       const auto rs = make_rsrc(static_cast<const float*>(p.bias) + (int64_t)h * T2 * (2 * gh - 1),
@@ -569,7 +613,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
         if (x0 >= count) break;  // uniform: the wave's later rows are past the window
         // lanes past the window reload its last entry into slots past it
         // (inside tbl, never read), so no lane is masked off
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t*)(sb.tbl + 1 + x0), 4, 4 * min(x0 + lane, count - 1),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t*)(tb + 1 + x0), 4, 4 * min(x0 + lane, count - 1),
                                                  4 * dr_lo * T2, 0, 0);
       }
     }
@@ -792,7 +836,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(sc[i], c0, bv[i]);
     } else if (is_relpos(BIAS)) {
-      const float* tb = sb.tbl;
+      const float* tb = tbl_of(sb);
       float bv[16];
       if constexpr (BIAS == BIAS_RELPOS_ROW && !TAIL) {
         // 16 keys on one grid row: a contiguous, reversed window. Its lowest
@@ -956,6 +1000,30 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       else if (sidx == 1) tail(IntC<1>());
       else if constexpr (NS == 3) tail(IntC<2>());
     }
+  };
+  // Resident mode: every tile into a stage of its own (V included), one
+  // wait and one barrier; then each pass is a loop over the stages with no
+  // wait and no barrier.
+  auto res_stage = [&]() {
+    if constexpr (RES) {
+      for (int t = 0; t < ntiles; ++t) {
+        if (t < nfull) dma_tile(t, t, true);
+        else stage_checked(t, t, true);
+      }
+      wait_vm0();
+      for (int t = 0; t < ntiles; ++t) {
+        finish_k(t);
+        if (t < nfull && !p.v_dma) copy_v_checked(t, t);
+      }
+      __syncthreads();
+    }
+  };
+  auto res_pass = [&](bool with_v, auto body) {
+    for (int t = 0; t < nfull; ++t) {
+      body(BoolC<false>(), t, t);
+      if (with_v) progress(t + 1);
+    }
+    if (ragged) body(BoolC<true>(), ntiles - 1, ntiles - 1);
   };
   if constexpr (MODE == MODE_SIGMA || MODE == MODE_SIGMA_RAW) {
     // the Q.K of every staged tile, as pass 2 forms it, written out
@@ -1260,10 +1328,15 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     __syncthreads();
     mrun = fmaxf(fmaxf(p1red[0][wave][ql], p1red[1][wave][ql]), fmaxf(p1red[2][wave][ql], p1red[3][wave][ql]));
   } else {
-    // (a wave with no live query stages its share of the tiles only; every
-    // wave meets the same barriers)
-    if (wave_live) run_pass(IntC<NS1>(), false, pass1_tile);
-    else run_pass(IntC<NS1>(), false, [](auto, int, auto) {});
+    if constexpr (RES) {
+      res_stage();
+      if (wave_live) res_pass(false, pass1_tile);
+    } else {
+      // (a wave with no live query stages its share of the tiles only;
+      // every wave meets the same barriers)
+      if (wave_live) run_pass(IntC<NS1>(), false, pass1_tile);
+      else run_pass(IntC<NS1>(), false, [](auto, int, auto) {});
+    }
     mrun = fmaxf(m0, m1);
     mrun = fmaxf(mrun, partner32(mrun, lane));
   }
@@ -1473,13 +1546,22 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     }
   };
   constexpr bool LEAN = (NCB == 3 && min_blocks<NCB, BIAS>() == 3) || min_blocks<NCB, BIAS>() == 4;
-  __syncthreads();  // pass 1 is done with both buffers
-  if constexpr (LEAN) {
+  if constexpr (RES) {
+    // (the stages stay as pass 1 left them)
+    if constexpr (LEAN) {
+      res_pass(true, pass2_tile_lean);
+    } else {
+      res_pass(true, pass2_tile);
+      pv_regs(vt_held, p_held);
+    }
+  } else if constexpr (LEAN) {
+    __syncthreads();  // pass 1 is done with both buffers
     // (a wave with no live query runs the lean tile on clamped queries and
     // stores nothing: a check per tile or a second copy of the pass measured
     // slower on the four-workgroup kernels than the wasted work)
     run_pass(IntC<NS2>(), true, pass2_tile_lean);
   } else {
+    __syncthreads();  // pass 1 is done with both buffers
     run_pass(IntC<NS2>(), true, pass2_tile);
     pv_regs(vt_held, p_held);
   }
@@ -1548,10 +1630,30 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   }
 }
 
-template <int NKB, int NCB, int BIAS, int MODE = MODE_ATTN>
+template <int NKB, int NCB, int BIAS, int MODE = MODE_ATTN, bool RES = false>
 hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<NKB, NCB, BIAS, MODE>), dim3(nblocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<NKB, NCB, BIAS, MODE, RES>), dim3(nblocks), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// Whether the resident mode takes this launch: at most kResTiles tiles, and
+// for a relative-position bias, the window of table rows that any query
+// block needs against all keys fits the LDS table (as tbl_window computes
+// it on the device).
+bool res_takes(const Params& p, bool relpos) {
+  if (p.N > kResTiles * kBC) return false;
+  if (!relpos) return true;
+  const int gw = p.grid_w, npre = p.n_prefix, N = p.N;
+  if (N - 1 < npre) return true;  // no grid token: an empty window
+  const int T2 = 2 * gw - 1;
+  const int rk_hi = (N - 1 - npre) / gw;
+  for (int qb = 0; qb < p.nqb; ++qb) {
+    const int q0 = qb * kQB, q1 = std::min(q0 + kQB - 1, N - 1);
+    if (q1 < npre) continue;
+    const int wq_lo = (std::max(q0, npre) - npre) / gw, wq_hi = (q1 - npre) / gw;
+    if ((int64_t)(wq_hi - wq_lo + rk_hi + 1) * T2 > kTblMax) return false;
+  }
+  return true;
 }
 
 // Workgroups of an instantiation that the chip holds at once: the CUs times
@@ -1560,6 +1662,9 @@ template <int NKB, int NCB, int BIAS, int MODE>
 hipError_t launch_b(Params p, int nblocks, hipStream_t s) {
   p.slots = kCUs * min_blocks<NCB, BIAS, MODE>();
   p.balance = nblocks <= p.slots ? 1 : 2;
+  if constexpr (res_fits<NKB, NCB, BIAS, MODE>()) {
+    if (res_takes(p, is_relpos(BIAS))) return launch_t<NKB, NCB, BIAS, MODE, true>(p, nblocks, s);
+  }
   return launch_t<NKB, NCB, BIAS, MODE>(p, nblocks, s);
 }
 
