@@ -269,15 +269,15 @@ constexpr bool res_fits() {
   if (!(BIAS == BIAS_NONE || BIAS == BIAS_DENSE_F32 || is_relpos(BIAS))) return false;
   constexpr int bytes = kResTiles * ((int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS, MODE>(), false>) +
                                      (int)sizeof(VStage<NCB>)) +
-                        (is_relpos(BIAS) ? 4 * (kTblMax + 4) : 0) + 2048 + 512;
+                        (is_relpos(BIAS) ? 4 * (kTblMax + 4) : 0) + 2048 + 512 + 512;
   return bytes <= 160 * 1024 / min_blocks<NCB, BIAS, MODE>();
 }
 template <int NKB, int NCB, int BIAS, int MODE>
 struct StageCfg {
   static constexpr int KS = (int)sizeof(KeyStage<NKB, BIAS, raw_k<NCB, BIAS, MODE>()>);
   static constexpr int VSZ = (int)sizeof(VStage<NCB>);
-  // less the pass-1 reduction buffer and the channel sums
-  static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS, MODE>() - 2048 - 512;
+  // less the pass-1 reduction buffer, the channel sums and scales
+  static constexpr int BUDGET = 160 * 1024 / min_blocks<NCB, BIAS, MODE>() - 2048 - 512 - 512;
   static constexpr int NS2 = 3 * KS + 3 * VSZ <= BUDGET ? 3 : 2;
   static constexpr int NS1 = 3 * KS + NS2 * VSZ <= BUDGET ? 3 : 2;
 };
@@ -306,6 +306,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   constexpr bool P1_SPLIT = BIAS == BIAS_NONE && !RES;
   __shared__ float p1red[4][4][kQW];  // per-wave partial row maxima (pass 1 split)
   __shared__ int32_t vtot[32 * NCB];  // channel sums of v8 over the head's keys
+  __shared__ float vscl[128];         // the head's V channel scales (DMA'd ahead of the epilogue)
   __shared__ __attribute__((aligned(16))) KS ks0;
   __shared__ __attribute__((aligned(16))) KS ks1;
   __shared__ __attribute__((aligned(16))) KS ks2;
@@ -398,11 +399,18 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     }
   };
   v8i qop[NKB];
-  q_operand(qi, qvalid, qop);
-  // (the sigma modes take no scales)
-  const float qmu = (is_attn(MODE) && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
-  const float c0 = qmu * p.inv_sqrt_d;  // natural-log units (bias path)
-  const float cq = c0 * kLog2e;         // base-2 units (no-bias path)
+  float c0 = 0.0f;  // mu_q / sqrt(d): natural-log units (bias path)
+  float cq = 0.0f;  // c0 * log2(e): base-2 units (no-bias path)
+  // the query operand and scale (the sigma modes take no scales); the
+  // resident mode loads them after it has started the DMA of the tiles, so
+  // the two memory latencies overlap
+  auto load_q = [&]() {
+    q_operand(qi, qvalid, qop);
+    const float qmu = (is_attn(MODE) && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
+    c0 = qmu * p.inv_sqrt_d;
+    cq = c0 * kLog2e;
+  };
+  if constexpr (!RES) load_q();
 
   const int ntiles = (N + kBC - 1) / kBC;
   const bool ragged = (N % kBC) != 0;
@@ -618,6 +626,29 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       }
     }
   };
+  // V rows of tile t by DMA (v_dma layouts): a full tile (CHECKED false,
+  // the tile's offset as a scalar) or the ragged one (CHECKED true, the
+  // offset in the per-lane part, which the descriptor's range check covers)
+  auto dma_v = [&](auto checked, int t, auto bufc) {
+    constexpr bool CHECKED = decltype(checked)::value;
+    VSt& vb = pick_v(bufc);
+    const int j0 = t * kBC;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (v_on[i])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16,
+                                                 CHECKED ? v_src[i] + j0 * d : v_src[i], CHECKED ? 0 : j0 * d, 0,
+                                                 0);
+  };
+  // the head's V channel scales into vscl (wave 0; entries past d read 0)
+  auto dma_vscale = [&]() {
+    if (wave == 0) {
+      const auto rs = make_rsrc(p.vscale + bh * d, 4u * d);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t*)(vscl + 64 * i), 4, 4 * lane, 256 * i, 0, 0);
+    }
+  };
   // full tile t (all keys < N), all by DMA: V, mu_k and the table window,
   // then the last group (kLastGroup instructions in every wave): the K words
   // and the fp16 bias tile
@@ -625,14 +656,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   auto dma_tile = [&](int t, auto bufc, bool with_v) {
     KS& sb = pick(bufc);
     const int j0 = t * kBC;
-    if (with_v && p.v_dma) {
-      VSt& vb = pick_v(bufc);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (v_on[i])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16, v_src[i],
-                                                   j0 * d, 0, 0);
-    }
+    if (with_v && p.v_dma) dma_v(BoolC<false>(), t, bufc);
     if (is_attn(MODE) && wave == 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * lane, 4 * j0, 0, 0);
     dma_tbl(t, bufc);
@@ -676,16 +700,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     KS& sb = pick(bufc);
     const int j0 = t * kBC;
     if (with_v) {
-      if (p.v_dma) {
-        VSt& vb = pick_v(bufc);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          if (v_on[i])
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lptr_t*)(vb.vr + 1024 * (wave + 4 * i)), 16,
-                                                     v_src[i] + j0 * d, 0, 0, 0);
-      } else {
-        copy_v_checked(t, bufc);
-      }
+      if (p.v_dma) dma_v(BoolC<true>(), t, bufc);
+      else copy_v_checked(t, bufc);
     }
     if (is_attn(MODE) && wave == 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kmu, (lptr_t*)(sb.mk), 4, 4 * (lane + j0), 0, 0, 0);
@@ -1001,20 +1017,26 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       else if constexpr (NS == 3) tail(IntC<2>());
     }
   };
-  // Resident mode: every tile into a stage of its own (V included), one
-  // wait and one barrier; then each pass is a loop over the stages with no
-  // wait and no barrier.
+  // Resident mode: every tile into a stage of its own. The key side of all
+  // tiles (K words, key scales, table window) is DMA'd first and the query
+  // operand loaded meanwhile; one wait, then the V rows of all tiles and the
+  // channel scales are started and pass 1 runs while they land; a second
+  // wait before pass 2. Neither pass waits or synchronises per tile.
   auto res_stage = [&]() {
     if constexpr (RES) {
       for (int t = 0; t < ntiles; ++t) {
-        if (t < nfull) dma_tile(t, t, true);
-        else stage_checked(t, t, true);
+        if (t < nfull) dma_tile(t, t, false);
+        else stage_checked(t, t, false);
       }
+      load_q();
       wait_vm0();
       for (int t = 0; t < ntiles; ++t) {
         finish_k(t);
-        if (t < nfull && !p.v_dma) copy_v_checked(t, t);
+        if (!p.v_dma) copy_v_checked(t, t);
+        else if (t < nfull) dma_v(BoolC<false>(), t, t);
+        else dma_v(BoolC<true>(), t, t);
       }
+      dma_vscale();
       __syncthreads();
     }
   };
@@ -1547,7 +1569,9 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   };
   constexpr bool LEAN = (NCB == 3 && min_blocks<NCB, BIAS>() == 3) || min_blocks<NCB, BIAS>() == 4;
   if constexpr (RES) {
-    // (the stages stay as pass 1 left them)
+    // (the stages stay as pass 1 left them; V and the scales have landed)
+    wait_vm0();
+    __syncthreads();
     if constexpr (LEAN) {
       res_pass(true, pass2_tile_lean);
     } else {
@@ -1556,12 +1580,14 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     }
   } else if constexpr (LEAN) {
     __syncthreads();  // pass 1 is done with both buffers
+    dma_vscale();     // (landed by the first tile's wait)
     // (a wave with no live query runs the lean tile on clamped queries and
     // stores nothing: a check per tile or a second copy of the pass measured
     // slower on the four-workgroup kernels than the wasted work)
     run_pass(IntC<NS2>(), true, pass2_tile_lean);
   } else {
     __syncthreads();  // pass 1 is done with both buffers
+    dma_vscale();
     run_pass(IntC<NS2>(), true, pass2_tile);
     pv_regs(vt_held, p_held);
   }
@@ -1580,7 +1606,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   if (!qvalid) return;
   const float inv_l = 1.0f / lrun;
   uint16_t* outp = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)h * p.out_sh + (int64_t)qi * p.out_sn;
-  const float* vs = p.vscale + bh * d;
+  const float* vs = vscl;
   const int32_t* vsm = vtot;
   if (p.out_mode & 2) {
     // whole groups of 4 channels: channel parameters at fixed offsets from
