@@ -9,6 +9,9 @@
         --fetch <a>/..._counter_collection.csv --write <b>/..._counter_collection.csv \\
         --copy-fetch <c>/... --copy-write <d>/... --copy-bytes N --out file.json
 
+    # SQ counter table (two --pmc passes per workload, see profiles/)
+    python -m bit_qk_attention_amd.profiling sq <root> <workload> ...
+
     # instruction issue rates and the three Q.K routes on the GPU
     python -m bit_qk_attention_amd.profiling probe
 
@@ -88,6 +91,64 @@ PROBES = [
 ]
 
 
+# workload -> (B*H, N): the score count B*H*N^2 of one launch
+SQ_SHAPES = {"deit_tiny": (3, 197), "deit_small": (384, 197), "dit_256": (512, 256), "dit_512": (128, 1024),
+             "long_4k": (32, 4096), "long_4k_rp": (32, 4096), "long_16k": (32, 16384), "long_16k_rp": (32, 16384)}
+
+
+def sq_row(workload: str, csv_a: str, csv_b: str, kernel: str = "attn_fwd_kernel") -> tuple[str, dict]:
+    """One row of the SQ counter table for the two-pass attention kernel of
+    a workload (medians over its dispatches; the one-pass form, MODE 4, is
+    left out), from the two counter passes."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for path in (csv_a, csv_b):
+        for r in csv.DictReader(open(path)):
+            n = r["Kernel_Name"]
+            if kernel not in n:
+                continue
+            inst = n[n.index(kernel):].split(">")[0] + ">"
+            if inst.replace(" ", "").split(",")[3] == "4":  # the one-pass extension
+                continue
+            key = (path, int(r["Dispatch_Id"]))
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[key] = inst
+    med = {}
+    for c in ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES",
+              "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT",
+              "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY"):
+        vals = [v[c] for k, v in per.items() if c in v]
+        if vals:
+            med[c] = median(vals)
+    inst = sorted(set(names.values()))
+    bh, n = SQ_SHAPES[workload]
+    scores = bh * n * n
+    T = med["GRBM_GUI_ACTIVE"] / 8  # cycles per XCD
+    valu = med["SQ_INSTS_VALU"]
+    row = (f"| {workload} | `{', '.join(inst)}` | {T / 2400:.1f} | {64 * valu / scores:.2f} | "
+           f"{64 * med['SQ_INSTS_VALU_TRANS_F32'] / scores:.2f} | {4 * valu / (1024 * T):.0%} | "
+           f"{4 * (valu + med['SQ_INSTS_VALU_TRANS_F32']) / (1024 * T):.0%} | "
+           f"{4 * med['SQ_ACTIVE_INST_VALU'] / (1024 * T):.0%} | {med['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * T):.0%} | "
+           f"{4 * med['SQ_WAVE_CYCLES'] / (256 * T):.1f} | {med['SQ_WAIT_INST_ANY'] / med['SQ_WAVE_CYCLES']:.0%} | "
+           f"{med['SQ_LDS_BANK_CONFLICT'] / med['SQ_ACTIVE_INST_LDS']:.2f} |")
+    return row, med
+
+
+def sq_table(args) -> str:
+    """The SQ counter table: for each workload w, sqa_w/a_counter_collection.csv
+    and sqb_w/b_counter_collection.csv under `root`."""
+    out = ["| workload | kernel | T (us at 2.4 GHz) | VALU / score | exp / score | VALU issue | with exp | "
+           "VALU active | MFMA busy | waves / CU | waiting | LDS conflicts |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    raw = ["| workload | counter | value |", "|---|---|---|"]
+    for w in args.workloads:
+        row, med = sq_row(w, os.path.join(args.root, f"sqa_{w}", "a_counter_collection.csv"),
+                          os.path.join(args.root, f"sqb_{w}", "b_counter_collection.csv"))
+        out.append(row)
+        raw += [f"| {w} | {c} | {v:.4g} |" for c, v in sorted(med.items())]
+    return "\n".join(out) + "\n\nRaw medians:\n\n" + "\n".join(raw)
+
+
 def probe() -> str:
     """Run every probe mode; a markdown table of the rates."""
     import ctypes
@@ -127,9 +188,15 @@ def main(argv=None) -> int:
     b.add_argument("--copy-kernel", default="copy")
     b.add_argument("--out")
     sub.add_parser("probe")
+    c = sub.add_parser("sq")
+    c.add_argument("root", help="folder holding sqa_<workload>/ and sqb_<workload>/")
+    c.add_argument("workloads", nargs="+")
     args = ap.parse_args(argv)
     if args.cmd == "probe":
         print(probe())
+        return 0
+    if args.cmd == "sq":
+        print(sq_table(args))
         return 0
     if args.cmd == "stats":
         print(stats_table(args.csv))
