@@ -50,31 +50,34 @@ __global__ __launch_bounds__(256) void pack_qk_kernel(
 
 // pack_qk for d % 8 == 0: the threads of a block cooperate on whole tokens.
 // The block's token range is a contiguous run of 16-byte chunks (8 channels
-// each, P = d/8 per token); thread i loads chunks i + 256u, u < kPackU (each
-// load of the block one fully coalesced 4 KB run, kPackU of them in flight
+// each, P = d/8 per token); thread i loads chunks i + 256u, u < U (each
+// load of the block one fully coalesced 4 KB run, U of them in flight
 // per thread), forms each chunk's 8 sign bits and a float64 partial sum of
 // |x|. The pieces are combined through LDS: each 32-bit word from its 4
 // chunks, mu from the P partial sums in channel order.
-constexpr int kPackU = 4;
+constexpr int kPackUCoop = 2;
+// U (chunks per thread) is 2 for the standalone packer (4096 tokens: 18.3 ->
+// 17.6 us for the pre-pass against 4) and chosen per launch for the fused
+// pre-pass (launch_prepass).
 // One block of NT threads packs tokens [blk * TB, blk * TB + TB) of x.
-// bits_s and sum_s hold NT * kPackU entries. STR: token t of x starts at
+// bits_s and sum_s hold NT * U entries. STR: token t of x starts at
 // x + t * sx (sx % 8 == 0) instead of x + t * d, so a block's chunks are
 // runs of P pieces, one run per token.
-template <int DT, int NT, bool STR = false>
+template <int DT, int NT, int U, bool STR = false>
 __device__ __forceinline__ void pack_block(const uint16_t* __restrict__ x, int64_t ntok, int d, int64_t blk,
                                            uint32_t* __restrict__ bits, float* __restrict__ mu,
                                            uint32_t* bits_s, double* sum_s, int64_t sx = 0) {
   const int P = d >> 3;                  // chunks per token (1..16)
-  const int TB = NT * kPackU / P;        // whole tokens per block
+  const int TB = NT * U / P;             // whole tokens per block
   const int W = (d + 31) >> 5;
   const int64_t tok0 = blk * TB;
   const int nchunk = (int)min((int64_t)TB, ntok - tok0) * P;  // valid chunks of this block
   const int i = threadIdx.x;
   // c / P for c < 4096 and P <= 16 as (c * ceil(2^16 / P)) >> 16 (exact there)
   const uint32_t pmag = STR ? (65536u + P - 1) / P : 0u;
-  u4v raw[kPackU];
+  u4v raw[U];
 #pragma unroll
-  for (int u = 0; u < kPackU; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int c = i + NT * u;
     const uint16_t* src;
     if constexpr (STR) {
@@ -86,7 +89,7 @@ __device__ __forceinline__ void pack_block(const uint16_t* __restrict__ x, int64
     raw[u] = c < nchunk ? *reinterpret_cast<const u4v*>(src) : (u4v){0u, 0u, 0u, 0u};
   }
 #pragma unroll
-  for (int u = 0; u < kPackU; ++u) {
+  for (int u = 0; u < U; ++u) {
     uint32_t b8 = 0;
     double s = 0.0;
 #pragma unroll
@@ -126,21 +129,21 @@ __global__ __launch_bounds__(256) void pack_qk_coop_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, InView in, int N, int64_t nbph,
     int64_t ntok, int d, uint32_t* __restrict__ qbits, float* __restrict__ qmu,
     uint32_t* __restrict__ kbits, float* __restrict__ kmu, uint32_t* __restrict__ zero, int64_t nzero) {
-  __shared__ uint32_t bits_s[256 * kPackU];
-  __shared__ double sum_s[256 * kPackU];
+  __shared__ uint32_t bits_s[256 * kPackUCoop];
+  __shared__ double sum_s[256 * kPackUCoop];
   if (blockIdx.y == 0)
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nzero; i += (int64_t)gridDim.x * 256) zero[i] = 0u;
   if constexpr (STR) {
     const bool isk = blockIdx.y != 0;
     const int64_t bh = blockIdx.x / nbph, tb = blockIdx.x - bh * nbph;
     const int W = (d + 31) >> 5;
-    pack_block<DT, 256, true>((isk ? k : q) + (bh / in.H) * in.sb + (bh % in.H) * in.sh, N, d, tb,
+    pack_block<DT, 256, kPackUCoop, true>((isk ? k : q) + (bh / in.H) * in.sb + (bh % in.H) * in.sh, N, d, tb,
                               (isk ? kbits : qbits) + bh * N * W, (isk ? kmu : qmu) + bh * N, bits_s, sum_s,
                               in.sn);
   } else if (blockIdx.y == 0) {
-    pack_block<DT, 256>(q, ntok, d, blockIdx.x, qbits, qmu, bits_s, sum_s);
+    pack_block<DT, 256, kPackUCoop>(q, ntok, d, blockIdx.x, qbits, qmu, bits_s, sum_s);
   } else {
-    pack_block<DT, 256>(k, ntok, d, blockIdx.x, kbits, kmu, bits_s, sum_s);
+    pack_block<DT, 256, kPackUCoop>(k, ntok, d, blockIdx.x, kbits, kmu, bits_s, sum_s);
   }
 }
 
@@ -163,7 +166,7 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InVie
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const int64_t ntok = (int64_t)nbh * N;
   if (in.vec) {
-    const int TB = 256 * kPackU / (d / 8);
+    const int TB = 256 * kPackUCoop / (d / 8);
     const bool str = !in.dense(N, d);
     const int64_t nbph = (N + TB - 1) / TB;
     const int64_t nblk = str ? nbh * nbph : (ntok + TB - 1) / TB;
@@ -307,14 +310,16 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
 
 // Heads per 1024-thread block for the register-resident quantiser: the most
 // (a power of two, at most 8) whose T = 1024 / HB threads per head still
-// hold at most 8 rows each (kQvRows when one head takes the whole block),
-// while leaving at least 64 blocks; with fewer heads than that, one head
-// per block keeps each head's rows spread over all 1024 threads.
+// hold at most kQvRows rows each, while leaving at least 64 blocks; with
+// fewer heads than that, one head per block keeps each head's rows spread
+// over all 1024 threads. (At most 8 rows per thread for several heads per
+// block measured slower: DiT-256 pre-pass 18.3 against 15.5 us, two heads
+// per block against four.)
 int quant_heads_per_block(int nbh, int N, int d) {
   const int P = d / 8;
   for (int hb = 8; hb > 1; hb >>= 1) {
     const int T = 1024 / hb;
-    if (T >= P && (int64_t)N <= 8 * (int64_t)(T / P) && nbh >= 64 * hb) return hb;
+    if (T >= P && (int64_t)N <= kQvRows * (int64_t)(T / P) && nbh >= 64 * hb) return hb;
   }
   return 1;
 }
@@ -332,14 +337,14 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
 // (the long-running ones, dispatched first), the rest pack npb blocks of
 // tokens of Q, then npb of K, all with 1024 threads. STR (a strided view):
 // the pack blocks are nbph per head, each within one head.
-template <int DT, bool STR>
+template <int DT, bool STR, int U>
 __global__ __launch_bounds__(1024) void prepass_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, InView in,
     int nbh, int N, int d, int HB, int64_t nvb, int64_t npb, int64_t nbph, uint32_t* __restrict__ qbits,
     float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
     float* __restrict__ vscale) {
-  __shared__ uint32_t bits_s[1024 * kPackU];
-  __shared__ double sum_s[1024 * kPackU];
+  __shared__ uint32_t bits_s[1024 * U];
+  __shared__ double sum_s[1024 * U];
   const int64_t ntok = (int64_t)nbh * N;
   const int64_t b = blockIdx.x;
   if (b < nvb) {
@@ -349,13 +354,13 @@ __global__ __launch_bounds__(1024) void prepass_fused_kernel(
     const int64_t pb = b - nvb - (isk ? npb : 0);
     const int64_t bh = pb / nbph, tb = pb - bh * nbph;
     const int W = (d + 31) >> 5;
-    pack_block<DT, 1024, true>((isk ? k : q) + (bh / in.H) * in.sb + (bh % in.H) * in.sh, N, d, tb,
+    pack_block<DT, 1024, U, true>((isk ? k : q) + (bh / in.H) * in.sb + (bh % in.H) * in.sh, N, d, tb,
                                (isk ? kbits : qbits) + bh * N * W, (isk ? kmu : qmu) + bh * N, bits_s, sum_s,
                                in.sn);
   } else if (b - nvb < npb) {
-    pack_block<DT, 1024>(q, ntok, d, b - nvb, qbits, qmu, bits_s, sum_s);
+    pack_block<DT, 1024, U>(q, ntok, d, b - nvb, qbits, qmu, bits_s, sum_s);
   } else {
-    pack_block<DT, 1024>(k, ntok, d, b - nvb - npb, kbits, kmu, bits_s, sum_s);
+    pack_block<DT, 1024, U>(k, ntok, d, b - nvb - npb, kbits, kmu, bits_s, sum_s);
   }
 }
 
@@ -550,16 +555,28 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
     return dt == BA_F16 ? launch_quant_v_split_ab<BA_F16>(v16, in, nbh, N, d, vq, vscale, s)
                         : launch_quant_v_split_ab<BA_BF16>(v16, in, nbh, N, d, vq, vscale, s);
   }
-  const int TB = 1024 * kPackU / (d / 8);
+  // chunks per thread of the packing blocks: 4, or 2 where 4 would leave
+  // fewer than two blocks per CU in all (DeiT-Small pre-pass 10.3 -> 9.3 us;
+  // with two at DiT-256 and DiT-512 16.0 and 15.8 us against 15.5)
   const bool str = !in.dense(N, d);
-  const int64_t nbph = (N + TB - 1) / TB;
-  const int64_t npb = str ? nbh * nbph : (ntok + TB - 1) / TB;
   const int HB = quant_heads_per_block(nbh, N, d);
   const int64_t nvb = (nbh + HB - 1) / HB;
+  auto pack_blocks = [&](int u, int64_t& nbph) {
+    const int TB = 1024 * u / (d / 8);
+    nbph = (N + TB - 1) / TB;
+    return str ? nbh * nbph : (ntok + TB - 1) / TB;
+  };
+  int64_t nbph4, nbph2;
+  const int64_t npb4 = pack_blocks(4, nbph4), npb2 = pack_blocks(2, nbph2);
+  const bool u2 = nvb + 2 * npb4 < 2 * 256;
+  const int64_t npb = u2 ? npb2 : npb4, nbph = u2 ? nbph2 : nbph4;
   const int64_t nblk = nvb + 2 * npb;
   if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
-  auto kern = dt == BA_F16 ? (str ? prepass_fused_kernel<BA_F16, true> : prepass_fused_kernel<BA_F16, false>)
-                           : (str ? prepass_fused_kernel<BA_BF16, true> : prepass_fused_kernel<BA_BF16, false>);
+  auto kern = dt == BA_F16
+                  ? (str ? (u2 ? prepass_fused_kernel<BA_F16, true, 2> : prepass_fused_kernel<BA_F16, true, 4>)
+                         : (u2 ? prepass_fused_kernel<BA_F16, false, 2> : prepass_fused_kernel<BA_F16, false, 4>))
+                  : (str ? (u2 ? prepass_fused_kernel<BA_BF16, true, 2> : prepass_fused_kernel<BA_BF16, true, 4>)
+                         : (u2 ? prepass_fused_kernel<BA_BF16, false, 2> : prepass_fused_kernel<BA_BF16, false, 4>));
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, nvb, npb, nbph,
                      qbits, qmu, kbits, kmu, vq, vscale);
   return hipGetLastError();
