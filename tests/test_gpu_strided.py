@@ -28,6 +28,7 @@ SENTINEL = -7.0
 CASES = [
     (2, 197, 3, 64, F16, 0, 0, "relpos_prefix"),   # one launch; relative position with a class token
     (2, 129, 3, 72, BF16, 0, 0, "dense_f16"),      # one launch, d = 72; dense fp16 bias
+    (8, 1024, 16, 72, BF16, 0, 0, "none"),         # one launch, four chunks per packing thread
     (1, 2000, 2, 64, BF16, 0, 4, "none"),          # separate packer + channel-group quantiser
     (1, 4096, 2, 64, F16, 0, 0, "relpos_grid"),    # 64 x 64 grid, row-run relative position
     (1, 300, 2, 40, F16, 0, 3, "none"),            # five 16-byte pieces per token; element stores
