@@ -14,6 +14,11 @@ d=72, dense fp16 bias shared over the batch); the same figures for the
 attention block around the kernels (QKV projection on the ROCm BLAS,
 BinaryAttention, output projection) at the 64x64-token shape.
 
+Before the W warm-up steps, each measurement runs the step back to back for
+--device-warmup seconds (0.3 by default): a fresh MI355X runs the first tens
+of milliseconds of sustained load at a lower clock, and the timed steps are
+meant to show the rate the device holds under sustained load.
+
 roofline: the fused attention kernel, timed alone with HIP events on the
 stream it runs on: achieved = effective ops per launch / mean launch time,
 against the int8 MFMA dense peak (5.0 POP/s; the effective op count is the
@@ -212,12 +217,31 @@ class Workload:
         return times[len(times) // 2]
 
 
-def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
+def device_warmup(fn, seconds: float) -> int:
+    """Run fn back to back for `seconds` of wall time (synchronising every ten
+    calls). A fresh MI355X runs the first tens of milliseconds of sustained
+    load at a lower clock (DiT-512: 87.6 us per step after 5 warm-up steps,
+    77.7 us after 1000); this brings it to the clock it holds under sustained
+    load before the W warm-up steps and the timed ones. Returns the calls."""
+    torch = __import__("torch")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        n += 10
+    return n
+
+
+def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmup_s: float = 0.3) -> dict:
     import workloads
     torch = __import__("torch")
     w = Workload(name)
     s = w.spec
     ops = workloads.eff_ops(s)
+    dev_warm = device_warmup(w.step, device_warmup_s)
     # whole step, bracketed by synchronisation on both sides
     for _ in range(warmup):
         w.step()
@@ -245,6 +269,7 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
     nbytes = algorithmic_bytes(s)
     return {
         "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
+        "device_warmup": {"seconds": device_warmup_s, "steps": dev_warm},
         "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms, "online_ms": online_ms,
         "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
@@ -254,7 +279,7 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False) -> dict:
     }
 
 
-def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64) -> dict:
+def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64, device_warmup_s: float = 0.3) -> dict:
     """The attention block (QKV projection -> BinaryAttention -> output
     projection) at the 64x64-token shape with synthetic bf16 weights: time per
     block (HIP events, back-to-back blocks), the attention call alone on the
@@ -285,6 +310,7 @@ def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    device_warmup(lambda: attention_block(x, w_qkv, b_qkv, w_out, b_out, H), device_warmup_s)
     block_ms = timed(lambda: attention_block(x, w_qkv, b_qkv, w_out, b_out, H))
     qkv = torch.addmm(b_qkv, x.view(B * N, C), w_qkv).view(B, N, 3 * C)
     q, k, v = split_heads(qkv, H)  # strided head views of the projection output
@@ -318,6 +344,9 @@ def main() -> int:
     ap.add_argument("--secondary", default="long_4k")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-warmup", type=float, default=0.3, metavar="SECONDS",
+                    help="wall time of back-to-back steps run before the W warm-up steps, so the timed "
+                         "steps run at the clock the GPU holds under sustained load (0 to skip)")
     ap.add_argument("--block", action="store_true",
                     help="only the attention block (QKV projection, BinaryAttention, output "
                          "projection) at B=2, N=4096, 16 heads of 64, synthetic bf16 weights")
@@ -343,7 +372,7 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": 4 * n}))
         return 0
     if args.block:
-        r = measure_block(args.steps, args.warmup)
+        r = measure_block(args.steps, args.warmup, device_warmup_s=args.device_warmup)
         print(json.dumps({
             "metric": "attention block tokens/s (QKV projection + BinaryAttention + output projection)",
             "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -359,7 +388,7 @@ def main() -> int:
     import workloads
     names = list(workloads.WORKLOADS) if args.all else [args.workload]
     for name in names:
-        r = measure(name, args.steps, args.warmup, cold=not args.all)
+        r = measure(name, args.steps, args.warmup, cold=not args.all, device_warmup_s=args.device_warmup)
         s = r["spec"]
         line = {
             "metric": "effective attention TOPS (4*B*H*N^2*d / t_step), step = pack Q/K + quantise V + fused attention",
@@ -370,6 +399,7 @@ def main() -> int:
             "dtype_detail": "Q.K: +-1 signs on fp4 MFMA (exact integer sums); softmax fp32; P.V u8 x int8 -> int32 MFMA",
             "data": "synthetic (seeded N(0,1) activations of the workload's shape)",
             "config": config_of(s),
+            "device_warmup": r["device_warmup"],
             "attn_ms": round(r["attn_ms"], 5), "attn_min_ms": round(r["attn_min_ms"], 5),
             "attn_tops": round(r["attn_tops"], 3),
             "roofline": {
@@ -398,7 +428,7 @@ def main() -> int:
                                    "note": "ba_attention_fwd_online: one pass over the keys with a running "
                                            "row maximum (same timing protocol)"}
         if not args.all and args.secondary:
-            r2 = measure(args.secondary, args.steps, args.warmup)
+            r2 = measure(args.secondary, args.steps, args.warmup, device_warmup_s=args.device_warmup)
             line["secondary"] = {"config": config_of(r2["spec"]), "value": round(r2["tops"], 3),
                                  "ms_per_step": round(r2["step_ms"], 5), "attn_ms": round(r2["attn_ms"], 5),
                                  "attn_online_ms": None if r2["online_ms"] is None else round(r2["online_ms"], 5),
