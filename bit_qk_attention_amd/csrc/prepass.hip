@@ -57,8 +57,9 @@ __global__ __launch_bounds__(256) void pack_qk_kernel(
 // chunks, mu from the P partial sums in channel order.
 constexpr int kPackUCoop = 2;
 // U (chunks per thread) is 2 for the standalone packer (4096 tokens: 18.3 ->
-// 17.6 us for the pre-pass against 4) and chosen per launch for the fused
-// pre-pass (launch_prepass).
+// 17.6 us for the pre-pass against 4) and for the fused pre-pass (two
+// blocks per CU: DiT-512 14.2 -> 13.8 us against 4, 16.0 with 1).
+constexpr int kPackUFused = 2;
 // One block of NT threads packs tokens [blk * TB, blk * TB + TB) of x.
 // bits_s and sum_s hold NT * U entries. STR: token t of x starts at
 // x + t * sx (sx % 8 == 0) instead of x + t * d, so a block's chunks are
@@ -237,7 +238,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(
 // 16*R*P bytes. Channel maxima go through an LDS atomic max on the float
 // bits (non-negative), then the held values are quantised and written as
 // int8.
-constexpr int kQvRows = 12;  // rows per thread held in registers
+// rows per thread held in registers: 10 keeps the fused pre-pass within 64
+// VGPRs, so two of its 1024-thread blocks share a CU
+constexpr int kQvRows = 10;
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 // heads bh0 .. bh0 + HB - 1 (those below nbh) by one block of 1024
 // threads; smem holds 2 * 128 words per head
@@ -259,11 +262,16 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
   __syncthreads();
   const uint16_t* vh = v + (hvalid ? (bh / in.H) * in.sb + (bh % in.H) * in.sh : 0) + 8 * piece;
   int8_t* qh = vq + (hvalid ? bh * N * d : 0) + 8 * piece;
+  // rows r0, r0 + R, ... below N: this thread holds the first cnt of them;
+  // the row addresses are stepped, not kept per row (register pressure)
+  const int cnt = active && r0 < N ? min(kQvRows, (N - r0 + R - 1) / R) : 0;
   u4v x[kQvRows];
+  {
+    const uint16_t* src = vh + (int64_t)r0 * in.sn;
+    const int64_t step = (int64_t)R * in.sn;
 #pragma unroll
-  for (int k = 0; k < kQvRows; ++k) {
-    const int r = r0 + k * R;
-    x[k] = (active && r < N) ? *reinterpret_cast<const u4v*>(vh + (int64_t)r * in.sn) : (u4v){0u, 0u, 0u, 0u};
+    for (int k = 0; k < kQvRows; ++k, src += step)
+      x[k] = k < cnt ? *reinterpret_cast<const u4v*>(src) : (u4v){0u, 0u, 0u, 0u};
   }
   // max |v| per channel on the 16-bit patterns: for finite fp16 / bf16
   // values the magnitude bits (sign cleared) order like |v|, so a packed
@@ -291,10 +299,10 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
   float inv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
+  int8_t* dst = qh + (int64_t)r0 * d;
 #pragma unroll
-  for (int k = 0; k < kQvRows; ++k) {
-    const int r = r0 + k * R;
-    if (active && r < N) {
+  for (int k = 0; k < kQvRows; ++k, dst += (int64_t)R * d) {
+    if (k < cnt) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -303,7 +311,7 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
         const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
         if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
       }
-      *reinterpret_cast<uint2*>(qh + (int64_t)r * d) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
     }
   }
 }
@@ -336,9 +344,12 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
 // register-resident quantiser): blocks 0 .. nvb-1 quantise HB heads each
 // (the long-running ones, dispatched first), the rest pack npb blocks of
 // tokens of Q, then npb of K, all with 1024 threads. STR (a strided view):
-// the pack blocks are nbph per head, each within one head.
+// the pack blocks are nbph per head, each within one head. At most 64 VGPRs
+// (eight waves per SIMD), so two blocks share a CU: a packing block runs
+// beside a quantising one instead of after it (DiT-512 15.5 -> 13.8 us,
+// DiT-256 15.4 -> 14.1, DeiT-Small 9.3 -> 8.4).
 template <int DT, bool STR, int U>
-__global__ __launch_bounds__(1024) void prepass_fused_kernel(
+__global__ __launch_bounds__(1024, 8) void prepass_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, InView in,
     int nbh, int N, int d, int HB, int64_t nvb, int64_t npb, int64_t nbph, uint32_t* __restrict__ qbits,
     float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
@@ -555,28 +566,17 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
     return dt == BA_F16 ? launch_quant_v_split_ab<BA_F16>(v16, in, nbh, N, d, vq, vscale, s)
                         : launch_quant_v_split_ab<BA_BF16>(v16, in, nbh, N, d, vq, vscale, s);
   }
-  // chunks per thread of the packing blocks: 4, or 2 where 4 would leave
-  // fewer than two blocks per CU in all (DeiT-Small pre-pass 10.3 -> 9.3 us;
-  // with two at DiT-256 and DiT-512 16.0 and 15.8 us against 15.5)
   const bool str = !in.dense(N, d);
   const int HB = quant_heads_per_block(nbh, N, d);
   const int64_t nvb = (nbh + HB - 1) / HB;
-  auto pack_blocks = [&](int u, int64_t& nbph) {
-    const int TB = 1024 * u / (d / 8);
-    nbph = (N + TB - 1) / TB;
-    return str ? nbh * nbph : (ntok + TB - 1) / TB;
-  };
-  int64_t nbph4, nbph2;
-  const int64_t npb4 = pack_blocks(4, nbph4), npb2 = pack_blocks(2, nbph2);
-  const bool u2 = nvb + 2 * npb4 < 2 * 256;
-  const int64_t npb = u2 ? npb2 : npb4, nbph = u2 ? nbph2 : nbph4;
+  const int TB = 1024 * kPackUFused / (d / 8);  // tokens per packing block
+  const int64_t nbph = (N + TB - 1) / TB;
+  const int64_t npb = str ? nbh * nbph : (ntok + TB - 1) / TB;
   const int64_t nblk = nvb + 2 * npb;
   if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
-  auto kern = dt == BA_F16
-                  ? (str ? (u2 ? prepass_fused_kernel<BA_F16, true, 2> : prepass_fused_kernel<BA_F16, true, 4>)
-                         : (u2 ? prepass_fused_kernel<BA_F16, false, 2> : prepass_fused_kernel<BA_F16, false, 4>))
-                  : (str ? (u2 ? prepass_fused_kernel<BA_BF16, true, 2> : prepass_fused_kernel<BA_BF16, true, 4>)
-                         : (u2 ? prepass_fused_kernel<BA_BF16, false, 2> : prepass_fused_kernel<BA_BF16, false, 4>));
+  constexpr int U = kPackUFused;
+  auto kern = dt == BA_F16 ? (str ? prepass_fused_kernel<BA_F16, true, U> : prepass_fused_kernel<BA_F16, false, U>)
+                           : (str ? prepass_fused_kernel<BA_BF16, true, U> : prepass_fused_kernel<BA_BF16, false, U>);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, nvb, npb, nbph,
                      qbits, qmu, kbits, kmu, vq, vscale);
   return hipGetLastError();

@@ -236,6 +236,9 @@ def test_key_permutation():
     (1, 1, 1, 8), (2, 3, 5, 72), (1, 2, 1024, 72), (8, 16, 300, 72), (1, 3, 777, 24),
     (1, 1, 16384, 64), (1, 1, 16385, 64), (2, 1, 4096, 128), (1, 2, 50, 20), (3, 1, 2049, 40),
     (5, 103, 77, 64), (3, 97, 200, 72), (1, 131, 250, 128),
+    # the register-resident quantiser's last head length (10 rows per thread)
+    # and the first one past it
+    (1, 4, 1280, 64), (1, 4, 1281, 64), (1, 2, 1130, 72), (1, 2, 1131, 72),
     # heads split over several blocks (maxima and sums combined across blocks)
     (2, 3, 1600, 72), (1, 1, 20000, 128), (2, 16, 4096, 64), (1, 4, 1537, 64), (1, 1, 7000, 16)])
 @pytest.mark.parametrize("dt", [F16, BF16])
