@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.ba_attention_fwd_strided.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P,
                                                ctypes.POINTER(ba_strides), I, P]
         L.ba_attention_fwd_strided.restype = I
+        L.ba_pack_k_quant_v.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P]
+        L.ba_pack_k_quant_v.restype = I
+        L.ba_attention_fwd_q16.argtypes = [P, I, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
+        L.ba_attention_fwd_q16.restype = I
         L.ba_debug_hamming_scores.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
         L.ba_debug_hamming_scores.restype = I
         L.ba_status_string.argtypes = [I]
@@ -83,7 +87,7 @@ def header_symbols() -> list[str]:
     """Names of the functions declared in include/binattn.h."""
     text = open(HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ba_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ba_[a-z0-9_]+)\s*\(", text)))
 
 
 def status_string(s: int) -> str:
@@ -237,6 +241,24 @@ def ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stre
         ctypes.byref(cb), B, H, N, d, _ptr(out), ctypes.byref(st), _dt(out), _stream(stream)))
 
 
+def ba_pack_k_quant_v(k, v, kbits, kmu, vq, vscale, stream=None) -> None:
+    """The K and V half of ba_pack_qk_quant_v (Q is left to ba_attention_fwd_q16)."""
+    _require_gpu(k, v, kbits, kmu, vq, vscale)
+    B, H, N, d = k.shape
+    _check("ba_pack_k_quant_v", lib().ba_pack_k_quant_v(
+        _ptr(k), _ptr(v), _dt(k), B, H, N, d, _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale), _stream(stream)))
+
+
+def ba_attention_fwd_q16(q, kbits, kmu, vq, vscale, bias, out, stream=None) -> None:
+    """ba_attention_fwd with q [B,H,N,d] fp16/bf16 packed inside the kernel (d % 8 == 0)."""
+    _require_gpu(q, kbits, kmu, vq, vscale, out)
+    B, H, N, d = out.shape
+    cb = (bias or Bias()).to_c()
+    _check("ba_attention_fwd_q16", lib().ba_attention_fwd_q16(
+        _ptr(q), _dt(q), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale),
+        ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
+
+
 def ba_debug_hamming_scores(qbits, kbits, d, bh_begin, bh_count, row_begin, row_count, sigma,
                             stream=None) -> None:
     """sigma int32 [bh_count, row_count, N] = d - 2*popcount(q xor k) over a window."""
@@ -301,4 +323,29 @@ def attention(q, k, v, bias: Bias | None = None, out=None, stream=None):
         ba_attention_fwd(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream)
     else:
         ba_attention_fwd_strided(qbits, qmu, kbits, kmu, vq, vscale, bias, out, stream)
+    return out
+
+
+def prepare_kv(k, v, stream=None):
+    """Packed K and quantised V (ba_pack_k_quant_v), for attention_q16."""
+    torch = _torch()
+    B, H, N, d = k.shape
+    W = ba_packed_words(d)
+    kbits = torch.empty((B, H, N, W), dtype=torch.int32, device=k.device)
+    kmu = torch.empty((B, H, N), dtype=torch.float32, device=k.device)
+    vq = torch.empty((B, H, N, d), dtype=torch.int8, device=v.device)
+    vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
+    ba_pack_k_quant_v(k, v, kbits, kmu, vq, vscale, stream)
+    return kbits, kmu, vq, vscale
+
+
+def attention_q16(q, k, v, bias: Bias | None = None, out=None, stream=None):
+    """Whole forward pass with Q packed inside the attention: ba_pack_k_quant_v,
+    then ba_attention_fwd_q16 (contiguous q, k, v, out; d % 8 == 0). The same
+    output as attention(), bit for bit."""
+    torch = _torch()
+    kbits, kmu, vq, vscale = prepare_kv(k, v, stream)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    ba_attention_fwd_q16(q, kbits, kmu, vq, vscale, bias, out, stream)
     return out

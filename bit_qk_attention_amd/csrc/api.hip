@@ -76,10 +76,14 @@ bool view_disjoint(const ba_strides& st, int B, int H, int N, int d) {
 
 // ba_pack_qk_quant_v on the view `in` (validated here); in_elems = the
 // elements each of q, k, v spans.
+// with_q false: K and V only (q, qbits, qmu unused).
 ba_status prepass_checked(const void* q, const void* k, const void* v, const InView& in, int64_t in_elems,
                           int in_align, int dt, int B, int H, int N, int d, uint32_t* qbits, float* qmu,
-                          uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, void* stream) {
-  if (!q || !k || !v || !qbits || !qmu || !kbits || !kmu || !vq || !vscale) return BA_ERR_INVALID_ARG;
+                          uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, void* stream,
+                          bool with_q = true) {
+  if (!with_q) q = nullptr, qbits = nullptr, qmu = nullptr;
+  if ((with_q && (!q || !qbits || !qmu)) || !k || !v || !kbits || !kmu || !vq || !vscale)
+    return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (!dtype16(dt)) return BA_ERR_UNSUPPORTED;
@@ -102,22 +106,26 @@ ba_status prepass_checked(const void* q, const void* k, const void* v, const InV
                                  static_cast<hipStream_t>(stream)));
 }
 
+// q16 != nullptr: Q given as 16-bit values of type q16_dt (qbits, qmu unused).
 ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint32_t* kbits, const float* kmu,
                             const int8_t* vq, const float* vscale, const ba_bias* bias, int B,
                             int H, int N, int d, void* out, const ba_strides& ost, int out_align, int out_dt,
-                            void* stream, int online = 0) {
-  if (!qbits || !qmu || !kbits || !kmu || !vq || !vscale || !out) return BA_ERR_INVALID_ARG;
+                            void* stream, int online = 0, const void* q16 = nullptr, int q16_dt = -1) {
+  if (q16) qbits = nullptr, qmu = nullptr;
+  if ((!q16 && (!qbits || !qmu)) || !kbits || !kmu || !vq || !vscale || !out) return BA_ERR_INVALID_ARG;
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (online && d > 64) return BA_ERR_UNSUPPORTED;
   if (!dtype16(out_dt)) return BA_ERR_UNSUPPORTED;
+  if (q16 && (!dtype16(q16_dt) || d % 8 != 0)) return BA_ERR_UNSUPPORTED;
   if (!aligned(qbits, 16) || !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(out, out_align) ||
-      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4))
+      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(q16, 16))
     return BA_ERR_INVALID_ARG;
   const int64_t ntok = (int64_t)B * H * N;
   const int64_t W = (d + 31) / 32;
   AttnArgs a = {};
   a.qbits = qbits; a.qmu = qmu; a.kbits = kbits; a.kmu = kmu; a.vq = vq; a.vscale = vscale;
+  a.q16 = q16; a.q16_dt = q16_dt;
   a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt; a.online = online;
   a.out_sb = ost.batch; a.out_sh = ost.head; a.out_sn = ost.token;
   a.bias_kind = BA_BIAS_NONE;
@@ -151,10 +159,10 @@ ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint3
     a.bias = bias->data;
   }
   const int64_t out_bytes = view_extent(ost, B, H, N, d) * 2;
-  const void* ins[7] = {qbits, qmu, kbits, kmu, vq, vscale, a.bias};
-  const int64_t isz[7] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
-                          (int64_t)B * H * d * 4, bias_bytes};
-  for (int i = 0; i < 7; ++i)
+  const void* ins[8] = {qbits, qmu, kbits, kmu, vq, vscale, a.bias, q16};
+  const int64_t isz[8] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
+                          (int64_t)B * H * d * 4, bias_bytes, ntok * d * 2};
+  for (int i = 0; i < 8; ++i)
     if (overlap(out, out_bytes, ins[i], isz[i])) return BA_ERR_INVALID_ARG;
   return from_hip(launch_attention(a, static_cast<hipStream_t>(stream)));
 }
@@ -237,6 +245,23 @@ ba_status ba_pack_qk_quant_v_strided(const void* q, const void* k, const void* v
            aligned(k, 16) && aligned(v, 16);
   return prepass_checked(q, k, v, in, view_extent(*in_strides, B, H, N, d), 2, raw(dt), B, H, N, d, qbits, qmu, kbits,
                          kmu, vq, vscale, stream);
+}
+
+ba_status ba_pack_k_quant_v(const void* k, const void* v, ba_dtype dt, int B, int H, int N, int d,
+                            uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, void* stream) {
+  const ba_status st = check_shape(B, H, N, d);
+  if (st != BA_OK) return st;
+  return prepass_checked(nullptr, k, v, dense_view(H, N, d), (int64_t)B * H * N * d, 16, raw(dt), B, H, N, d,
+                         nullptr, nullptr, kbits, kmu, vq, vscale, stream, false);
+}
+
+ba_status ba_attention_fwd_q16(const void* q, ba_dtype q_dt, const uint32_t* kbits, const float* kmu,
+                               const int8_t* vq, const float* vscale, const ba_bias* bias, int B, int H,
+                               int N, int d, void* out, ba_dtype out_dt, void* stream) {
+  if (!q) return BA_ERR_INVALID_ARG;
+  const ba_strides dense = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  return attention_checked(nullptr, nullptr, kbits, kmu, vq, vscale, bias, B, H, N, d, out, dense, 16,
+                           raw(out_dt), stream, 0, q, raw(q_dt));
 }
 
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,

@@ -115,6 +115,8 @@ constexpr float kLog2_255 = 7.9943534368588578f;
 struct Params {
   const uint32_t* qbits;
   const float* qmu;
+  const uint16_t* q16;  // Q as 16-bit values, packed in the prologue (then qbits, qmu unused)
+  int q16_f16;          // q16 is fp16 (else bf16)
   const uint32_t* kbits;
   const float* kmu;
   const int8_t* vq;
@@ -191,6 +193,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ float partner32(float x, int lane) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+__device__ __forceinline__ uint32_t partner32u(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return lane < 32 ? r[1] : r[0];
+}
+__device__ __forceinline__ double partner64(double x, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint64_t lo = partner32u((uint32_t)u, lane), hi = partner32u((uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, (hi << 32) | lo);
 }
 
 
@@ -384,33 +395,137 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   // Word w of a query covers channels 32w..32w+31; of those, the first
   // min(max(d - 32w, 0), 32) are real. Dword m of the fp4 operand holds
   // channel 32w + m + 4p at nibble p, so its nibble mask is bit m + 4p of
-  // the real-channel mask spread to four bits.
-  auto q_operand = [&](int q, bool valid, v8i* op) {
+  // the real-channel mask spread to four bits. wb[kk] is word 2 kk + g.
+  auto q_operand_w = [&](const uint32_t* wb, v8i* op) {
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
       const int w = 2 * kk + g;
-      const uint32_t bits = (valid && w < W) ? p.qbits[(bh * N + q) * W + w] : 0u;
       const int nv = min(max(d - 32 * w, 0), 32);
       const uint32_t vm = nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
       v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int m = 0; m < 4; ++m) o[m] = (int)(fp4_signs(bits, m) & (((vm >> m) & 0x11111111u) * 0xFu));
+      for (int m = 0; m < 4; ++m) o[m] = (int)(fp4_signs(wb[kk], m) & (((vm >> m) & 0x11111111u) * 0xFu));
       op[kk] = o;
     }
+  };
+  auto q_operand = [&](int q, bool valid, v8i* op) {
+    uint32_t wb[NKB];
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) {
+      const int w = 2 * kk + g;
+      wb[kk] = (valid && w < W) ? p.qbits[(bh * N + q) * W + w] : 0u;
+    }
+    q_operand_w(wb, op);
+  };
+  // Q given as 16-bit values (d % 8 == 0): the two lanes of a query pack it
+  // here with the arithmetic of the packing kernels, so bits and scale are
+  // those ba_pack_qk writes. Lane g takes the words 2 kk + g: sign bits from
+  // a float compare (x < 0), a float64 sum of |x| per 8-channel piece. The
+  // scale adds the piece sums in channel order (the running sum passes
+  // between the two lanes word by word), divides by d in float64 and rounds
+  // to float once. raw: the lane's 16-byte pieces (zero past d).
+  auto pack_q16 = [&](auto dtc, const u4v (&raw)[NKB][4], bool valid, uint32_t* wb, float& mu) {
+    constexpr int DT = decltype(dtc)::value;
+    double ps[NKB][4];
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        double s = 0.0;
+        // (uniform: pieces past d for lane 0 are past d for lane 1 too)
+        if (64 * kk + 8 * pc < d) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xf = to_f32<DT>((uint16_t)(raw[kk][pc][e >> 1] >> ((e & 1) * 16)));
+            word |= xf < 0.0f ? (1u << (8 * pc + e)) : 0u;
+            s += (double)fabsf(xf);
+          }
+        }
+        ps[kk][pc] = s;
+      }
+      wb[kk] = valid ? word : 0u;
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int w = 0; w < 2 * NKB; ++w) {
+      if (w < W) {  // (uniform)
+        const bool own = (w & 1) == g;
+        double mine = acc;
+        if (own) {
+#pragma unroll
+          for (int pc = 0; pc < 4; ++pc)
+            if (32 * w + 8 * pc < d) mine += ps[w >> 1][pc];
+        }
+        const double other = partner64(mine, lane);
+        acc = own ? mine : other;
+      }
+    }
+    mu = valid ? (float)(acc / (double)d) : 0.0f;
   };
   v8i qop[NKB];
   float c0 = 0.0f;  // mu_q / sqrt(d): natural-log units (bias path)
   float cq = 0.0f;  // c0 * log2(e): base-2 units (no-bias path)
-  // the query operand and scale (the sigma modes take no scales); the
-  // resident mode loads them after it has started the DMA of the tiles, so
-  // the two memory latencies overlap
-  auto load_q = [&]() {
-    q_operand(qi, qvalid, qop);
-    const float qmu = (is_attn(MODE) && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
+  // The query operand and scale (the sigma modes take no scales), in two
+  // steps: issue_q starts the loads (16-bit rows, or sign words and scale),
+  // finish_q forms the operand. The staged and resident passes start the
+  // first tiles' DMA in between, so the two memory latencies overlap and
+  // the packing runs while the tiles land. Packed here from 16-bit Q, the
+  // key-split pass 1 also needs the other waves' queries: each wave leaves
+  // its signs and scales in the first V stage (unused until pass 2).
+  const bool q_from16 = MODE == MODE_ATTN && p.q16 != nullptr;
+  u4v qraw[NKB][4];
+  uint32_t qwb[NKB];
+  float qmu_ld = 0.0f;
+  auto issue_q = [&]() {
+    if (q_from16) {
+      const uint16_t* row = p.q16 + (bh * N + qc) * d;
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc) {
+          const int c = 32 * (2 * kk + g) + 8 * pc;
+          qraw[kk][pc] = c < d ? *reinterpret_cast<const u4v*>(row + c) : (u4v){0u, 0u, 0u, 0u};
+        }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) {
+        const int w = 2 * kk + g;
+        qwb[kk] = (qvalid && w < W) ? p.qbits[(bh * N + qi) * W + w] : 0u;
+      }
+      qmu_ld = (is_attn(MODE) && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
+    }
+  };
+  auto finish_q = [&]() {
+    float qmu = qmu_ld;
+    if (q_from16) {
+      uint32_t wb[NKB];
+      if (p.q16_f16) pack_q16(IntC<BA_F16>(), qraw, qvalid, wb, qmu);
+      else pack_q16(IntC<BA_BF16>(), qraw, qvalid, wb, qmu);
+      q_operand_w(wb, qop);
+      if constexpr (P1_SPLIT) {
+        uint32_t* tw = reinterpret_cast<uint32_t*>(vs0.vr);
+        const int qr = wave * kQW + ql;
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk)
+          if (2 * kk + g < W) tw[qr * W + 2 * kk + g] = wb[kk];
+        if (g == 0) reinterpret_cast<float*>(tw + kQB * W)[qr] = qmu;
+      }
+    } else {
+      q_operand_w(qwb, qop);
+    }
     c0 = qmu * p.inv_sqrt_d;
     cq = c0 * kLog2e;
   };
-  if constexpr (!RES) load_q();
+  // the staged pass 1 of the attention and the resident mode split the two
+  // steps around their first DMA; every other form loads the queries here
+  constexpr bool Q_SPLIT = MODE == MODE_ATTN && !P1_SPLIT;
+  if constexpr (!Q_SPLIT) {
+    issue_q();
+    finish_q();
+  } else if constexpr (!RES) {
+    issue_q();
+  }
 
   const int ntiles = (N + kBC - 1) / kBC;
   const bool ragged = (N % kBC) != 0;
@@ -960,7 +1075,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   // unrolled by NS so the stage is known at compile time): tile t + NS - 1
   // is loaded while tile t is computed, and the end of step t waits only
   // for tile t + 1. Then the ragged tile, staged synchronously.
-  auto run_pass = [&](auto nsc, bool with_v, auto body) {
+  // pre: work done while the first tiles' DMA is in flight
+  auto run_pass = [&](auto nsc, bool with_v, auto body, auto pre) {
     // (with_v: pass 2, whose progress sets the issue priority)
     constexpr int NS = decltype(nsc)::value;
     if (nfull > 0) {
@@ -968,12 +1084,14 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       if constexpr (NS == 3) {
         if (nfull > 1) dma_tile(1, IntC<1>(), with_v);
       }
+      pre();
       if (NS == 3 && nfull > 1) wait_vm_last();
       else wait_vm0();
       finish_k(IntC<0>());
       if (with_v && !p.v_dma) copy_v_checked(0, IntC<0>());
     } else {
       stage_checked(0, IntC<0>(), with_v);
+      pre();
       wait_vm0();
       finish_k(IntC<0>());
     }
@@ -1017,18 +1135,19 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       else if constexpr (NS == 3) tail(IntC<2>());
     }
   };
-  // Resident mode: every tile into a stage of its own. The key side of all
-  // tiles (K words, key scales, table window) is DMA'd first and the query
-  // operand loaded meanwhile; one wait, then the V rows of all tiles and the
+  // Resident mode: every tile into a stage of its own. The query loads and
+  // then the key side of all tiles (K words, key scales, table window) are
+  // issued, and the query operand formed while they land; one wait, then the V rows of all tiles and the
   // channel scales are started and pass 1 runs while they land; a second
   // wait before pass 2. Neither pass waits or synchronises per tile.
   auto res_stage = [&]() {
     if constexpr (RES) {
+      issue_q();
       for (int t = 0; t < ntiles; ++t) {
         if (t < nfull) dma_tile(t, t, false);
         else stage_checked(t, t, false);
       }
-      load_q();
+      finish_q();
       wait_vm0();
       for (int t = 0; t < ntiles; ++t) {
         finish_k(t);
@@ -1058,7 +1177,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
         put_sigma(BoolC<MODE == MODE_SIGMA_RAW>(), qi, t * kBC + kb * 32 + 16 * g, qk_mfma(a));
       }
     };
-    run_pass(IntC<Cfg::NS2>(), false, sigma_tile);
+    run_pass(IntC<Cfg::NS2>(), false, sigma_tile, [] {});
     return;
   }
   if constexpr (MODE == MODE_ONLINE) {
@@ -1154,7 +1273,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       oblock(tail, t, bufc, 0);
       if (!(TAIL && t * kBC + 32 >= N)) oblock(tail, t, bufc, 1);  // (a block holding a key < N)
     };
-    run_pass(IntC<NS2>(), true, otile);
+    run_pass(IntC<NS2>(), true, otile, [] {});
     fold(1.0f);
     const float lr = ls + partner32(ls, lane);  // 255 l over both halves of the keys
     if (!qvalid) return;
@@ -1196,11 +1315,29 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     // query are combined through LDS at the end.
     v8i qop4[4][NKB];
     float c04[4];
+    if (MODE == MODE_ATTN && p.q16) {
+      // the workgroup's query signs and scales as the waves packed them
+      // (finish_q); the stage is not touched again before pass 2's barrier
+      static_assert((2 * NKB + 1) * kQB * 4 <= (int)sizeof(VSt::vr), "query table fits the first V stage");
+      __syncthreads();
+      const uint32_t* tw = reinterpret_cast<const uint32_t*>(vs0.vr);
+      const float* tm = reinterpret_cast<const float*>(tw + kQB * W);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int qq = qb * kQB + kQW * q + ql;
-      q_operand(qq, qq < N, qop4[q]);
-      c04[q] = (MODE == MODE_ATTN && qq < N) ? p.qmu[bh * N + qq] * p.inv_sqrt_d : 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        const int qr = kQW * q + ql;
+        uint32_t wb[NKB];
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) wb[kk] = 2 * kk + g < W ? tw[qr * W + 2 * kk + g] : 0u;
+        q_operand_w(wb, qop4[q]);
+        c04[q] = tm[qr] * p.inv_sqrt_d;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int qq = qb * kQB + kQW * q + ql;
+        q_operand(qq, qq < N, qop4[q]);
+        c04[q] = (MODE == MODE_ATTN && qq < N) ? p.qmu[bh * N + qq] * p.inv_sqrt_d : 0.0f;
+      }
     }
     struct Blk {
       uint32_t kw[NKB];
@@ -1356,8 +1493,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     } else {
       // (a wave with no live query stages its share of the tiles only;
       // every wave meets the same barriers)
-      if (wave_live) run_pass(IntC<NS1>(), false, pass1_tile);
-      else run_pass(IntC<NS1>(), false, [](auto, int, auto) {});
+      if (wave_live) run_pass(IntC<NS1>(), false, pass1_tile, finish_q);
+      else run_pass(IntC<NS1>(), false, [](auto, int, auto) {}, finish_q);
     }
     mrun = fmaxf(m0, m1);
     mrun = fmaxf(mrun, partner32(mrun, lane));
@@ -1584,11 +1721,11 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
     // (a wave with no live query runs the lean tile on clamped queries and
     // stores nothing: a check per tile or a second copy of the pass measured
     // slower on the four-workgroup kernels than the wasted work)
-    run_pass(IntC<NS2>(), true, pass2_tile_lean);
+    run_pass(IntC<NS2>(), true, pass2_tile_lean, [] {});
   } else {
     __syncthreads();  // pass 1 is done with both buffers
     dma_vscale();
-    run_pass(IntC<NS2>(), true, pass2_tile);
+    run_pass(IntC<NS2>(), true, pass2_tile, [] {});
     pv_regs(vt_held, p_held);
   }
 
@@ -1725,6 +1862,8 @@ hipError_t launch_sigma_routes(const Params& p, int nblocks, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   Params p = {};
   p.qbits = a.qbits; p.qmu = a.qmu; p.kbits = a.kbits; p.kmu = a.kmu;
+  p.q16 = static_cast<const uint16_t*>(a.q16);
+  p.q16_f16 = a.q16_dt == BA_F16;
   p.vq = a.vq; p.vscale = a.vscale;
   p.bias = a.bias; p.bias_bstride = a.bias_bstride;
   p.grid_h = a.grid_h; p.grid_w = a.grid_w; p.n_prefix = a.n_prefix;

@@ -65,7 +65,8 @@ struct InView {
 };
 InView dense_view(int H, int N, int d);
 
-// zero, nzero: a buffer of nzero words the packing launch also zeroes
+// zero, nzero: a buffer of nzero words the packing launch also zeroes.
+// q == nullptr (launch_pack_qk, launch_prepass): K (and V) only.
 hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InView& in, int nbh, int N,
                           int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
                           float* kmu, hipStream_t s, uint32_t* zero = nullptr, int64_t nzero = 0);
@@ -97,6 +98,8 @@ struct AttnArgs {
   int out_dt;
   int64_t out_sb, out_sh, out_sn;  // element strides of out's [B, H, N, d] view
   int online;                      // one pass with a running maximum (d <= 64)
+  const void* q16;                 // Q as 16-bit values [B,H,N,d] (d % 8 == 0), packed by the
+  int q16_dt;                      // attention kernel itself; then qbits and qmu are unused
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

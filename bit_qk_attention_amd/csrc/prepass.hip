@@ -163,6 +163,13 @@ InView dense_view(int H, int N, int d) {
 hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InView& in, int nbh, int N,
                           int d, uint32_t* qbits, float* qmu, uint32_t* kbits,
                           float* kmu, hipStream_t s, uint32_t* zero, int64_t nzero) {
+  // q == nullptr: K alone (grid.y 0 then selects K)
+  const unsigned ny = q ? 2 : 1;
+  if (!q) {
+    q = k;
+    qbits = kbits;
+    qmu = kmu;
+  }
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const int64_t ntok = (int64_t)nbh * N;
@@ -172,7 +179,7 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InVie
     const int64_t nbph = (N + TB - 1) / TB;
     const int64_t nblk = str ? nbh * nbph : (ntok + TB - 1) / TB;
     if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nblk, 2);
+    const dim3 grid((unsigned)nblk, ny);
     auto kern = dt == BA_F16 ? (str ? pack_qk_coop_kernel<BA_F16, true> : pack_qk_coop_kernel<BA_F16, false>)
                              : (str ? pack_qk_coop_kernel<BA_BF16, true> : pack_qk_coop_kernel<BA_BF16, false>);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, q16, k16, in, N, nbph, ntok, d, qbits, qmu, kbits, kmu, zero,
@@ -184,7 +191,7 @@ hipError_t launch_pack_qk(const void* q, const void* k, ba_dtype dt, const InVie
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nzero + 255) / 256)), dim3(256), 0, s, zero, nzero);
   }
   if ((ntok + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((ntok + 255) / 256), 2);
+  const dim3 grid((unsigned)((ntok + 255) / 256), ny);
   if (dt == BA_F16)
     hipLaunchKernelGGL(pack_qk_kernel<BA_F16>, grid, dim3(256), 0, s, q16, k16, in, N, ntok, d, qbits, qmu, kbits, kmu);
   else
@@ -342,8 +349,9 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
 
 // Pack Q and K and quantise V in one launch (d % 8 == 0, heads that fit the
 // register-resident quantiser): blocks 0 .. nvb-1 quantise HB heads each
-// (the long-running ones, dispatched first), the rest pack npb blocks of
-// tokens of Q, then npb of K, all with 1024 threads. STR (a strided view):
+// (the long-running ones, dispatched first), the rest pack npq blocks of
+// tokens of Q (npb, or 0 when Q is left to the attention), then npb of K,
+// all with 1024 threads. STR (a strided view):
 // the pack blocks are nbph per head, each within one head. At most 64 VGPRs
 // (eight waves per SIMD), so two blocks share a CU: a packing block runs
 // beside a quantising one instead of after it (DiT-512 15.5 -> 13.8 us,
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
 template <int DT, bool STR, int U>
 __global__ __launch_bounds__(1024, 8) void prepass_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, InView in,
-    int nbh, int N, int d, int HB, int64_t nvb, int64_t npb, int64_t nbph, uint32_t* __restrict__ qbits,
+    int nbh, int N, int d, int HB, int64_t nvb, int64_t npq, int64_t npb, int64_t nbph, uint32_t* __restrict__ qbits,
     float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
     float* __restrict__ vscale) {
   __shared__ uint32_t bits_s[1024 * U];
@@ -361,17 +369,17 @@ __global__ __launch_bounds__(1024, 8) void prepass_fused_kernel(
   if (b < nvb) {
     quant_heads_block<DT>(v, in, N, d, b * HB, nbh, HB, vq, vscale, bits_s);
   } else if constexpr (STR) {
-    const bool isk = b - nvb >= npb;
-    const int64_t pb = b - nvb - (isk ? npb : 0);
+    const bool isk = b - nvb >= npq;
+    const int64_t pb = b - nvb - (isk ? npq : 0);
     const int64_t bh = pb / nbph, tb = pb - bh * nbph;
     const int W = (d + 31) >> 5;
     pack_block<DT, 1024, U, true>((isk ? k : q) + (bh / in.H) * in.sb + (bh % in.H) * in.sh, N, d, tb,
                                (isk ? kbits : qbits) + bh * N * W, (isk ? kmu : qmu) + bh * N, bits_s, sum_s,
                                in.sn);
-  } else if (b - nvb < npb) {
+  } else if (b - nvb < npq) {
     pack_block<DT, 1024, U>(q, ntok, d, b - nvb, qbits, qmu, bits_s, sum_s);
   } else {
-    pack_block<DT, 1024, U>(k, ntok, d, b - nvb - npb, kbits, kmu, bits_s, sum_s);
+    pack_block<DT, 1024, U>(k, ntok, d, b - nvb - npq, kbits, kmu, bits_s, sum_s);
   }
 }
 
@@ -572,12 +580,13 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
   const int TB = 1024 * kPackUFused / (d / 8);  // tokens per packing block
   const int64_t nbph = (N + TB - 1) / TB;
   const int64_t npb = str ? nbh * nbph : (ntok + TB - 1) / TB;
-  const int64_t nblk = nvb + 2 * npb;
+  const int64_t npq = q ? npb : 0;  // (no Q: packed by the attention)
+  const int64_t nblk = nvb + npq + npb;
   if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
   constexpr int U = kPackUFused;
   auto kern = dt == BA_F16 ? (str ? prepass_fused_kernel<BA_F16, true, U> : prepass_fused_kernel<BA_F16, false, U>)
                            : (str ? prepass_fused_kernel<BA_BF16, true, U> : prepass_fused_kernel<BA_BF16, false, U>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, nvb, npb, nbph,
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, nvb, npq, npb, nbph,
                      qbits, qmu, kbits, kmu, vq, vscale);
   return hipGetLastError();
 }

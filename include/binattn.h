@@ -124,7 +124,7 @@ ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
  * ba_attention_fwd (as every forward pass does): the same outputs, bit for
  * bit, with the same layouts, alignment and error rules as the two calls
  * (q, k, v all [B,H,N,d] of dt). Where d % 8 == 0 and a head fits the
- * register-resident V quantiser (N <= 12 * 1024 / (d / 8)) it is a single
+ * register-resident V quantiser (N <= 10 * 1024 / (d / 8)) it is a single
  * launch in which the V heads and the Q/K token blocks run side by side;
  * with longer heads the packing launch also clears vscale and the V
  * quantiser's two passes follow; otherwise it enqueues the two calls'
@@ -212,6 +212,36 @@ ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu,
                                    int B, int H, int N, int d, void* out,
                                    const ba_strides* out_strides, ba_dtype out_dt,
                                    void* stream);
+
+/* Extension: the path with Q packed inside the attention (zh technical
+ * summary section 2.3: the steps fused into one kernel; section 2.2 item 1
+ * for the packing itself). Each query row is
+ * read once, by the workgroup that owns it, so binarising it in the
+ * attention's prologue repeats no work; K and V rows are read by every
+ * query block of their head, so they are still packed and quantised first,
+ * by ba_pack_k_quant_v.
+ *
+ * ba_pack_k_quant_v: the K and V half of ba_pack_qk_quant_v (kbits, kmu,
+ * vq, vscale bit for bit as that call writes them; same layouts, alignment
+ * and error rules, k and v [B,H,N,d] of dt, no output overlapping another
+ * output or an input). */
+ba_status ba_pack_k_quant_v(const void* k, const void* v, ba_dtype dt, int B, int H, int N, int d,
+                            uint32_t* kbits, float* kmu, int8_t* vq, float* vscale, void* stream);
+
+/* ba_attention_fwd_q16: ba_attention_fwd with Q given as 16-bit values q
+ * [B,H,N,d] of q_dt (BA_F16 or BA_BF16; 16-byte aligned, dense), packed by
+ * the attention kernel into the same sign bits and scales that ba_pack_qk
+ * forms (same arithmetic: bit = x < 0; scale = float64 sum of |x| in
+ * channel order / d, rounded to float once); the output equals
+ * ba_pack_qk followed by ba_attention_fwd bit for bit. d % 8 == 0 only
+ * (BA_ERR_UNSUPPORTED otherwise); the other arguments, layouts and errors
+ * as ba_attention_fwd; out must not overlap q. */
+ba_status ba_attention_fwd_q16(const void* q, ba_dtype q_dt,
+                               const uint32_t* kbits, const float* kmu,
+                               const int8_t* vq, const float* vscale,
+                               const ba_bias* bias,
+                               int B, int H, int N, int d,
+                               void* out, ba_dtype out_dt, void* stream);
 
 /* Integer Hamming similarity for inspection (zh sections 2.1 and 2.2 item 1;
  * it section 2A; fr section 2A): for heads [bh_begin, bh_begin+bh_count) and

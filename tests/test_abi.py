@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(L):
     names = ba.header_symbols()
     assert set(names) == {"ba_packed_words", "ba_pack_qk", "ba_quant_v", "ba_pack_qk_quant_v",
                           "ba_pack_qk_quant_v_strided", "ba_attention_fwd", "ba_attention_fwd_strided",
-                          "ba_attention_fwd_online",
+                          "ba_attention_fwd_online", "ba_pack_k_quant_v", "ba_attention_fwd_q16",
                           "ba_debug_hamming_scores", "ba_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -50,7 +50,7 @@ def _prototypes():
     import re
     text = re.sub(r"/\*.*?\*/", "", open(ba.HEADER_PATH).read(), flags=re.S)
     out = {}
-    for m in re.finditer(r"ba_status\s+(ba_[a-z_]+)\s*\(([^;]*?)\)\s*;", text):
+    for m in re.finditer(r"ba_status\s+(ba_[a-z0-9_]+)\s*\(([^;]*?)\)\s*;", text):
         out[m.group(1)] = " ".join(m.group(2).split())
     return out
 
@@ -157,6 +157,33 @@ def test_online_rejections(L):
     assert attn(L, d=0, fn=f) == INV and attn(L, d=65, fn=f) == UNS and attn(L, d=129, fn=f) == UNS
     assert attn(L, out_dt=ba.BA_F32, fn=f) == UNS
     assert attn(L, bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, 0), fn=f) == INV
+
+
+def test_pack_k_quant_v_rejections(L):
+    def pkv(k=A(1), v=A(2), dt=ba.BA_BF16, B=1, H=1, N=8, d=64, kb=A(5), km=A(6), vq=A(7), vs=A(8)):
+        return L.ba_pack_k_quant_v(k, v, dt, B, H, N, d, kb, km, vq, vs, None)
+    assert pkv(k=None) == INV and pkv(v=None) == INV and pkv(km=None) == INV and pkv(vs=None) == INV
+    assert pkv(N=0) == INV and pkv(d=129) == UNS and pkv(dt=ba.BA_F32) == UNS
+    assert pkv(N=ba.BA_MAX_TOKENS + 1) == UNS
+    assert pkv(k=ctypes.c_void_p(P + 1 * (1 << 32) + 8)) == INV   # not 16-byte aligned
+    assert pkv(vq=A(5)) == INV    # outputs overlap
+    assert pkv(kb=A(1)) == INV    # output aliases the K input
+
+
+def test_attention_q16_rejections(L):
+    def aq(q=A(0), q_dt=ba.BA_BF16, bias=None, B=2, H=2, N=16, d=64, out=A(9), out_dt=ba.BA_BF16, **kw):
+        args = dict(kb=A(3), km=A(4), vq=A(5), vs=A(6))
+        args.update(kw)
+        pb = ctypes.byref(bias) if bias is not None else None
+        return L.ba_attention_fwd_q16(q, q_dt, args["kb"], args["km"], args["vq"], args["vs"], pb, B, H, N, d,
+                                      out, out_dt, None)
+    assert aq(q=None) == INV and aq(kb=None) == INV and aq(out=None) == INV
+    assert aq(d=20) == UNS and aq(d=129) == UNS and aq(d=0) == INV    # d % 8 == 0 only
+    assert aq(q_dt=ba.BA_F32) == UNS and aq(out_dt=ba.BA_F32) == UNS
+    assert aq(q=ctypes.c_void_p(P + 8)) == INV                        # not 16-byte aligned
+    assert aq(out=A(0)) == INV                                        # output aliases Q
+    assert aq(out=A(5)) == INV                                        # output aliases vq
+    assert aq(bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, 0)) == INV
 
 
 def test_hamming_rejections(L):
