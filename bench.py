@@ -5,7 +5,9 @@
 One step = the whole hot path over one batch of synthetic input already
 resident in HBM: ba_pack_qk_quant_v (sign bits + scales of Q and K and
 channel-wise int8 V, one call: the outputs of ba_pack_qk and ba_quant_v) and
-ba_attention_fwd (fused attention), on one stream.
+ba_attention_fwd (fused attention), on one stream. The same pass with Q
+binarised inside the attention (ba_pack_k_quant_v + ba_attention_fwd_q16, the
+same output bit for bit) is timed beside it under "q_in_prologue".
 The headline value is effective attention throughput 4*B*H*N^2*d / t_step
 (d the real head dim), for the DiT-XL/2 512px layer (B=8, H=16, N=1024,
 d=72, dense fp16 bias shared over the batch); the same figures for the
@@ -178,6 +180,16 @@ class Workload:
         self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
                                  self.bias, self.out, self.stream)
 
+    def step_q16(self):
+        """The same pass with Q packed inside the attention: ba_pack_k_quant_v
+        (K signs and scales, int8 V) and ba_attention_fwd_q16."""
+        self.ba.ba_pack_k_quant_v(self.k, self.v, self.kbits, self.kmu, self.vq, self.vscale, self.stream)
+        self.attn_q16()
+
+    def attn_q16(self):
+        self.ba.ba_attention_fwd_q16(self.q, self.kbits, self.kmu, self.vq, self.vscale, self.bias, self.out,
+                                     self.stream)
+
     def attn_online(self):
         self.ba.ba_attention_fwd_online(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
                                         self.bias, self.out, self.stream)
@@ -235,42 +247,54 @@ def device_warmup(fn, seconds: float) -> int:
     return n
 
 
-def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmup_s: float = 0.3) -> dict:
+def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmup_s: float = 0.3,
+            with_q16: bool = True, form: str = "two-step") -> dict:
+    """form: "two-step" (ba_pack_qk_quant_v + ba_attention_fwd) or "q16"
+    (ba_pack_k_quant_v + ba_attention_fwd_q16) is the step timed."""
     import workloads
     torch = __import__("torch")
     w = Workload(name)
     s = w.spec
     ops = workloads.eff_ops(s)
-    dev_warm = device_warmup(w.step, device_warmup_s)
+    step_fn, attn_fn = (w.step, w.attn) if form == "two-step" else (w.step_q16, w.attn_q16)
+    dev_warm = device_warmup(step_fn, device_warmup_s)
     # whole step, bracketed by synchronisation on both sides
     for _ in range(warmup):
-        w.step()
+        step_fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(w.stream)
     for _ in range(steps):
-        w.step()
+        step_fn()
     e1.record(w.stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     step_ms = e0.elapsed_time(e1) / steps
     # the dominant kernel alone: median (and min) of five runs of back-to-back
     # launches, and the median of single launches with cold caches
-    runs = sorted(w.time(w.attn, iters=max(steps, 20), warmup=3 if i == 0 else 0) for i in range(5))
+    runs = sorted(w.time(attn_fn, iters=max(steps, 20), warmup=3 if i == 0 else 0) for i in range(5))
     attn_ms = runs[2]
-    attn_cold_ms = w.time_cold(w.attn) if cold else None
+    # the step with Q packed in the attention's prologue (d % 8 == 0), same
+    # protocol, right after the step's own runs (before the cold-cache launches)
+    q16 = None
+    if with_q16 and form == "two-step" and s.d % 8 == 0:
+        device_warmup(w.step_q16, min(device_warmup_s, 0.1))
+        q16 = {"step_ms": sorted(w.time(w.step_q16, iters=steps, warmup=warmup) for _ in range(3))[1],
+               "attn_ms": sorted(w.time(w.attn_q16, iters=max(steps, 20), warmup=3) for _ in range(3))[1]}
+    attn_cold_ms = w.time_cold(attn_fn) if cold else None
     # the one-pass (running maximum) form beside it, d <= 64
     online_ms = None
     if s.d <= 64:
         online_ms = sorted(w.time(w.attn_online, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
-        w.attn()  # leave the two-pass output in place
+    step_fn()  # leave the step's output in place
     nbytes = algorithmic_bytes(s)
     return {
         "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
         "device_warmup": {"seconds": device_warmup_s, "steps": dev_warm},
         "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms, "online_ms": online_ms,
+        "q16": q16,
         "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
         "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
@@ -347,6 +371,12 @@ def main() -> int:
     ap.add_argument("--device-warmup", type=float, default=0.3, metavar="SECONDS",
                     help="wall time of back-to-back steps run before the W warm-up steps, so the timed "
                          "steps run at the clock the GPU holds under sustained load (0 to skip)")
+    ap.add_argument("--form", choices=["two-step", "q16"], default="two-step",
+                    help="the step timed: two-step (ba_pack_qk_quant_v + ba_attention_fwd, the default) or "
+                         "q16 (ba_pack_k_quant_v + ba_attention_fwd_q16: Q binarised inside the attention)")
+    ap.add_argument("--no-q16", action="store_true",
+                    help="do not time the step with Q packed inside the attention (its attention launches share "
+                         "the kernel name of the two-step form's in a profile)")
     ap.add_argument("--block", action="store_true",
                     help="only the attention block (QKV projection, BinaryAttention, output "
                          "projection) at B=2, N=4096, 16 heads of 64, synthetic bf16 weights")
@@ -388,7 +418,8 @@ def main() -> int:
     import workloads
     names = list(workloads.WORKLOADS) if args.all else [args.workload]
     for name in names:
-        r = measure(name, args.steps, args.warmup, cold=not args.all, device_warmup_s=args.device_warmup)
+        r = measure(name, args.steps, args.warmup, cold=not args.all, device_warmup_s=args.device_warmup,
+                    with_q16=not args.no_q16, form=args.form)
         s = r["spec"]
         line = {
             "metric": "effective attention TOPS (4*B*H*N^2*d / t_step), step = pack Q/K + quantise V + fused attention",
@@ -399,6 +430,7 @@ def main() -> int:
             "dtype_detail": "Q.K: +-1 signs on fp4 MFMA (exact integer sums); softmax fp32; P.V u8 x int8 -> int32 MFMA",
             "data": "synthetic (seeded N(0,1) activations of the workload's shape)",
             "config": config_of(s),
+            "step_form": args.form,
             "device_warmup": r["device_warmup"],
             "attn_ms": round(r["attn_ms"], 5), "attn_min_ms": round(r["attn_min_ms"], 5),
             "attn_tops": round(r["attn_tops"], 3),
@@ -427,11 +459,21 @@ def main() -> int:
             line["attn_online"] = {"ms": round(r["online_ms"], 5), "vs_two_pass": round(r["online_ms"] / r["attn_ms"], 3),
                                    "note": "ba_attention_fwd_online: one pass over the keys with a running "
                                            "row maximum (same timing protocol)"}
+        if r["q16"] is not None:
+            q = r["q16"]
+            line["q_in_prologue"] = {
+                "ms_per_step": round(q["step_ms"], 5), "attn_ms": round(q["attn_ms"], 5),
+                "value": round(r["ops"] / (q["step_ms"] * 1e-3) / 1e12, 3),
+                "note": "step = ba_pack_k_quant_v + ba_attention_fwd_q16 (Q binarised inside the attention; "
+                        "the same output bit for bit); mean of back-to-back steps, median of 3 runs"}
         if not args.all and args.secondary:
-            r2 = measure(args.secondary, args.steps, args.warmup, device_warmup_s=args.device_warmup)
+            r2 = measure(args.secondary, args.steps, args.warmup, device_warmup_s=args.device_warmup,
+                         with_q16=not args.no_q16, form=args.form)
             line["secondary"] = {"config": config_of(r2["spec"]), "value": round(r2["tops"], 3),
                                  "ms_per_step": round(r2["step_ms"], 5), "attn_ms": round(r2["attn_ms"], 5),
                                  "attn_online_ms": None if r2["online_ms"] is None else round(r2["online_ms"], 5),
+                                 "q_in_prologue_ms_per_step": None if r2["q16"] is None
+                                 else round(r2["q16"]["step_ms"], 5),
                                  "attn_tops": round(r2["attn_tops"], 3),
                                  "frac_int8_peak": round(r2["attn_tops"] / INT8_PEAK_TOPS, 4),
                                  "frac_valu_peak": round(r2["valu_tops"] / VALU_PEAK_TLANEOPS, 4)}
