@@ -323,6 +323,118 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
   }
 }
 
+// quant_v for heads split over S blocks of 1024 threads, each part's rows
+// held in registers as in quant_heads_block (2 <= S <= kQvMaxParts): every
+// block takes the channel maxima over ALL N rows of its head itself,
+// streaming them once (eight 16-byte loads in flight per thread), so no
+// block depends on another and no zero fill or second launch is needed;
+// then it loads its own rows [s RB, s RB + RB), quantises them and writes
+// int8, and part 0 stores the scales. The maximum and the float32
+// arithmetic are those of the other quantisers, so the outputs are the same
+// bit for bit. Block b takes head 8 (i / S) + b % 8, part i % S, with
+// i = b / 8: the parts of a head run on one XCD (blocks are dealt to the
+// XCDs in turn) and share its L2 for the repeated reads. Blocks whose head
+// is past nbh do nothing.
+constexpr int kQvMaxParts = 4;
+template <int DT>
+__device__ __forceinline__ void quant_head_part_block(const uint16_t* __restrict__ v, const InView& in, int N,
+                                                      int d, int64_t nbh, int S, int RB, int64_t b,
+                                                      int8_t* __restrict__ vq, float* __restrict__ vscale,
+                                                      uint32_t* smem) {
+  const int64_t i = b >> 3;
+  const int part = (int)(i % S);
+  const int64_t bh = 8 * (i / S) + (b & 7);
+  if (bh >= nbh) return;  // (the whole block)
+  uint32_t* amax_bits = smem;
+  float* inv_s = reinterpret_cast<float*>(smem + 128);
+  const int P = d >> 3, R = 1024 / P;
+  const int piece = threadIdx.x % P, r0 = threadIdx.x / P;
+  const bool active = r0 < R;
+  if (threadIdx.x < d) amax_bits[threadIdx.x] = 0u;
+  const uint16_t* vh = v + (bh / in.H) * in.sb + (bh % in.H) * in.sh + 8 * piece;
+  // channel maxima of |v| over the head on the 16-bit patterns (magnitude
+  // bits order like |v| for finite values)
+  us2 mb[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+  auto take = [&](const u4v& raw) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mb[w] = __builtin_elementwise_max(mb[w], __builtin_bit_cast(us2, raw[w] & 0x7FFF7FFFu));
+  };
+  if (active) {
+    int j = r0;
+    for (; j + 7 * R < N; j += 8 * R) {
+      u4v raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * R) * in.sn);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) take(raw[u]);
+    }
+    for (; j < N; j += R) take(*reinterpret_cast<const u4v*>(vh + (int64_t)j * in.sn));
+  }
+  __syncthreads();  // (the zeroed maxima)
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicMax(&amax_bits[8 * piece + e], __float_as_uint(to_f32<DT>(mb[e >> 1][e & 1])));
+  }
+  __syncthreads();
+  if (threadIdx.x < d) {
+    const float a = __uint_as_float(amax_bits[threadIdx.x]);
+    inv_s[threadIdx.x] = a > 0.0f ? 127.0f / a : 0.0f;
+    if (part == 0) vscale[bh * d + threadIdx.x] = a / 127.0f;
+  }
+  __syncthreads();
+  // this part's rows: r_begin + r0, + R, ... below r_end, held in registers
+  const int r_begin = part * RB, r_end = min(N, r_begin + RB);
+  const int cnt = active && r_begin + r0 < r_end ? min(kQvRows, (r_end - r_begin - r0 + R - 1) / R) : 0;
+  u4v x[kQvRows];
+  {
+    const uint16_t* src = vh + (int64_t)(r_begin + r0) * in.sn;
+    const int64_t step = (int64_t)R * in.sn;
+#pragma unroll
+    for (int k = 0; k < kQvRows; ++k, src += step)
+      x[k] = k < cnt ? *reinterpret_cast<const u4v*>(src) : (u4v){0u, 0u, 0u, 0u};
+  }
+  float inv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
+  int8_t* dst = vq + bh * N * d + 8 * piece + (int64_t)(r_begin + r0) * d;
+#pragma unroll
+  for (int k = 0; k < kQvRows; ++k, dst += (int64_t)R * d) {
+    if (k < cnt) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float y = __builtin_rintf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16))) * inv[e]);
+        y = fminf(fmaxf(y, -127.0f), 127.0f);
+        const uint32_t bq = (uint32_t)(uint8_t)(int8_t)(int)y;
+        if (e < 4) lo |= bq << (8 * e); else hi |= bq << (8 * (e - 4));
+      }
+      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    }
+  }
+}
+
+// Parts per head for quant_head_part_block: 0 where one block holds a head
+// (or the rows are not 16-byte pieces), and where more than kQvMaxParts
+// would be needed (the split quantiser then takes the head).
+int quant_parts(int N, int d) {
+  if (d % 8 != 0) return 0;
+  const int64_t cap = (int64_t)kQvRows * (1024 / (d / 8));  // rows one block holds
+  if (N <= cap) return 0;
+  const int64_t S = (N + cap - 1) / cap;
+  return S <= kQvMaxParts ? (int)S : 0;
+}
+// V blocks (XCD-dealt, see quant_head_part_block) and rows per part
+int64_t quant_part_blocks(int64_t nbh, int S) { return 8 * (int64_t)S * ((nbh + 7) / 8); }
+int quant_part_rows(int N, int S) { return (N + S - 1) / S; }
+
+template <int DT>
+__global__ __launch_bounds__(1024) void quant_v_parts_kernel(
+    const uint16_t* __restrict__ v, InView in, int nbh, int N, int d, int S, int RB, int8_t* __restrict__ vq,
+    float* __restrict__ vscale) {
+  __shared__ uint32_t smem[2 * 128];
+  quant_head_part_block<DT>(v, in, N, d, nbh, S, RB, blockIdx.x, vq, vscale, smem);
+}
+
 // Heads per 1024-thread block for the register-resident quantiser: the most
 // (a power of two, at most 8) whose T = 1024 / HB threads per head still
 // hold at most kQvRows rows each, while leaving at least 64 blocks; with
@@ -348,8 +460,9 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
 }
 
 // Pack Q and K and quantise V in one launch (d % 8 == 0, heads that fit the
-// register-resident quantiser): blocks 0 .. nvb-1 quantise HB heads each
-// (the long-running ones, dispatched first), the rest pack npq blocks of
+// register-resident quantiser, whole or in S parts): blocks 0 .. nvb-1
+// quantise HB heads each, or S > 0 parts of heads (the long-running ones,
+// dispatched first), the rest pack npq blocks of
 // tokens of Q (npb, or 0 when Q is left to the attention), then npb of K,
 // all with 1024 threads. STR (a strided view):
 // the pack blocks are nbph per head, each within one head. At most 64 VGPRs
@@ -359,15 +472,16 @@ __global__ __launch_bounds__(1024) void quant_v_head_kernel(
 template <int DT, bool STR, int U>
 __global__ __launch_bounds__(1024, 8) void prepass_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, InView in,
-    int nbh, int N, int d, int HB, int64_t nvb, int64_t npq, int64_t npb, int64_t nbph, uint32_t* __restrict__ qbits,
-    float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu, int8_t* __restrict__ vq,
-    float* __restrict__ vscale) {
+    int nbh, int N, int d, int HB, int S, int RB, int64_t nvb, int64_t npq, int64_t npb, int64_t nbph,
+    uint32_t* __restrict__ qbits, float* __restrict__ qmu, uint32_t* __restrict__ kbits, float* __restrict__ kmu,
+    int8_t* __restrict__ vq, float* __restrict__ vscale) {
   __shared__ uint32_t bits_s[1024 * U];
   __shared__ double sum_s[1024 * U];
   const int64_t ntok = (int64_t)nbh * N;
   const int64_t b = blockIdx.x;
   if (b < nvb) {
-    quant_heads_block<DT>(v, in, N, d, b * HB, nbh, HB, vq, vscale, bits_s);
+    if (S > 0) quant_head_part_block<DT>(v, in, N, d, nbh, S, RB, b, vq, vscale, bits_s);
+    else quant_heads_block<DT>(v, in, N, d, b * HB, nbh, HB, vq, vscale, bits_s);
   } else if constexpr (STR) {
     const bool isk = b - nvb >= npq;
     const int64_t pb = b - nvb - (isk ? npq : 0);
@@ -537,6 +651,18 @@ hipError_t launch_quant_v(const void* v, ba_dtype dt, const InView& in, int nbh,
       hipLaunchKernelGGL(quant_v_head_kernel<BA_BF16>, dim3(nvb), dim3(1024), 0, s, v16, in, nbh, N, d, HB, vq, vscale);
     return hipGetLastError();
   }
+  if (in.vec && quant_parts(N, d) > 0) {
+    const int S = quant_parts(N, d), RB = quant_part_rows(N, S);
+    const int64_t nvb = quant_part_blocks(nbh, S);
+    if (nvb > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (dt == BA_F16)
+      hipLaunchKernelGGL(quant_v_parts_kernel<BA_F16>, dim3((unsigned)nvb), dim3(1024), 0, s, v16, in, nbh, N, d, S, RB,
+                         vq, vscale);
+    else
+      hipLaunchKernelGGL(quant_v_parts_kernel<BA_BF16>, dim3((unsigned)nvb), dim3(1024), 0, s, v16, in, nbh, N, d, S,
+                         RB, vq, vscale);
+    return hipGetLastError();
+  }
   if (in.vec) {
     const int64_t n = (int64_t)nbh * d;
     if ((n + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -565,7 +691,8 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
     if (e != hipSuccess) return e;
     return launch_quant_v(v, dt, in, nbh, N, d, vq, vscale, s);
   }
-  if (!quant_in_registers(N, d)) {
+  const int S = quant_in_registers(N, d) ? 0 : quant_parts(N, d);
+  if (!quant_in_registers(N, d) && S == 0) {
     // long heads: the packing launch also zeroes vscale, then the split
     // quantiser's two passes
     hipError_t e = launch_pack_qk(q, k, dt, in, nbh, N, d, qbits, qmu, kbits, kmu, s,
@@ -575,8 +702,9 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
                         : launch_quant_v_split_ab<BA_BF16>(v16, in, nbh, N, d, vq, vscale, s);
   }
   const bool str = !in.dense(N, d);
-  const int HB = quant_heads_per_block(nbh, N, d);
-  const int64_t nvb = (nbh + HB - 1) / HB;
+  const int HB = S > 0 ? 1 : quant_heads_per_block(nbh, N, d);
+  const int RB = S > 0 ? quant_part_rows(N, S) : 0;
+  const int64_t nvb = S > 0 ? quant_part_blocks(nbh, S) : (nbh + HB - 1) / HB;
   const int TB = 1024 * kPackUFused / (d / 8);  // tokens per packing block
   const int64_t nbph = (N + TB - 1) / TB;
   const int64_t npb = str ? nbh * nbph : (ntok + TB - 1) / TB;
@@ -586,7 +714,8 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, ba_dtype 
   constexpr int U = kPackUFused;
   auto kern = dt == BA_F16 ? (str ? prepass_fused_kernel<BA_F16, true, U> : prepass_fused_kernel<BA_F16, false, U>)
                            : (str ? prepass_fused_kernel<BA_BF16, true, U> : prepass_fused_kernel<BA_BF16, false, U>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, nvb, npq, npb, nbph,
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(1024), 0, s, q16, k16, v16, in, nbh, N, d, HB, S, RB, nvb, npq,
+                     npb, nbph,
                      qbits, qmu, kbits, kmu, vq, vscale);
   return hipGetLastError();
 }

@@ -124,11 +124,13 @@ ba_status ba_quant_v(const void* v, ba_dtype dt, int B, int H, int N, int d,
  * ba_attention_fwd (as every forward pass does): the same outputs, bit for
  * bit, with the same layouts, alignment and error rules as the two calls
  * (q, k, v all [B,H,N,d] of dt). Where d % 8 == 0 and a head fits the
- * register-resident V quantiser (N <= 10 * 1024 / (d / 8)) it is a single
- * launch in which the V heads and the Q/K token blocks run side by side;
- * with longer heads the packing launch also clears vscale and the V
- * quantiser's two passes follow; otherwise it enqueues the two calls'
- * kernels in turn. No output may overlap another output or an input. */
+ * register-resident V quantiser whole (N <= 10 * 1024 / (d / 8)) or in up
+ * to four parts (each part's block then reads the whole head for the
+ * channel maxima itself), it is a single launch in which the V heads and
+ * the Q/K token blocks run side by side; with longer heads the packing
+ * launch also clears vscale and the V quantiser's two passes follow;
+ * otherwise it enqueues the two calls' kernels in turn. No output may
+ * overlap another output or an input. */
 ba_status ba_pack_qk_quant_v(const void* q, const void* k, const void* v, ba_dtype dt, int B, int H,
                              int N, int d, uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu,
                              int8_t* vq, float* vscale, void* stream);

@@ -239,8 +239,11 @@ def test_key_permutation():
     # the register-resident quantiser's last head length (10 rows per thread)
     # and the first one past it
     (1, 4, 1280, 64), (1, 4, 1281, 64), (1, 2, 1130, 72), (1, 2, 1131, 72),
-    # heads split over several blocks (maxima and sums combined across blocks)
-    (2, 3, 1600, 72), (1, 1, 20000, 128), (2, 16, 4096, 64), (1, 4, 1537, 64), (1, 1, 7000, 16)])
+    # heads split over two to four blocks that each take the whole head's
+    # maxima (head counts not a multiple of the eight XCDs included), and the
+    # two-pass split quantiser past four parts
+    (2, 3, 1600, 72), (1, 1, 20000, 128), (2, 16, 4096, 64), (1, 4, 1537, 64), (1, 1, 7000, 16),
+    (1, 3, 5120, 64), (1, 1, 5121, 64), (3, 5, 2261, 72), (1, 2, 2560, 128), (1, 1, 2561, 128)])
 @pytest.mark.parametrize("dt", [F16, BF16])
 def test_quant_v_launch_shapes(B, H, N, d, dt):
     rng = np.random.default_rng(B * 1000003 + H * 1009 + N * 13 + d + dt)
@@ -255,6 +258,31 @@ def test_quant_v_launch_shapes(B, H, N, d, dt):
     rq, rs = oracle.quant_v(bits, dt)
     assert np.array_equal(vq.cpu().numpy(), rq)
     assert np.array_equal(vs.cpu().numpy(), rs)
+
+
+# the one-launch pre-pass (and its K/V-only form) at the head lengths that
+# select each V path: heads in registers, heads in two to four parts, the
+# split quantiser with the zero fill in the packing launch
+@pytest.mark.parametrize("B,H,N,d", [(2, 3, 1130, 72), (2, 3, 1600, 72), (1, 3, 5120, 64), (3, 5, 2261, 72),
+                                     (1, 1, 5121, 64), (1, 2, 2560, 128), (2, 16, 4096, 64)])
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_prepass_launch_shapes(B, H, N, d, dt):
+    rng = np.random.default_rng(B * 7919 + H * 101 + N * 7 + d + dt)
+    x = rng.standard_normal((3, B, H, N, d)).astype(np.float32)
+    x[2, ..., 0] *= 30.0
+    x[2, ..., 3] = 0.0
+    q16, k16, v16 = (to_bits(x[i], dt) for i in range(3))
+    qd, kd, vd = (to_dev(b, dt) for b in (q16, k16, v16))
+    qb, qm, kb, km, vq, vs = ba.prepare(qd, kd, vd)
+    kb2, km2, vq2, vs2 = ba.prepare_kv(kd, vd)
+    torch.cuda.synchronize()
+    rqb, rqm = oracle.pack(q16, dt)
+    rkb, rkm = oracle.pack(k16, dt)
+    rvq, rvs = oracle.quant_v(v16, dt)
+    assert np.array_equal(qb.cpu().numpy().view(np.uint32), rqb) and np.array_equal(qm.cpu().numpy(), rqm)
+    for b_, m_, q_, s_ in ((kb, km, vq, vs), (kb2, km2, vq2, vs2)):
+        assert np.array_equal(b_.cpu().numpy().view(np.uint32), rkb) and np.array_equal(m_.cpu().numpy(), rkm)
+        assert np.array_equal(q_.cpu().numpy(), rvq) and np.array_equal(s_.cpu().numpy(), rvs)
 
 
 # every bias kind at head dims that select the smaller kernel instantiations
