@@ -83,6 +83,15 @@ def algorithmic_bytes(s) -> int:
     return nb
 
 
+def prepass_bytes(s) -> int:
+    """HBM bytes the pre-pass (ba_pack_qk_quant_v) must move: Q, K and V read
+    once (16-bit), sign words and scales of Q and K, int8 V and the channel
+    scales written."""
+    W = (s.d + 31) // 32
+    BH, N, d = s.B * s.H, s.N, s.d
+    return 3 * 2 * BH * N * d + 2 * BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d
+
+
 def traffic_for(name: str):
     """Measured HBM bytes per attention launch, if the counters were taken
     on the current kernel source."""
@@ -171,10 +180,15 @@ class Workload:
         self.stream = torch.cuda.current_stream()
 
     def step(self):
-        ba = self.ba
-        ba.ba_pack_qk_quant_v(self.q, self.k, self.v, self.qbits, self.qmu, self.kbits, self.kmu,
-                              self.vq, self.vscale, self.stream)
+        self.prepass()
         self.attn()
+
+    def prepass(self):
+        self.ba.ba_pack_qk_quant_v(self.q, self.k, self.v, self.qbits, self.qmu, self.kbits, self.kmu,
+                                   self.vq, self.vscale, self.stream)
+
+    def prepass_kv(self):
+        self.ba.ba_pack_k_quant_v(self.k, self.v, self.kbits, self.kmu, self.vq, self.vscale, self.stream)
 
     def attn(self):
         self.ba.ba_attention_fwd(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
@@ -183,7 +197,7 @@ class Workload:
     def step_q16(self):
         """The same pass with Q packed inside the attention: ba_pack_k_quant_v
         (K signs and scales, int8 V) and ba_attention_fwd_q16."""
-        self.ba.ba_pack_k_quant_v(self.k, self.v, self.kbits, self.kmu, self.vq, self.vscale, self.stream)
+        self.prepass_kv()
         self.attn_q16()
 
     def attn_q16(self):
@@ -276,6 +290,9 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmu
     # launches, and the median of single launches with cold caches
     runs = sorted(w.time(attn_fn, iters=max(steps, 20), warmup=3 if i == 0 else 0) for i in range(5))
     attn_ms = runs[2]
+    # the pre-pass alone (HBM-bound), same protocol
+    pre_fn = w.prepass if form == "two-step" else w.prepass_kv
+    pre_ms = sorted(w.time(pre_fn, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
     # the step with Q packed in the attention's prologue (d % 8 == 0), same
     # protocol, right after the step's own runs (before the cold-cache launches)
     q16 = None
@@ -294,7 +311,7 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmu
         "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
         "device_warmup": {"seconds": device_warmup_s, "steps": dev_warm},
         "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms, "online_ms": online_ms,
-        "q16": q16,
+        "q16": q16, "pre_ms": pre_ms,
         "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
         "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
@@ -348,6 +365,22 @@ def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64, device_warmu
             "attn_dense_inputs_ms": attn_dense_ms,
             "gemm_ms": gemm_ms, "tokens_per_s": B * N / (block_ms * 1e-3),
             "attn_ops": 4.0 * B * H * N * N * d, "gemm_flops": 2.0 * B * N * C * 4 * C}
+
+
+def prepass_line(r, form: str) -> dict:
+    """The pre-pass launch against the HBM roofline (it moves each input and
+    output once and does little arithmetic)."""
+    s = r["spec"]
+    nb = prepass_bytes(s)
+    if form != "two-step":  # K and V only
+        W = (s.d + 31) // 32
+        nb -= 2 * s.B * s.H * s.N * s.d + s.B * s.H * s.N * (4 * W + 4)
+    gbs = nb / (r["pre_ms"] * 1e-3) / 1e9
+    return {"call": "ba_pack_qk_quant_v" if form == "two-step" else "ba_pack_k_quant_v",
+            "ms": round(r["pre_ms"], 5), "bound": "hbm", "alg_bytes": nb, "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "note": "algorithmic bytes (16-bit Q, K, V read; packed and quantised outputs written) / launch "
+                    "time (HIP events, back-to-back launches, median of 3 runs)"}
 
 
 def config_of(s) -> dict:
@@ -449,6 +482,7 @@ def main() -> int:
                           "note": "effective ops 4*B*H*N^2*d per launch / launch time"},
             "hbm": {"alg_bytes_per_launch": r["alg_bytes"], "achieved_GBs": round(r["attn_gbs"], 1),
                     "peak_GBs": HBM_PEAK_GBS, "frac": round(r["attn_gbs"] / HBM_PEAK_GBS, 4)},
+            "prepass": prepass_line(r, args.form),
         }
         if r["attn_cold_ms"] is not None:
             c = r["attn_cold_ms"]
