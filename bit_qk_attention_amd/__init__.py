@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.ba_pack_k_quant_v.restype = I
         L.ba_attention_fwd_q16.argtypes = [P, I, P, P, P, P, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
         L.ba_attention_fwd_q16.restype = I
+        L.ba_attention_fwd_qkv16.argtypes = [P, P, P, I, ctypes.POINTER(ba_bias), I, I, I, I, P, I, P]
+        L.ba_attention_fwd_qkv16.restype = I
         L.ba_debug_hamming_scores.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
         L.ba_debug_hamming_scores.restype = I
         L.ba_status_string.argtypes = [I]
@@ -257,6 +259,16 @@ def ba_attention_fwd_q16(q, kbits, kmu, vq, vscale, bias, out, stream=None) -> N
     _check("ba_attention_fwd_q16", lib().ba_attention_fwd_q16(
         _ptr(q), _dt(q), _ptr(kbits), _ptr(kmu), _ptr(vq), _ptr(vscale),
         ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
+
+
+def ba_attention_fwd_qkv16(q, k, v, bias, out, stream=None) -> None:
+    """The whole forward pass in one launch for short heads (N <= 256, d % 8 == 0,
+    d <= 96): q, k, v [B,H,N,d] fp16/bf16, binarised and quantised inside the kernel."""
+    _require_gpu(q, k, v, out)
+    B, H, N, d = out.shape
+    cb = (bias or Bias()).to_c()
+    _check("ba_attention_fwd_qkv16", lib().ba_attention_fwd_qkv16(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(cb), B, H, N, d, _ptr(out), _dt(out), _stream(stream)))
 
 
 def ba_debug_hamming_scores(qbits, kbits, d, bh_begin, bh_count, row_begin, row_count, sigma,

@@ -106,26 +106,35 @@ ba_status prepass_checked(const void* q, const void* k, const void* v, const InV
                                  static_cast<hipStream_t>(stream)));
 }
 
-// q16 != nullptr: Q given as 16-bit values of type q16_dt (qbits, qmu unused).
+// q16 != nullptr: Q given as 16-bit values of type q16_dt (qbits, qmu unused);
+// kv16: K and V too, as k16 and v16 of the same type (kbits, kmu, vq, vscale
+// unused).
 ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint32_t* kbits, const float* kmu,
                             const int8_t* vq, const float* vscale, const ba_bias* bias, int B,
                             int H, int N, int d, void* out, const ba_strides& ost, int out_align, int out_dt,
-                            void* stream, int online = 0, const void* q16 = nullptr, int q16_dt = -1) {
+                            void* stream, int online = 0, const void* q16 = nullptr, int q16_dt = -1,
+                            bool kv16 = false, const void* k16 = nullptr, const void* v16 = nullptr) {
   if (q16) qbits = nullptr, qmu = nullptr;
-  if ((!q16 && (!qbits || !qmu)) || !kbits || !kmu || !vq || !vscale || !out) return BA_ERR_INVALID_ARG;
+  if (kv16) {
+    kbits = nullptr, kmu = nullptr, vq = nullptr, vscale = nullptr;
+    if (!q16 || !k16 || !v16 || !out) return BA_ERR_INVALID_ARG;
+  } else if ((!q16 && (!qbits || !qmu)) || !kbits || !kmu || !vq || !vscale || !out) {
+    return BA_ERR_INVALID_ARG;
+  }
   ba_status st = check_shape(B, H, N, d);
   if (st != BA_OK) return st;
   if (online && d > 64) return BA_ERR_UNSUPPORTED;
   if (!dtype16(out_dt)) return BA_ERR_UNSUPPORTED;
   if (q16 && (!dtype16(q16_dt) || d % 8 != 0)) return BA_ERR_UNSUPPORTED;
   if (!aligned(qbits, 16) || !aligned(kbits, 16) || !aligned(vq, 16) || !aligned(out, out_align) ||
-      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(q16, 16))
+      !aligned(qmu, 4) || !aligned(kmu, 4) || !aligned(vscale, 4) || !aligned(q16, 16) || !aligned(k16, 16) ||
+      !aligned(v16, 16))
     return BA_ERR_INVALID_ARG;
   const int64_t ntok = (int64_t)B * H * N;
   const int64_t W = (d + 31) / 32;
   AttnArgs a = {};
   a.qbits = qbits; a.qmu = qmu; a.kbits = kbits; a.kmu = kmu; a.vq = vq; a.vscale = vscale;
-  a.q16 = q16; a.q16_dt = q16_dt;
+  a.q16 = q16; a.q16_dt = q16_dt; a.k16 = k16; a.v16 = v16;
   a.B = B; a.H = H; a.N = N; a.d = d; a.out = out; a.out_dt = out_dt; a.online = online;
   a.out_sb = ost.batch; a.out_sh = ost.head; a.out_sn = ost.token;
   a.bias_kind = BA_BIAS_NONE;
@@ -159,12 +168,14 @@ ba_status attention_checked(const uint32_t* qbits, const float* qmu, const uint3
     a.bias = bias->data;
   }
   const int64_t out_bytes = view_extent(ost, B, H, N, d) * 2;
-  const void* ins[8] = {qbits, qmu, kbits, kmu, vq, vscale, a.bias, q16};
-  const int64_t isz[8] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
-                          (int64_t)B * H * d * 4, bias_bytes, ntok * d * 2};
-  for (int i = 0; i < 8; ++i)
+  const void* ins[10] = {qbits, qmu, kbits, kmu, vq, vscale, a.bias, q16, k16, v16};
+  const int64_t isz[10] = {ntok * W * 4, ntok * 4, ntok * W * 4, ntok * 4, ntok * d,
+                           (int64_t)B * H * d * 4, bias_bytes, ntok * d * 2, ntok * d * 2, ntok * d * 2};
+  for (int i = 0; i < 10; ++i)
     if (overlap(out, out_bytes, ins[i], isz[i])) return BA_ERR_INVALID_ARG;
-  return from_hip(launch_attention(a, static_cast<hipStream_t>(stream)));
+  const hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
+  // (16-bit K and V outside the resident mode: refused before any launch)
+  return (kv16 && e == hipErrorNotSupported) ? BA_ERR_UNSUPPORTED : from_hip(e);
 }
 
 }  // namespace
@@ -262,6 +273,14 @@ ba_status ba_attention_fwd_q16(const void* q, ba_dtype q_dt, const uint32_t* kbi
   const ba_strides dense = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
   return attention_checked(nullptr, nullptr, kbits, kmu, vq, vscale, bias, B, H, N, d, out, dense, 16,
                            raw(out_dt), stream, 0, q, raw(q_dt));
+}
+
+ba_status ba_attention_fwd_qkv16(const void* q, const void* k, const void* v, ba_dtype dt, const ba_bias* bias,
+                                 int B, int H, int N, int d, void* out, ba_dtype out_dt, void* stream) {
+  if (!q || !k || !v) return BA_ERR_INVALID_ARG;
+  const ba_strides dense = {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  return attention_checked(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, bias, B, H, N, d, out, dense, 16,
+                           raw(out_dt), stream, 0, q, raw(dt), true, k, v);
 }
 
 ba_status ba_attention_fwd(const uint32_t* qbits, const float* qmu, const uint32_t* kbits,

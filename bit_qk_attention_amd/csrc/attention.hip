@@ -116,7 +116,9 @@ struct Params {
   const uint32_t* qbits;
   const float* qmu;
   const uint16_t* q16;  // Q as 16-bit values, packed in the prologue (then qbits, qmu unused)
-  int q16_f16;          // q16 is fp16 (else bf16)
+  int q16_f16;          // q16, k16, v16 are fp16 (else bf16)
+  const uint16_t* k16;  // resident mode only: K and V as 16-bit values, binarised and quantised
+  const uint16_t* v16;  // by the workgroup itself (then kbits, kmu, vq, vscale unused)
   const uint32_t* kbits;
   const float* kmu;
   const int8_t* vq;
@@ -424,7 +426,8 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   // scale adds the piece sums in channel order (the running sum passes
   // between the two lanes word by word), divides by d in float64 and rounds
   // to float once. raw: the lane's 16-byte pieces (zero past d).
-  auto pack_q16 = [&](auto dtc, const u4v (&raw)[NKB][4], bool valid, uint32_t* wb, float& mu) {
+  auto pack_q16 = [&](auto dtc, const u4v (&raw)[NKB][4], bool valid, uint32_t* wb, float& mu)
+      __attribute__((always_inline)) {
     constexpr int DT = decltype(dtc)::value;
     double ps[NKB][4];
 #pragma unroll
@@ -477,7 +480,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   u4v qraw[NKB][4];
   uint32_t qwb[NKB];
   float qmu_ld = 0.0f;
-  auto issue_q = [&]() {
+  auto issue_q = [&]() __attribute__((always_inline)) {
     if (q_from16) {
       const uint16_t* row = p.q16 + (bh * N + qc) * d;
 #pragma unroll
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
       qmu_ld = (is_attn(MODE) && qvalid) ? p.qmu[bh * N + qi] : 0.0f;
     }
   };
-  auto finish_q = [&]() {
+  auto finish_q = [&]() __attribute__((always_inline)) {
     float qmu = qmu_ld;
     if (q_from16) {
       uint32_t wb[NKB];
@@ -1140,7 +1143,138 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
   // issued, and the query operand formed while they land; one wait, then the V rows of all tiles and the
   // channel scales are started and pass 1 runs while they land; a second
   // wait before pass 2. Neither pass waits or synchronises per tile.
-  auto res_stage = [&]() {
+  // Resident mode from 16-bit K and V (p.k16, p.v16; d % 8 == 0): the
+  // workgroup binarises and quantises its head's keys and values itself,
+  // with the pre-pass kernels' arithmetic, straight into the stages, so the
+  // packed arrays never go through HBM (each head is read by its nqb <= 2
+  // query blocks). Thread j packs key j: the row's 16-byte pieces, sign bits
+  // by a float compare, float64 piece sums of |x| added in channel order,
+  // one float64 division by d; the fp4 operand goes to the slots expand_k
+  // uses. V: channel maxima of |v| (a 16-bit magnitude max per thread, an
+  // LDS max on the float bits), inv = 127 / amax and scale = amax / 127 in
+  // float32, then a second read of the rows quantised into the V stage
+  // layout; the scales stay in LDS for the epilogue. Keys and V rows past N
+  // are left unwritten: their scores are masked and their P.V operand bytes
+  // and channel-sum bytes zeroed, as for the ragged tile's DMA.
+  auto res_stage16 = [&](auto dtc) __attribute__((always_inline)) {
+    constexpr int DT = decltype(dtc)::value;
+    if constexpr (RES && MODE == MODE_ATTN) {
+    static_assert(!RAWK, "the resident mode keeps the fp4 K operand in LDS");
+    issue_q();
+    for (int t = 0; t < ntiles; ++t) {
+      dma_tbl(t, t);
+      stage_koff(t, t);
+    }
+    // vscl holds the maxima' float bits, then 127 / amax while the rows are
+    // quantised, then the scales amax / 127 (thread c keeps amax of channel c)
+    uint32_t* vamax = reinterpret_cast<uint32_t*>(vscl);
+    if (tid < d) vamax[tid] = 0u;
+    if (tid < N) {
+      const uint16_t* row = p.k16 + (bh * N + tid) * d;
+      uint32_t wb[2 * NKB];
+#pragma unroll
+      for (int w = 0; w < 2 * NKB; ++w) wb[w] = 0u;
+      double acc = 0.0;
+#pragma unroll
+      for (int pc = 0; pc < 8 * NKB; ++pc) {
+        if (8 * pc < d) {
+          const u4v raw = *reinterpret_cast<const u4v*>(row + 8 * pc);
+          uint32_t b8 = 0;
+          double sm = 0.0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xf = to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16)));
+            b8 |= xf < 0.0f ? (1u << e) : 0u;
+            sm += (double)fabsf(xf);
+          }
+          wb[pc >> 2] |= b8 << (8 * (pc & 3));
+          acc += sm;
+        }
+      }
+      KS& sb = ksr[tid >> 6];
+      const int kl = tid & 63;
+#pragma unroll
+      for (int w = 0; w < 2 * NKB; ++w)
+        *reinterpret_cast<u4v*>(sb.kx + kl * KROW + kslot<NKB>(kl, w) * 16) =
+            (u4v){fp4_signs(wb[w], 0), fp4_signs(wb[w], 1), fp4_signs(wb[w], 2), fp4_signs(wb[w], 3)};
+      sb.mk[kl] = (float)(acc / (double)d);
+    }
+    // V: thread tid takes 16-byte piece tid % P of rows tid / P + k R
+    const int P = d >> 3, R = 256 / P;
+    const int piece = tid % P, r0 = tid / P;
+    const bool vact = r0 < R;
+    const uint16_t* vh = p.v16 + bh * N * d + 8 * piece;
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 mb[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+    auto take = [&](const u4v& raw) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        mb[w] = __builtin_elementwise_max(mb[w], __builtin_bit_cast(us2, raw[w] & 0x7FFF7FFFu));
+    };
+    if (vact) {
+      int j = r0;
+      for (; j + 3 * R < N; j += 4 * R) {
+        u4v raw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * R) * d);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) take(raw[u]);
+      }
+      for (; j < N; j += R) take(*reinterpret_cast<const u4v*>(vh + (int64_t)j * d));
+    }
+    __syncthreads();  // (the zeroed maxima)
+    if (vact) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        atomicMax(&vamax[8 * piece + e], __float_as_uint(to_f32<DT>(mb[e >> 1][e & 1])));
+    }
+    __syncthreads();
+    float amax_c = 0.0f;
+    if (tid < d) {
+      amax_c = __uint_as_float(vamax[tid]);
+      vscl[tid] = amax_c > 0.0f ? 127.0f / amax_c : 0.0f;
+    }
+    __syncthreads();
+    if (vact) {
+      float inv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) inv[e] = vscl[8 * piece + e];
+      auto quant8 = [&](const u4v& raw, int j) __attribute__((always_inline)) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
+          y = fminf(fmaxf(y, -127.0f), 127.0f);
+          const uint32_t bq = (uint32_t)(uint8_t)(int8_t)(int)y;
+          if (e < 4) lo |= bq << (8 * e); else hi |= bq << (8 * (e - 4));
+        }
+        *reinterpret_cast<uint2*>(vsr[j >> 6].vr + vaddr(j & 63, 8 * piece)) = make_uint2(lo, hi);
+      };
+      int j = r0;
+      for (; j + 3 * R < N; j += 4 * R) {
+        u4v raw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const u4v*>(vh + (int64_t)(j + u * R) * d);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) quant8(raw[u], j + u * R);
+      }
+      for (; j < N; j += R) quant8(*reinterpret_cast<const u4v*>(vh + (int64_t)j * d), j);
+    }
+    finish_q();
+    wait_vm0();
+    __syncthreads();  // (every thread has read its 127 / amax)
+    if (tid < d) vscl[tid] = amax_c / 127.0f;
+    __syncthreads();
+    }
+  };
+  auto res_stage = [&]() __attribute__((always_inline)) {
+    if constexpr (RES && MODE == MODE_ATTN) {
+      if (p.k16) {
+        if (p.q16_f16) res_stage16(IntC<BA_F16>());
+        else res_stage16(IntC<BA_BF16>());
+        return;
+      }
+    }
     if constexpr (RES) {
       issue_q();
       for (int t = 0; t < ntiles; ++t) {
@@ -1828,6 +1962,7 @@ hipError_t launch_b(Params p, int nblocks, hipStream_t s) {
   if constexpr (res_fits<NKB, NCB, BIAS, MODE>()) {
     if (res_takes(p, is_relpos(BIAS))) return launch_t<NKB, NCB, BIAS, MODE, true>(p, nblocks, s);
   }
+  if (p.k16) return hipErrorNotSupported;  // (16-bit K and V: the resident mode only)
   return launch_t<NKB, NCB, BIAS, MODE>(p, nblocks, s);
 }
 
@@ -1864,6 +1999,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.qbits = a.qbits; p.qmu = a.qmu; p.kbits = a.kbits; p.kmu = a.kmu;
   p.q16 = static_cast<const uint16_t*>(a.q16);
   p.q16_f16 = a.q16_dt == BA_F16;
+  p.k16 = static_cast<const uint16_t*>(a.k16);
+  p.v16 = static_cast<const uint16_t*>(a.v16);
   p.vq = a.vq; p.vscale = a.vscale;
   p.bias = a.bias; p.bias_bstride = a.bias_bstride;
   p.grid_h = a.grid_h; p.grid_w = a.grid_w; p.n_prefix = a.n_prefix;

@@ -100,6 +100,9 @@ struct AttnArgs {
   int online;                      // one pass with a running maximum (d <= 64)
   const void* q16;                 // Q as 16-bit values [B,H,N,d] (d % 8 == 0), packed by the
   int q16_dt;                      // attention kernel itself; then qbits and qmu are unused
+  const void* k16;                 // K and V as 16-bit values of q16_dt, binarised and quantised
+  const void* v16;                 // in the resident mode (heads of at most 256 tokens; the launch
+                                   // returns hipErrorNotSupported where it does not apply)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

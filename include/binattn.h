@@ -245,6 +245,24 @@ ba_status ba_attention_fwd_q16(const void* q, ba_dtype q_dt,
                                int B, int H, int N, int d,
                                void* out, ba_dtype out_dt, void* stream);
 
+/* ba_attention_fwd_qkv16: the whole forward pass in one launch, for short
+ * heads: Q, K and V given as 16-bit values [B,H,N,d] of dt (16-byte
+ * aligned, dense), each workgroup binarising its queries and its head's
+ * keys and quantising its head's V itself, with the arithmetic of
+ * ba_pack_qk and ba_quant_v, straight into on-chip memory (zh technical
+ * summary section 2.3: one fused kernel; section 2.2 items 1 and 3). The
+ * output equals ba_pack_qk + ba_quant_v + ba_attention_fwd bit for bit; no
+ * packed or quantised array is written. It applies where a head's keys all
+ * stay on chip at once: N <= 256, d % 8 == 0 and d <= 96, and no bias, a
+ * relative-position table, or a dense fp32 bias with 16-byte rows (N % 4 ==
+ * 0, batch stride % 4 == 0, 16-byte aligned); BA_ERR_UNSUPPORTED otherwise,
+ * with nothing enqueued. Each head's K and V are read by each of its (at most two) query
+ * blocks. Other arguments, layouts and errors as ba_attention_fwd; out must
+ * not overlap q, k or v. */
+ba_status ba_attention_fwd_qkv16(const void* q, const void* k, const void* v, ba_dtype dt,
+                                 const ba_bias* bias, int B, int H, int N, int d,
+                                 void* out, ba_dtype out_dt, void* stream);
+
 /* Integer Hamming similarity for inspection (zh sections 2.1 and 2.2 item 1;
  * it section 2A; fr section 2A): for heads [bh_begin, bh_begin+bh_count) and
  * query rows [row_begin, row_begin+row_count),

@@ -26,6 +26,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"ba_packed_words", "ba_pack_qk", "ba_quant_v", "ba_pack_qk_quant_v",
                           "ba_pack_qk_quant_v_strided", "ba_attention_fwd", "ba_attention_fwd_strided",
                           "ba_attention_fwd_online", "ba_pack_k_quant_v", "ba_attention_fwd_q16",
+                          "ba_attention_fwd_qkv16",
                           "ba_debug_hamming_scores", "ba_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -184,6 +185,21 @@ def test_attention_q16_rejections(L):
     assert aq(out=A(0)) == INV                                        # output aliases Q
     assert aq(out=A(5)) == INV                                        # output aliases vq
     assert aq(bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, 0)) == INV
+
+
+def test_attention_qkv16_rejections(L):
+    """Refused before any launch (also the shapes the one-launch form does
+    not take: those are decided on the host)."""
+    def aqkv(q=A(0), k=A(1), v=A(2), dt=ba.BA_BF16, bias=None, B=2, H=2, N=64, d=64, out=A(9), out_dt=ba.BA_BF16):
+        pb = ctypes.byref(bias) if bias is not None else None
+        return L.ba_attention_fwd_qkv16(q, k, v, dt, pb, B, H, N, d, out, out_dt, None)
+    assert aqkv(q=None) == INV and aqkv(k=None) == INV and aqkv(v=None) == INV and aqkv(out=None) == INV
+    assert aqkv(d=20) == UNS and aqkv(d=128) == UNS and aqkv(N=257) == UNS and aqkv(dt=ba.BA_F32) == UNS
+    assert aqkv(bias=ba_bias(ba.BA_BIAS_DENSE, P + 7 * (1 << 32), ba.BA_F16, 0, 0, 0, 0)) == UNS
+    assert aqkv(N=66, bias=ba_bias(ba.BA_BIAS_DENSE, P + 7 * (1 << 32), ba.BA_F32, 0, 0, 0, 0)) == UNS
+    assert aqkv(v=ctypes.c_void_p(P + 2 * (1 << 32) + 8)) == INV     # not 16-byte aligned
+    assert aqkv(out=A(1)) == INV                                      # output aliases K
+    assert aqkv(bias=ba_bias(ba.BA_BIAS_RELPOS, P + 7 * (1 << 32), ba.BA_F32, 0, 3, 5, 0)) == INV
 
 
 def test_hamming_rejections(L):
