@@ -7,7 +7,9 @@ resident in HBM: ba_pack_qk_quant_v (sign bits + scales of Q and K and
 channel-wise int8 V, one call: the outputs of ba_pack_qk and ba_quant_v) and
 ba_attention_fwd (fused attention), on one stream. The same pass with Q
 binarised inside the attention (ba_pack_k_quant_v + ba_attention_fwd_q16, the
-same output bit for bit) is timed beside it under "q_in_prologue".
+same output bit for bit) is timed beside it under "q_in_prologue", and for
+heads of at most 256 tokens the whole pass in one launch
+(ba_attention_fwd_qkv16) under "qkv_in_one_launch".
 The headline value is effective attention throughput 4*B*H*N^2*d / t_step
 (d the real head dim), for the DiT-XL/2 512px layer (B=8, H=16, N=1024,
 d=72, dense fp16 bias shared over the batch); the same figures for the
@@ -204,6 +206,10 @@ class Workload:
         self.ba.ba_attention_fwd_q16(self.q, self.kbits, self.kmu, self.vq, self.vscale, self.bias, self.out,
                                      self.stream)
 
+    def step_qkv16(self):
+        """The whole pass in one launch (ba_attention_fwd_qkv16; short heads only)."""
+        self.ba.ba_attention_fwd_qkv16(self.q, self.k, self.v, self.bias, self.out, self.stream)
+
     def attn_online(self):
         self.ba.ba_attention_fwd_online(self.qbits, self.qmu, self.kbits, self.kmu, self.vq, self.vscale,
                                         self.bias, self.out, self.stream)
@@ -300,6 +306,17 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmu
         device_warmup(w.step_q16, min(device_warmup_s, 0.1))
         q16 = {"step_ms": sorted(w.time(w.step_q16, iters=steps, warmup=warmup) for _ in range(3))[1],
                "attn_ms": sorted(w.time(w.attn_q16, iters=max(steps, 20), warmup=3) for _ in range(3))[1]}
+    # the whole pass in one launch where it applies (heads of at most 256 tokens)
+    qkv16_ms = None
+    if with_q16 and form == "two-step":
+        try:
+            w.step_qkv16()
+        except w.ba.BinAttnError as e:
+            if e.status != w.ba.BA_ERR_UNSUPPORTED:
+                raise
+        else:
+            device_warmup(w.step_qkv16, min(device_warmup_s, 0.1))
+            qkv16_ms = sorted(w.time(w.step_qkv16, iters=steps, warmup=warmup) for _ in range(3))[1]
     attn_cold_ms = w.time_cold(attn_fn) if cold else None
     # the one-pass (running maximum) form beside it, d <= 64
     online_ms = None
@@ -311,7 +328,7 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmu
         "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
         "device_warmup": {"seconds": device_warmup_s, "steps": dev_warm},
         "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms, "online_ms": online_ms,
-        "q16": q16, "pre_ms": pre_ms,
+        "q16": q16, "pre_ms": pre_ms, "qkv16_ms": qkv16_ms,
         "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
         "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
@@ -500,6 +517,11 @@ def main() -> int:
                 "value": round(r["ops"] / (q["step_ms"] * 1e-3) / 1e12, 3),
                 "note": "step = ba_pack_k_quant_v + ba_attention_fwd_q16 (Q binarised inside the attention; "
                         "the same output bit for bit); mean of back-to-back steps, median of 3 runs"}
+        if r["qkv16_ms"] is not None:
+            line["qkv_in_one_launch"] = {
+                "ms_per_step": round(r["qkv16_ms"], 5), "value": round(r["ops"] / (r["qkv16_ms"] * 1e-3) / 1e12, 3),
+                "note": "step = ba_attention_fwd_qkv16 alone (Q, K binarised and V quantised inside the "
+                        "attention; heads of at most 256 tokens; the same output bit for bit)"}
         if not args.all and args.secondary:
             r2 = measure(args.secondary, args.steps, args.warmup, device_warmup_s=args.device_warmup,
                          with_q16=not args.no_q16, form=args.form)
