@@ -264,7 +264,9 @@ def test_quant_v_launch_shapes(B, H, N, d, dt):
 # select each V path: heads in registers, heads in two to four parts, the
 # split quantiser with the zero fill in the packing launch
 @pytest.mark.parametrize("B,H,N,d", [(2, 3, 1130, 72), (2, 3, 1600, 72), (1, 3, 5120, 64), (3, 5, 2261, 72),
-                                     (1, 1, 5121, 64), (1, 2, 2560, 128), (2, 16, 4096, 64)])
+                                     (1, 1, 5121, 64), (1, 2, 2560, 128), (2, 16, 4096, 64),
+                                     # heads one block holds, in two parts (fewer heads than CUs)
+                                     (1, 16, 1024, 72), (2, 8, 700, 64), (1, 3, 566, 72), (1, 2, 565, 72)])
 @pytest.mark.parametrize("dt", [F16, BF16])
 def test_prepass_launch_shapes(B, H, N, d, dt):
     rng = np.random.default_rng(B * 7919 + H * 101 + N * 7 + d + dt)
