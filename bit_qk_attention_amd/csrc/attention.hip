@@ -1240,15 +1240,7 @@ __global__ __launch_bounds__(256, (min_blocks<NCB, BIAS, MODE>())) void attn_fwd
 #pragma unroll
       for (int e = 0; e < 8; ++e) inv[e] = vscl[8 * piece + e];
       auto quant8 = [&](const u4v& raw, int j) __attribute__((always_inline)) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
-          y = fminf(fmaxf(y, -127.0f), 127.0f);
-          const uint32_t bq = (uint32_t)(uint8_t)(int8_t)(int)y;
-          if (e < 4) lo |= bq << (8 * e); else hi |= bq << (8 * (e - 4));
-        }
-        *reinterpret_cast<uint2*>(vsr[j >> 6].vr + vaddr(j & 63, 8 * piece)) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(vsr[j >> 6].vr + vaddr(j & 63, 8 * piece)) = quant8_codes<DT>(raw, inv);
       };
       int j = r0;
       for (; j + 3 * R < N; j += 4 * R) {

@@ -51,6 +51,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// ---- channel-wise int8 V ---------------------------------------------------
+
+// The int8 codes clamp(rne(x * inv), -127, 127) of 8 values (16-bit
+// patterns in 4 dwords, channel e with its inv[e] = 127 / amax_e in float32,
+// or 0), as two dwords of bytes. The product is rounded to float32, then
+// 1.5 * 2^23 is added: that sum has a unit spacing of 1, so it is the
+// product rounded once to an integer (ties to even, as rintf) plus 1.5 * 2^23,
+// and its bit pattern is 0x4B400000 + that integer, whose low byte is the
+// integer's two's-complement code. For |x| <= amax, |x * inv| <= 127 (1 +
+// 2^-24)^2 < 127.5, so the integer lies in [-127, 127] and the clamp never
+// acts. Contraction into a fused multiply-add is off (it would round the
+// exact product and the sum once, not the product first).
+template <int DT>
+__device__ __forceinline__ uint2 quant8_codes(const u4v& raw, const float* inv) {
+#pragma clang fp contract(off)
+  uint32_t u[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e];
+    u[e] = __float_as_uint(t + 12582912.0f);
+  }
+  const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u) | __builtin_amdgcn_perm(u[3], u[2], 0x04000c0cu);
+  const uint32_t hi = __builtin_amdgcn_perm(u[5], u[4], 0x0c0c0400u) | __builtin_amdgcn_perm(u[7], u[6], 0x04000c0cu);
+  return make_uint2(lo, hi);
+}
+
 // ---- launchers (host side; arguments already validated) -------------------
 
 // Element strides of a [B, H, N, d] view of 16-bit Q, K or V with contiguous

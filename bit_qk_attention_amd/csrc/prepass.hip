@@ -309,17 +309,7 @@ __device__ __forceinline__ void quant_heads_block(const uint16_t* __restrict__ v
   int8_t* dst = qh + (int64_t)r0 * d;
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k, dst += (int64_t)R * d) {
-    if (k < cnt) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y = __builtin_rintf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16))) * inv[e]);
-        y = fminf(fmaxf(y, -127.0f), 127.0f);
-        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
-        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
-      }
-      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-    }
+    if (k < cnt) *reinterpret_cast<uint2*>(dst) = quant8_codes<DT>(x[k], inv);
   }
 }
 
@@ -399,17 +389,7 @@ __device__ __forceinline__ void quant_head_part_block(const uint16_t* __restrict
   int8_t* dst = vq + bh * N * d + 8 * piece + (int64_t)(r_begin + r0) * d;
 #pragma unroll
   for (int k = 0; k < kQvRows; ++k, dst += (int64_t)R * d) {
-    if (k < cnt) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y = __builtin_rintf(to_f32<DT>((uint16_t)(x[k][e >> 1] >> ((e & 1) * 16))) * inv[e]);
-        y = fminf(fmaxf(y, -127.0f), 127.0f);
-        const uint32_t bq = (uint32_t)(uint8_t)(int8_t)(int)y;
-        if (e < 4) lo |= bq << (8 * e); else hi |= bq << (8 * (e - 4));
-      }
-      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-    }
+    if (k < cnt) *reinterpret_cast<uint2*>(dst) = quant8_codes<DT>(x[k], inv);
   }
 }
 
@@ -579,17 +559,7 @@ __global__ __launch_bounds__(256) void quant_v_split_kernel(
     float inv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) inv[e] = inv_s[8 * piece + e];
-    auto quant8 = [&](const u4v& raw) -> uint2 {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y = __builtin_rintf(to_f32<DT>((uint16_t)(raw[e >> 1] >> ((e & 1) * 16))) * inv[e]);
-        y = fminf(fmaxf(y, -127.0f), 127.0f);
-        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)y;
-        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
-      }
-      return make_uint2(lo, hi);
-    };
+    auto quant8 = [&](const u4v& raw) -> uint2 { return quant8_codes<DT>(raw, inv); };
     int8_t* qh = vq + bh * N * d + 8 * piece;
     if (active) {
       int j = r_begin + r0;
