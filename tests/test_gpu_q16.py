@@ -108,6 +108,18 @@ def test_q16_special_values():
         assert_same(out, run.out, dt)
 
 
+def test_q16_longest_head_and_per_batch_bias():
+    """The token limit (65536 keys, the query blocks' last rows) and a dense
+    bias given per batch element: still the two-step path's bits."""
+    run = DeviceRun(synth(1, 1, 65536, 64, BF16, 12))
+    _, out = q16_run(run)
+    assert_same(out, run.out, "N=65536")
+    run = DeviceRun(generate(replace(WORKLOADS["dit_512"], name="q16_pb", B=3, H=2, N=264, bias_shared=False)))
+    assert run.inp.bias_batch_stride == 2 * 264 * 264
+    _, out = q16_run(run)
+    assert_same(out, run.out, "per-batch bias")
+
+
 FULL = ["deit_tiny", "deit_small", "dit_256", "dit_512", "long_4k", "long_4k_rp", "long_16k", "long_16k_rp"]
 
 
