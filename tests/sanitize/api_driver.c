@@ -89,6 +89,7 @@ int main(void) {
   ba_bias rp_bad = {BA_BIAS_RELPOS, A(7), BA_F32, 0, 31, 32, 0};
   ba_bias rp_wide = {BA_BIAS_RELPOS, A(7), BA_F32, 0, 4, 257, 0};
   ba_bias kind_bad = {(ba_bias_kind)9, A(7), BA_F32, 0, 0, 0, 0};
+  ba_bias rp_small = {BA_BIAS_RELPOS, A(7), BA_F32, 0, 14, 14, 1};
   expect("attn no bias", attn(NULL, 1024, A(9), bf), BA_OK, 1);
   expect("attn kind none", attn(&none, 1024, A(9), bf), BA_OK, 1);
   expect("attn dense f16", attn(&dense16, 1024, A(9), bf), BA_OK, 1);
@@ -110,6 +111,34 @@ int main(void) {
   expect("attn strided alias", ba_attention_fwd_strided(P(uint32_t, 1), P(float, 2), P(uint32_t, 3), P(float, 4),
                                                         P(int8_t, 5), P(float, 6), NULL, 8, 16, 1024, 72, A(9),
                                                         &alias, bf, NULL), BA_ERR_INVALID_ARG, 0);
+  /* the fused forms */
+  expect("pack k/v ok", ba_pack_k_quant_v(A(1), A(2), bf, 8, 16, 1024, 72, P(uint32_t, 5), P(float, 6), P(int8_t, 7),
+                                          P(float, 8), NULL), BA_OK, 1);
+  expect("pack k/v overlap", ba_pack_k_quant_v(A(1), A(2), bf, 8, 16, 1024, 72, P(uint32_t, 5), P(float, 6),
+                                               P(int8_t, 5), P(float, 8), NULL), BA_ERR_INVALID_ARG, 0);
+  expect("attn q16 ok", ba_attention_fwd_q16(A(0), bf, P(uint32_t, 3), P(float, 4), P(int8_t, 5), P(float, 6),
+                                             &dense16, 8, 16, 1024, 72, A(9), bf, NULL), BA_OK, 1);
+  expect("attn q16 d=20", ba_attention_fwd_q16(A(0), bf, P(uint32_t, 3), P(float, 4), P(int8_t, 5), P(float, 6),
+                                               NULL, 8, 16, 1024, 20, A(9), bf, NULL), BA_ERR_UNSUPPORTED, 0);
+  expect("attn q16 out aliases q", ba_attention_fwd_q16(A(0), bf, P(uint32_t, 3), P(float, 4), P(int8_t, 5),
+                                                        P(float, 6), NULL, 8, 16, 1024, 72, A(0), bf, NULL),
+         BA_ERR_INVALID_ARG, 0);
+  expect("attn qkv16 ok", ba_attention_fwd_qkv16(A(0), A(1), A(2), bf, &rp_small, 64, 6, 197, 64, A(9), BA_F16, NULL),
+         BA_OK, 1);
+  /* (refused by the launcher, before any launch: the stub is consulted once) */
+  {
+    const int before = ba_stub_calls;
+    const ba_status st = ba_attention_fwd_qkv16(A(0), A(1), A(2), bf, NULL, 8, 16, 1024, 72, A(9), bf, NULL);
+    if (st != BA_ERR_UNSUPPORTED || ba_stub_calls - before != 1) {
+      printf("FAIL attn qkv16 long: status %d\n", (int)st);
+      ++fails;
+    }
+    expect("(resync)", BA_OK, BA_OK, 1);
+  }
+  expect("attn qkv16 out aliases v", ba_attention_fwd_qkv16(A(0), A(1), A(2), bf, NULL, 8, 16, 256, 72, A(2), bf,
+                                                            NULL), BA_ERR_INVALID_ARG, 0);
+  expect("attn qkv16 no v", ba_attention_fwd_qkv16(A(0), A(1), NULL, bf, NULL, 8, 16, 256, 72, A(9), bf, NULL),
+         BA_ERR_INVALID_ARG, 0);
   /* the similarity window */
   expect("hamming ok", ba_debug_hamming_scores(P(uint32_t, 0), P(uint32_t, 1), 2, 16, 4096, 64, 3, 5, 100, 200,
                                                P(int32_t, 2), NULL), BA_OK, 1);

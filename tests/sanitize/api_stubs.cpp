@@ -39,8 +39,13 @@ hipError_t launch_hamming(const uint32_t*, const uint32_t*, int, int, int, int, 
 }
 hipError_t launch_attention(const AttnArgs& a, hipStream_t) {
   ++ba_stub_calls;
+  // 16-bit K and V outside the resident mode (the real launcher refuses
+  // them before any launch)
+  if (a.k16 && a.N > 256) return hipErrorNotSupported;
   // the descriptor validation hands over is consistent with the call
-  return (a.B > 0 && a.H > 0 && a.N > 0 && a.d > 0 && a.out) ? hipSuccess : hipErrorInvalidValue;
+  const bool q_ok = a.q16 ? (a.qbits == nullptr && a.qmu == nullptr) : (a.qbits && a.qmu);
+  const bool kv_ok = a.k16 ? (a.v16 && !a.kbits && !a.kmu && !a.vq && !a.vscale) : (a.kbits && a.kmu && a.vq && a.vscale);
+  return (a.B > 0 && a.H > 0 && a.N > 0 && a.d > 0 && a.out && q_ok && kv_ok) ? hipSuccess : hipErrorInvalidValue;
 }
 
 }  // namespace binattn
