@@ -45,6 +45,11 @@
 //  * A sigma mode of the same kernel writes the integer similarity that its
 //    Q.K path produces (the staged-tile route, the raw-word route and the
 //    pass-1 route straight from global memory), for inspection.
+//  * The queries may come as 16-bit values, binarised in the prologue with
+//    the packing kernels' arithmetic (each query row belongs to one
+//    workgroup); for heads whose keys all stay on chip, the keys and values
+//    too (the resident mode binarises and quantises them into its stages).
+//    The outputs are those of the packed-input path bit for bit.
 #include <algorithm>
 #include <type_traits>
 

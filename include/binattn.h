@@ -217,11 +217,10 @@ ba_status ba_attention_fwd_strided(const uint32_t* qbits, const float* qmu,
 
 /* Extension: the path with Q packed inside the attention (zh technical
  * summary section 2.3: the steps fused into one kernel; section 2.2 item 1
- * for the packing itself). Each query row is
- * read once, by the workgroup that owns it, so binarising it in the
- * attention's prologue repeats no work; K and V rows are read by every
- * query block of their head, so they are still packed and quantised first,
- * by ba_pack_k_quant_v.
+ * for the packing itself). Each query row is read once, by the workgroup
+ * that owns it, so binarising it in the attention's prologue repeats no
+ * work; K and V rows are read by every query block of their head, so they
+ * are still packed and quantised first, by ba_pack_k_quant_v.
  *
  * ba_pack_k_quant_v: the K and V half of ba_pack_qk_quant_v (kbits, kmu,
  * vq, vscale bit for bit as that call writes them; same layouts, alignment
@@ -256,9 +255,9 @@ ba_status ba_attention_fwd_q16(const void* q, ba_dtype q_dt,
  * stay on chip at once: N <= 256, d % 8 == 0 and d <= 96, and no bias, a
  * relative-position table, or a dense fp32 bias with 16-byte rows (N % 4 ==
  * 0, batch stride % 4 == 0, 16-byte aligned); BA_ERR_UNSUPPORTED otherwise,
- * with nothing enqueued. Each head's K and V are read by each of its (at most two) query
- * blocks. Other arguments, layouts and errors as ba_attention_fwd; out must
- * not overlap q, k or v. */
+ * with nothing enqueued. Each head's K and V are read by each of its (at
+ * most two) query blocks. Other arguments, layouts and errors as
+ * ba_attention_fwd; out must not overlap q, k or v. */
 ba_status ba_attention_fwd_qkv16(const void* q, const void* k, const void* v, ba_dtype dt,
                                  const ba_bias* bias, int B, int H, int N, int d,
                                  void* out, ba_dtype out_dt, void* stream);
