@@ -3,13 +3,14 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all | --block]
 
 One step = the whole hot path over one batch of synthetic input already
-resident in HBM: ba_pack_qk_quant_v (sign bits + scales of Q and K and
-channel-wise int8 V, one call: the outputs of ba_pack_qk and ba_quant_v) and
-ba_attention_fwd (fused attention), on one stream. The same pass with Q
-binarised inside the attention (ba_pack_k_quant_v + ba_attention_fwd_q16, the
-same output bit for bit) is timed beside it under "q_in_prologue", and for
-heads of at most 256 tokens the whole pass in one launch
-(ba_attention_fwd_qkv16) under "qkv_in_one_launch".
+resident in HBM, on one stream. By default (--form q16, for d % 8 == 0) it is
+ba_pack_k_quant_v (sign bits + scales of K, channel-wise int8 V) and
+ba_attention_fwd_q16 (the fused attention, binarising Q in its prologue);
+--form two-step, and any d % 8 != 0, time ba_pack_qk_quant_v (Q and K packed,
+V quantised: the outputs of ba_pack_qk and ba_quant_v) and ba_attention_fwd.
+Both forms give the same output bit for bit; the other one is timed beside
+the step under "other_form", and for heads of at most 256 tokens the whole
+pass in one launch (ba_attention_fwd_qkv16) under "qkv_in_one_launch".
 The headline value is effective attention throughput 4*B*H*N^2*d / t_step
 (d the real head dim), for the DiT-XL/2 512px layer (B=8, H=16, N=1024,
 d=72, dense fp16 bias shared over the batch); the same figures for the
@@ -68,14 +69,15 @@ def kernel_sha() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(s) -> int:
-    """HBM bytes one attention launch must move at minimum: packed Q and K
-    (bits + scale), int8 V + channel scales, the output, and the bias (a
-    shared dense bias once, not per batch element; a relative-position
-    table)."""
+def algorithmic_bytes(s, form: str = "two-step") -> int:
+    """HBM bytes one attention launch must move at minimum: packed Q (16-bit
+    Q for the q16 form) and packed K (bits + scale), int8 V + channel scales,
+    the output, and the bias (a shared dense bias once, not per batch
+    element; a relative-position table)."""
     W = (s.d + 31) // 32
     BH, N, d = s.B * s.H, s.N, s.d
-    nb = 2 * BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d + 2 * BH * N * d
+    q_bytes = 2 * BH * N * d if form == "q16" else BH * N * (4 * W + 4)
+    nb = q_bytes + BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d + 2 * BH * N * d
     if s.bias.startswith("dense"):
         esz = 4 if s.bias == "dense_f32" else 2
         nb += (1 if s.bias_shared else s.B) * s.H * N * N * esz
@@ -94,10 +96,10 @@ def prepass_bytes(s) -> int:
     return 3 * 2 * BH * N * d + 2 * BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d
 
 
-def traffic_for(name: str):
-    """Measured HBM bytes per attention launch, if the counters were taken
-    on the current kernel source."""
-    path = os.path.join(PROFILE_DIR, f"attn_fwd_{name}_traffic.json")
+def traffic_for(name: str, form: str = "two-step"):
+    """Measured HBM bytes per attention launch of the form, if the counters
+    were taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"attn_fwd_{'q16_' if form == 'q16' else ''}{name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -267,15 +269,22 @@ def device_warmup(fn, seconds: float) -> int:
     return n
 
 
+def step_form(s, form: str) -> str:
+    """The form timed for a workload: q16 needs d % 8 == 0."""
+    return "q16" if form == "q16" and s.d % 8 == 0 else "two-step"
+
+
 def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmup_s: float = 0.3,
-            with_q16: bool = True, form: str = "two-step") -> dict:
-    """form: "two-step" (ba_pack_qk_quant_v + ba_attention_fwd) or "q16"
-    (ba_pack_k_quant_v + ba_attention_fwd_q16) is the step timed."""
+            alt: bool = True, form: str = "q16") -> dict:
+    """form: "q16" (ba_pack_k_quant_v + ba_attention_fwd_q16, where d % 8 ==
+    0) or "two-step" (ba_pack_qk_quant_v + ba_attention_fwd) is the step
+    timed; alt: also time the other form and the one-launch pass."""
     import workloads
     torch = __import__("torch")
     w = Workload(name)
     s = w.spec
     ops = workloads.eff_ops(s)
+    form = step_form(s, form)
     step_fn, attn_fn = (w.step, w.attn) if form == "two-step" else (w.step_q16, w.attn_q16)
     dev_warm = device_warmup(step_fn, device_warmup_s)
     # whole step, bracketed by synchronisation on both sides
@@ -299,16 +308,18 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmu
     # the pre-pass alone (HBM-bound), same protocol
     pre_fn = w.prepass if form == "two-step" else w.prepass_kv
     pre_ms = sorted(w.time(pre_fn, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
-    # the step with Q packed in the attention's prologue (d % 8 == 0), same
-    # protocol, right after the step's own runs (before the cold-cache launches)
-    q16 = None
-    if with_q16 and form == "two-step" and s.d % 8 == 0:
-        device_warmup(w.step_q16, min(device_warmup_s, 0.1))
-        q16 = {"step_ms": sorted(w.time(w.step_q16, iters=steps, warmup=warmup) for _ in range(3))[1],
-               "attn_ms": sorted(w.time(w.attn_q16, iters=max(steps, 20), warmup=3) for _ in range(3))[1]}
+    # the other form of the step (where both apply), same protocol, right
+    # after the step's own runs (before the cold-cache launches)
+    other = None
+    if alt and s.d % 8 == 0:
+        o_step, o_attn = (w.step_q16, w.attn_q16) if form == "two-step" else (w.step, w.attn)
+        device_warmup(o_step, min(device_warmup_s, 0.1))
+        other = {"form": "q16" if form == "two-step" else "two-step",
+                 "step_ms": sorted(w.time(o_step, iters=steps, warmup=warmup) for _ in range(3))[1],
+                 "attn_ms": sorted(w.time(o_attn, iters=max(steps, 20), warmup=3) for _ in range(3))[1]}
     # the whole pass in one launch where it applies (heads of at most 256 tokens)
     qkv16_ms = None
-    if with_q16 and form == "two-step":
+    if alt:
         try:
             w.step_qkv16()
         except w.ba.BinAttnError as e:
@@ -321,14 +332,16 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmu
     # the one-pass (running maximum) form beside it, d <= 64
     online_ms = None
     if s.d <= 64:
+        if form == "q16":
+            w.prepass()  # (the packed queries the one-pass form reads)
         online_ms = sorted(w.time(w.attn_online, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
     step_fn()  # leave the step's output in place
-    nbytes = algorithmic_bytes(s)
+    nbytes = algorithmic_bytes(s, form)
     return {
-        "name": name, "spec": s, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
+        "name": name, "spec": s, "form": form, "ops": ops, "step_ms": step_ms, "wall_ms": wall_ms,
         "device_warmup": {"seconds": device_warmup_s, "steps": dev_warm},
         "attn_ms": attn_ms, "attn_min_ms": runs[0], "attn_cold_ms": attn_cold_ms, "online_ms": online_ms,
-        "q16": q16, "pre_ms": pre_ms, "qkv16_ms": qkv16_ms,
+        "other": other, "pre_ms": pre_ms, "qkv16_ms": qkv16_ms,
         "tops": ops / (step_ms * 1e-3) / 1e12,
         "attn_tops": ops / (attn_ms * 1e-3) / 1e12,
         "attn_gbs": nbytes / (attn_ms * 1e-3) / 1e9, "alg_bytes": nbytes, "inp": w.inp,
@@ -421,12 +434,13 @@ def main() -> int:
     ap.add_argument("--device-warmup", type=float, default=0.3, metavar="SECONDS",
                     help="wall time of back-to-back steps run before the W warm-up steps, so the timed "
                          "steps run at the clock the GPU holds under sustained load (0 to skip)")
-    ap.add_argument("--form", choices=["two-step", "q16"], default="two-step",
-                    help="the step timed: two-step (ba_pack_qk_quant_v + ba_attention_fwd, the default) or "
-                         "q16 (ba_pack_k_quant_v + ba_attention_fwd_q16: Q binarised inside the attention)")
-    ap.add_argument("--no-q16", action="store_true",
-                    help="do not time the step with Q packed inside the attention (its attention launches share "
-                         "the kernel name of the two-step form's in a profile)")
+    ap.add_argument("--form", choices=["q16", "two-step"], default="q16",
+                    help="the step timed: q16 (ba_pack_k_quant_v + ba_attention_fwd_q16: Q binarised inside the "
+                         "attention; the default, where d %% 8 == 0) or two-step (ba_pack_qk_quant_v + "
+                         "ba_attention_fwd)")
+    ap.add_argument("--no-alt", action="store_true",
+                    help="do not time the other form or the one-launch pass beside the step (the two forms' "
+                         "attention launches share one kernel name in a profile)")
     ap.add_argument("--block", action="store_true",
                     help="only the attention block (QKV projection, BinaryAttention, output "
                          "projection) at B=2, N=4096, 16 heads of 64, synthetic bf16 weights")
@@ -469,7 +483,7 @@ def main() -> int:
     names = list(workloads.WORKLOADS) if args.all else [args.workload]
     for name in names:
         r = measure(name, args.steps, args.warmup, cold=not args.all, device_warmup_s=args.device_warmup,
-                    with_q16=not args.no_q16, form=args.form)
+                    alt=not args.no_alt, form=args.form)
         s = r["spec"]
         line = {
             "metric": "effective attention TOPS (4*B*H*N^2*d / t_step), step = pack Q/K + quantise V + fused attention",
@@ -480,26 +494,28 @@ def main() -> int:
             "dtype_detail": "Q.K: +-1 signs on fp4 MFMA (exact integer sums); softmax fp32; P.V u8 x int8 -> int32 MFMA",
             "data": "synthetic (seeded N(0,1) activations of the workload's shape)",
             "config": config_of(s),
-            "step_form": args.form,
+            "step_form": r["form"],
             "device_warmup": r["device_warmup"],
             "attn_ms": round(r["attn_ms"], 5), "attn_min_ms": round(r["attn_min_ms"], 5),
             "attn_tops": round(r["attn_tops"], 3),
             "roofline": {
                 "bound": "alu", "achieved": round(r["valu_tops"], 3), "peak": round(VALU_PEAK_TLANEOPS, 2),
                 "unit": "T lane-ops/s", "frac": round(r["valu_tops"] / VALU_PEAK_TLANEOPS, 4),
-                "traffic": traffic_for(name),
-                "kernel": "attn_fwd_kernel", "scores_per_launch": r["scores"],
+                "traffic": traffic_for(name, r["form"]),
+                "kernel": "attn_fwd_kernel (ba_attention_fwd_q16)" if r["form"] == "q16"
+                          else "attn_fwd_kernel (ba_attention_fwd)",
+                "scores_per_launch": r["scores"],
                 "lane_ops_per_score": valu_ops_per_score(s),
                 "note": "vector-ALU bound: B*H*N^2 scores x the minimum issue slots per score / launch time "
                         "(HIP events on the launch stream; median of 5 runs of back-to-back launches); peak "
-                        "256 CUs x 64 lanes x 2.4 GHz",
+                        "256 CUs x 64 lanes x 2.4 GHz; the q16 form's query packing is not counted as work",
             },
             "int8_mfma": {"achieved": round(r["attn_tops"], 3), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                           "frac": round(r["attn_tops"] / INT8_PEAK_TOPS, 4),
                           "note": "effective ops 4*B*H*N^2*d per launch / launch time"},
             "hbm": {"alg_bytes_per_launch": r["alg_bytes"], "achieved_GBs": round(r["attn_gbs"], 1),
                     "peak_GBs": HBM_PEAK_GBS, "frac": round(r["attn_gbs"] / HBM_PEAK_GBS, 4)},
-            "prepass": prepass_line(r, args.form),
+            "prepass": prepass_line(r, r["form"]),
         }
         if r["attn_cold_ms"] is not None:
             c = r["attn_cold_ms"]
@@ -510,13 +526,14 @@ def main() -> int:
             line["attn_online"] = {"ms": round(r["online_ms"], 5), "vs_two_pass": round(r["online_ms"] / r["attn_ms"], 3),
                                    "note": "ba_attention_fwd_online: one pass over the keys with a running "
                                            "row maximum (same timing protocol)"}
-        if r["q16"] is not None:
-            q = r["q16"]
-            line["q_in_prologue"] = {
-                "ms_per_step": round(q["step_ms"], 5), "attn_ms": round(q["attn_ms"], 5),
-                "value": round(r["ops"] / (q["step_ms"] * 1e-3) / 1e12, 3),
-                "note": "step = ba_pack_k_quant_v + ba_attention_fwd_q16 (Q binarised inside the attention; "
-                        "the same output bit for bit); mean of back-to-back steps, median of 3 runs"}
+        if r["other"] is not None:
+            o = r["other"]
+            line["other_form"] = {
+                "form": o["form"], "ms_per_step": round(o["step_ms"], 5), "attn_ms": round(o["attn_ms"], 5),
+                "value": round(r["ops"] / (o["step_ms"] * 1e-3) / 1e12, 3),
+                "note": ("ba_pack_qk_quant_v + ba_attention_fwd" if o["form"] == "two-step" else
+                         "ba_pack_k_quant_v + ba_attention_fwd_q16") +
+                        " (the same output bit for bit); mean of back-to-back steps, median of 3 runs"}
         if r["qkv16_ms"] is not None:
             line["qkv_in_one_launch"] = {
                 "ms_per_step": round(r["qkv16_ms"], 5), "value": round(r["ops"] / (r["qkv16_ms"] * 1e-3) / 1e12, 3),
@@ -524,12 +541,13 @@ def main() -> int:
                         "attention; heads of at most 256 tokens; the same output bit for bit)"}
         if not args.all and args.secondary:
             r2 = measure(args.secondary, args.steps, args.warmup, device_warmup_s=args.device_warmup,
-                         with_q16=not args.no_q16, form=args.form)
-            line["secondary"] = {"config": config_of(r2["spec"]), "value": round(r2["tops"], 3),
+                         alt=not args.no_alt, form=args.form)
+            line["secondary"] = {"config": config_of(r2["spec"]), "step_form": r2["form"],
+                                 "value": round(r2["tops"], 3),
                                  "ms_per_step": round(r2["step_ms"], 5), "attn_ms": round(r2["attn_ms"], 5),
                                  "attn_online_ms": None if r2["online_ms"] is None else round(r2["online_ms"], 5),
-                                 "q_in_prologue_ms_per_step": None if r2["q16"] is None
-                                 else round(r2["q16"]["step_ms"], 5),
+                                 "other_form_ms_per_step": None if r2["other"] is None
+                                 else round(r2["other"]["step_ms"], 5),
                                  "attn_tops": round(r2["attn_tops"], 3),
                                  "frac_int8_peak": round(r2["attn_tops"] / INT8_PEAK_TOPS, 4),
                                  "frac_valu_peak": round(r2["valu_tops"] / VALU_PEAK_TLANEOPS, 4)}
