@@ -254,8 +254,11 @@ ba_status ba_attention_fwd_q16(const void* q, ba_dtype q_dt,
  * packed or quantised array is written. It applies where a head's keys all
  * stay on chip at once: N <= 256, d % 8 == 0 and d <= 96, and no bias, a
  * relative-position table, or a dense fp32 bias with 16-byte rows (N % 4 ==
- * 0, batch stride % 4 == 0, 16-byte aligned); BA_ERR_UNSUPPORTED otherwise,
- * with nothing enqueued. Each head's K and V are read by each of its (at
+ * 0, batch stride % 4 == 0, 16-byte aligned); except a relative-position
+ * table over grid rows that are multiples of 16 tokens wide with no leading
+ * tokens at 33..64 channels (that kernel runs four workgroups per CU and
+ * has no room for a whole head); BA_ERR_UNSUPPORTED otherwise, with nothing
+ * enqueued. Each head's K and V are read by each of its (at
  * most two) query blocks. Other arguments, layouts and errors as
  * ba_attention_fwd; out must not overlap q, k or v. */
 ba_status ba_attention_fwd_qkv16(const void* q, const void* k, const void* v, ba_dtype dt,

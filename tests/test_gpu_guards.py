@@ -25,9 +25,11 @@ CASES = [
     # name, B, H, N, d, dtype, bias kind (workload-style), n_prefix/grid for relpos
     ("dense_f32_ragged", 1, 3, 197, 64, workloads.F16, "dense_f32"),
     ("dense_f16_odd_rows", 2, 3, 129, 72, workloads.BF16, "dense_f16"),
-    ("long_head_split_quantiser", 1, 2, 2000, 64, workloads.BF16, "none"),
+    ("long_head_split_quantiser", 1, 2, 6000, 64, workloads.BF16, "none"),
     ("element_paths_d20", 2, 2, 77, 20, workloads.BF16, "none"),
     ("resident_d72", 1, 2, 256, 72, workloads.BF16, "none"),
+    ("resident_relpos_d64", 2, 3, 197, 64, workloads.F16, "relpos"),
+    ("long_head_parts", 1, 2, 4096, 64, workloads.BF16, "none"),
     ("d100_relpos", 1, 2, 197, 100, workloads.F16, "relpos"),
 ]
 
@@ -95,6 +97,34 @@ def test_outputs_stop_at_their_end(name, B, H, N, d, dt, bias):
         torch.cuda.synchronize()
         assert tail_intact(buf, n), f"{fn.__name__}: output written past its end"
         if fn is ba.ba_attention_fwd:
+            assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+
+    # the fused forms: K/V pre-pass, attention binarising Q, and (short
+    # heads) the whole pass in one launch
+    if d % 8 == 0:
+        g3 = fresh()
+        ba.ba_pack_k_quant_v(k, v, *(g3[key][0] for key in ("kbits", "kmu", "vq", "vscale")))
+        out, buf, n = guarded(tuple(q.shape), q.dtype)
+        ba.ba_attention_fwd_q16(q, *(g3[key][0] for key in ("kbits", "kmu", "vq", "vscale")), lib_bias, out)
+        torch.cuda.synchronize()
+        for key, r in zip(("kbits", "kmu", "vq", "vscale"), ref[2:]):
+            t, gbuf, gn = g3[key]
+            assert tail_intact(gbuf, gn), f"{key} (K/V pre-pass) written past its end"
+            assert torch.equal(t, r), key
+        for key in ("qbits", "qmu"):
+            assert bool((g3[key][1] == FILL).all()), f"{key} touched by the K/V pre-pass"
+        assert tail_intact(buf, n), "ba_attention_fwd_q16: output written past its end"
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        out, buf, n = guarded(tuple(q.shape), q.dtype)
+        try:
+            ba.ba_attention_fwd_qkv16(q, k, v, lib_bias, out)
+        except ba.BinAttnError as e:
+            assert e.status == ba.BA_ERR_UNSUPPORTED
+            torch.cuda.synchronize()
+            assert bool((buf == FILL).all()), "a refused one-launch call wrote"
+        else:
+            torch.cuda.synchronize()
+            assert tail_intact(buf, n), "ba_attention_fwd_qkv16: output written past its end"
             assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
 
     # a window of the similarity

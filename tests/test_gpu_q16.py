@@ -8,6 +8,7 @@ the reduced workloads are also checked against the oracle directly.
 """
 from dataclasses import replace
 
+import numpy as np
 import pytest
 import torch
 
@@ -152,3 +153,27 @@ def test_q16_rejects():
     with pytest.raises(ba.BinAttnError) as e:
         ba.ba_attention_fwd_q16(qmis, kbits, kmu, vq, vscale, None, torch.empty_like(run.out))
     assert e.value.status == ba.BA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_q16_random_shapes(seed):
+    """Seeded random shapes, dtypes and biases: the q16 path's output equals
+    the two-step path's bit for bit, and a second call gives the same bits."""
+    rng = np.random.default_rng(4242 + seed)
+    d = int(rng.choice([8, 16, 24, 32, 40, 48, 56, 64, 72, 80, 88, 96, 104, 112, 120, 128]))
+    N = int(rng.integers(1, 1500))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    dt = BF16 if rng.random() < 0.5 else F16
+    kind = ["none", "dense_f32", "dense_f16", "relpos"][int(rng.integers(0, 4))]
+    kw = {}
+    if kind.startswith("dense"):
+        kw = dict(bias=kind)
+    elif kind == "relpos":
+        grid, npre = relpos_grid(N)
+        kw = dict(bias="relpos", grid=grid, n_prefix=npre)
+    print(f"q16 random {seed}: B={B} H={H} N={N} d={d} dt={dt} bias={kind}", flush=True)
+    run = DeviceRun(synth(B, H, N, d, dt, 100 + seed, **kw))
+    _, out = q16_run(run)
+    assert_same(out, run.out, (seed, B, H, N, d, kind))
+    _, out2 = q16_run(run)
+    assert_same(out2, out, "repeat")

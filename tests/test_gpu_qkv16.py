@@ -113,11 +113,14 @@ def test_qkv16_special_values():
 
 @pytest.mark.parametrize("shape,bias", [((1, 1, 257, 64), "none"), ((1, 1, 128, 128), "none"),
                                          ((1, 1, 128, 20), "none"), ((1, 2, 128, 72), "dense_f16"),
-                                         ((1, 2, 197, 64), "dense_f32")])
+                                         ((1, 2, 197, 64), "dense_f32"), ((1, 2, 144, 40), "relpos_rows")])
 def test_qkv16_unsupported(shape, bias):
     """Outside the resident mode the call refuses and enqueues nothing."""
     B, H, N, d = shape
-    run = DeviceRun(synth(B, H, N, d, BF16, 5, bias=bias))
+    kw = dict(bias=bias)
+    if bias == "relpos_rows":  # grid rows of 16 keys, no leading token, 33..64 channels
+        kw = dict(bias="relpos", grid=(N // 16, 16), n_prefix=0)
+    run = DeviceRun(synth(B, H, N, d, BF16, 5, **kw))
     out = torch.full_like(run.out, 7.0)
     with pytest.raises(ba.BinAttnError) as e:
         ba.ba_attention_fwd_qkv16(run.q, run.k, run.v, run.lib_bias, out)
@@ -138,3 +141,34 @@ def test_qkv16_rejects_bad_pointers():
         ba.ba_attention_fwd_qkv16(run.q, run.k, vmis, None, out)      # V not 16-byte aligned
     assert e.value.status == ba.BA_ERR_INVALID_ARG
     assert np.isfinite(run.out.float().cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_qkv16_random_shapes(seed):
+    """Seeded random short heads, dtypes and biases the one-launch form
+    takes: its output equals the two-step path's bit for bit, and a second
+    call gives the same bits."""
+    rng = np.random.default_rng(8484 + seed)
+    d = int(rng.choice([8, 16, 24, 32, 40, 48, 56, 64, 72, 80, 88, 96]))
+    N = int(rng.integers(1, 257))
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    dt = BF16 if rng.random() < 0.5 else F16
+    kind = ["none", "dense", "relpos", "relpos0"][int(rng.integers(0, 4))]
+    kw = {}
+    if kind == "dense":
+        N = max(4, N - N % 4)
+        kw = dict(bias="dense_f32")
+    elif kind.startswith("relpos"):
+        grid, npre = relpos_grid(N, 0 if kind == "relpos0" else 1)
+        kw = dict(bias="relpos", grid=grid, n_prefix=npre)
+    print(f"qkv16 random {seed}: B={B} H={H} N={N} d={d} dt={dt} bias={kind}", flush=True)
+    run = DeviceRun(synth(B, H, N, d, dt, 300 + seed, **kw))
+    if kind.startswith("relpos") and kw["n_prefix"] == 0 and kw["grid"][1] % 16 == 0 and 32 < d <= 64:
+        # grid-run relative position at 33..64 channels: no resident form
+        with pytest.raises(ba.BinAttnError) as e:
+            qkv16_out(run)
+        assert e.value.status == ba.BA_ERR_UNSUPPORTED
+        return
+    out = qkv16_out(run)
+    assert same_bits(out, run.out), (seed, B, H, N, d, kind)
+    assert same_bits(qkv16_out(run), out), "repeat"
