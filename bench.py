@@ -11,6 +11,8 @@ V quantised: the outputs of ba_pack_qk and ba_quant_v) and ba_attention_fwd.
 Both forms give the same output bit for bit; the other one is timed beside
 the step under "other_form", and for heads of at most 256 tokens the whole
 pass in one launch (ba_attention_fwd_qkv16) under "qkv_in_one_launch".
+--form qkv16 times that one launch as the step where it applies (q16
+elsewhere), with the q16 form beside it.
 The headline value is effective attention throughput 4*B*H*N^2*d / t_step
 (d the real head dim), for the DiT-XL/2 512px layer (B=8, H=16, N=1024,
 d=72, dense fp16 bias shared over the batch); the same figures for the
@@ -76,8 +78,11 @@ def algorithmic_bytes(s, form: str = "two-step") -> int:
     element; a relative-position table)."""
     W = (s.d + 31) // 32
     BH, N, d = s.B * s.H, s.N, s.d
-    q_bytes = 2 * BH * N * d if form == "q16" else BH * N * (4 * W + 4)
-    nb = q_bytes + BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d + 2 * BH * N * d
+    q_bytes = 2 * BH * N * d if form in ("q16", "qkv16") else BH * N * (4 * W + 4)
+    if form == "qkv16":  # 16-bit K and V, nothing packed in HBM
+        nb = q_bytes + 2 * 2 * BH * N * d + 2 * BH * N * d
+    else:
+        nb = q_bytes + BH * N * (4 * W + 4) + BH * N * d + 4 * BH * d + 2 * BH * N * d
     if s.bias.startswith("dense"):
         esz = 4 if s.bias == "dense_f32" else 2
         nb += (1 if s.bias_shared else s.B) * s.H * N * N * esz
@@ -99,7 +104,8 @@ def prepass_bytes(s) -> int:
 def traffic_for(name: str, form: str = "two-step"):
     """Measured HBM bytes per attention launch of the form, if the counters
     were taken on the current kernel source."""
-    path = os.path.join(PROFILE_DIR, f"attn_fwd_{'q16_' if form == 'q16' else ''}{name}_traffic.json")
+    pre = {"q16": "q16_", "qkv16": "qkv16_"}.get(form, "")
+    path = os.path.join(PROFILE_DIR, f"attn_fwd_{pre}{name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -274,18 +280,34 @@ def step_form(s, form: str) -> str:
     return "q16" if form == "q16" and s.d % 8 == 0 else "two-step"
 
 
+def qkv16_applies(w) -> bool:
+    """Whether ba_attention_fwd_qkv16 takes the workload (one trial call)."""
+    try:
+        w.step_qkv16()
+    except w.ba.BinAttnError as e:
+        if e.status != w.ba.BA_ERR_UNSUPPORTED:
+            raise
+        return False
+    return True
+
+
 def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmup_s: float = 0.3,
             alt: bool = True, form: str = "q16") -> dict:
     """form: "q16" (ba_pack_k_quant_v + ba_attention_fwd_q16, where d % 8 ==
-    0) or "two-step" (ba_pack_qk_quant_v + ba_attention_fwd) is the step
+    0), "two-step" (ba_pack_qk_quant_v + ba_attention_fwd) or "qkv16"
+    (ba_attention_fwd_qkv16 alone, where it applies; else q16) is the step
     timed; alt: also time the other form and the one-launch pass."""
     import workloads
     torch = __import__("torch")
     w = Workload(name)
     s = w.spec
     ops = workloads.eff_ops(s)
-    form = step_form(s, form)
-    step_fn, attn_fn = (w.step, w.attn) if form == "two-step" else (w.step_q16, w.attn_q16)
+    if form == "qkv16" and not qkv16_applies(w):
+        form = "q16"
+    if form != "qkv16":
+        form = step_form(s, form)
+    step_fn, attn_fn = {"two-step": (w.step, w.attn), "q16": (w.step_q16, w.attn_q16),
+                        "qkv16": (w.step_qkv16, w.step_qkv16)}[form]
     dev_warm = device_warmup(step_fn, device_warmup_s)
     # whole step, bracketed by synchronisation on both sides
     for _ in range(warmup):
@@ -305,34 +327,31 @@ def measure(name: str, steps: int, warmup: int, cold: bool = False, device_warmu
     # launches, and the median of single launches with cold caches
     runs = sorted(w.time(attn_fn, iters=max(steps, 20), warmup=3 if i == 0 else 0) for i in range(5))
     attn_ms = runs[2]
-    # the pre-pass alone (HBM-bound), same protocol
-    pre_fn = w.prepass if form == "two-step" else w.prepass_kv
-    pre_ms = sorted(w.time(pre_fn, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
+    # the pre-pass alone (HBM-bound), same protocol; the one-launch form has none
+    pre_ms = None
+    if form != "qkv16":
+        pre_fn = w.prepass if form == "two-step" else w.prepass_kv
+        pre_ms = sorted(w.time(pre_fn, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
     # the other form of the step (where both apply), same protocol, right
     # after the step's own runs (before the cold-cache launches)
     other = None
     if alt and s.d % 8 == 0:
-        o_step, o_attn = (w.step_q16, w.attn_q16) if form == "two-step" else (w.step, w.attn)
+        o_form = "two-step" if form == "q16" else "q16"
+        o_step, o_attn = (w.step, w.attn) if o_form == "two-step" else (w.step_q16, w.attn_q16)
         device_warmup(o_step, min(device_warmup_s, 0.1))
-        other = {"form": "q16" if form == "two-step" else "two-step",
+        other = {"form": o_form,
                  "step_ms": sorted(w.time(o_step, iters=steps, warmup=warmup) for _ in range(3))[1],
                  "attn_ms": sorted(w.time(o_attn, iters=max(steps, 20), warmup=3) for _ in range(3))[1]}
     # the whole pass in one launch where it applies (heads of at most 256 tokens)
     qkv16_ms = None
-    if alt:
-        try:
-            w.step_qkv16()
-        except w.ba.BinAttnError as e:
-            if e.status != w.ba.BA_ERR_UNSUPPORTED:
-                raise
-        else:
-            device_warmup(w.step_qkv16, min(device_warmup_s, 0.1))
-            qkv16_ms = sorted(w.time(w.step_qkv16, iters=steps, warmup=warmup) for _ in range(3))[1]
+    if alt and form != "qkv16" and qkv16_applies(w):
+        device_warmup(w.step_qkv16, min(device_warmup_s, 0.1))
+        qkv16_ms = sorted(w.time(w.step_qkv16, iters=steps, warmup=warmup) for _ in range(3))[1]
     attn_cold_ms = w.time_cold(attn_fn) if cold else None
     # the one-pass (running maximum) form beside it, d <= 64
     online_ms = None
     if s.d <= 64:
-        if form == "q16":
+        if form != "two-step":
             w.prepass()  # (the packed queries the one-pass form reads)
         online_ms = sorted(w.time(w.attn_online, iters=max(steps, 20), warmup=3) for _ in range(3))[1]
     step_fn()  # leave the step's output in place
@@ -397,9 +416,11 @@ def measure_block(steps: int, warmup: int, B=2, N=4096, H=16, d=64, device_warmu
             "attn_ops": 4.0 * B * H * N * N * d, "gemm_flops": 2.0 * B * N * C * 4 * C}
 
 
-def prepass_line(r, form: str) -> dict:
+def prepass_line(r, form: str):
     """The pre-pass launch against the HBM roofline (it moves each input and
-    output once and does little arithmetic)."""
+    output once and does little arithmetic); None for the one-launch form."""
+    if form == "qkv16":
+        return None
     s = r["spec"]
     nb = prepass_bytes(s)
     if form != "two-step":  # K and V only
@@ -434,10 +455,11 @@ def main() -> int:
     ap.add_argument("--device-warmup", type=float, default=0.3, metavar="SECONDS",
                     help="wall time of back-to-back steps run before the W warm-up steps, so the timed "
                          "steps run at the clock the GPU holds under sustained load (0 to skip)")
-    ap.add_argument("--form", choices=["q16", "two-step"], default="q16",
+    ap.add_argument("--form", choices=["q16", "two-step", "qkv16"], default="q16",
                     help="the step timed: q16 (ba_pack_k_quant_v + ba_attention_fwd_q16: Q binarised inside the "
-                         "attention; the default, where d %% 8 == 0) or two-step (ba_pack_qk_quant_v + "
-                         "ba_attention_fwd)")
+                         "attention; the default, where d %% 8 == 0), two-step (ba_pack_qk_quant_v + "
+                         "ba_attention_fwd) or qkv16 (ba_attention_fwd_qkv16 alone, heads of at most 256 tokens; "
+                         "q16 elsewhere)")
     ap.add_argument("--no-alt", action="store_true",
                     help="do not time the other form or the one-launch pass beside the step (the two forms' "
                          "attention launches share one kernel name in a profile)")
@@ -502,13 +524,15 @@ def main() -> int:
                 "bound": "alu", "achieved": round(r["valu_tops"], 3), "peak": round(VALU_PEAK_TLANEOPS, 2),
                 "unit": "T lane-ops/s", "frac": round(r["valu_tops"] / VALU_PEAK_TLANEOPS, 4),
                 "traffic": traffic_for(name, r["form"]),
-                "kernel": "attn_fwd_kernel (ba_attention_fwd_q16)" if r["form"] == "q16"
-                          else "attn_fwd_kernel (ba_attention_fwd)",
+                "kernel": {"q16": "attn_fwd_kernel (ba_attention_fwd_q16)",
+                           "qkv16": "attn_fwd_kernel (ba_attention_fwd_qkv16)"}.get(
+                               r["form"], "attn_fwd_kernel (ba_attention_fwd)"),
                 "scores_per_launch": r["scores"],
                 "lane_ops_per_score": valu_ops_per_score(s),
                 "note": "vector-ALU bound: B*H*N^2 scores x the minimum issue slots per score / launch time "
                         "(HIP events on the launch stream; median of 5 runs of back-to-back launches); peak "
-                        "256 CUs x 64 lanes x 2.4 GHz; the q16 form's query packing is not counted as work",
+                        "256 CUs x 64 lanes x 2.4 GHz; the packing inside the q16 and qkv16 forms is not "
+                        "counted as work",
             },
             "int8_mfma": {"achieved": round(r["attn_tops"], 3), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                           "frac": round(r["attn_tops"] / INT8_PEAK_TOPS, 4),
