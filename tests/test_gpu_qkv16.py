@@ -172,3 +172,14 @@ def test_qkv16_random_shapes(seed):
     out = qkv16_out(run)
     assert same_bits(out, run.out), (seed, B, H, N, d, kind)
     assert same_bits(qkv16_out(run), out), "repeat"
+
+
+@pytest.mark.parametrize("dt,bias", [(BF16, "none"), (F16, "dense_f32")])
+def test_qkv16_largest_resident_shape(dt, bias):
+    """The largest head the one-launch form takes (256 tokens, 96 channels:
+    four key tiles, three 32-channel blocks) on a grid of 512 heads, with and
+    without a dense fp32 bias: the two-step path's bits."""
+    print(f"qkv16 largest: B=32 H=16 N=256 d=96 dt={dt} bias={bias}", flush=True)
+    run = DeviceRun(synth(32, 16, 256, 96, dt, 4321 + dt, bias=bias))
+    out = qkv16_out(run)
+    assert same_bits(out, run.out), (dt, bias)
